@@ -1,0 +1,353 @@
+"""Pins of the fp64 oracle to the pages' definitions and to mathematics.
+
+Every check here compares the oracle with something other than itself: a
+hand-worked case (tests/golden/hand_cases.json), a closed form, an invariant,
+brute force, or a library routine (torch's scaled_dot_product_attention and
+logsumexp in fp64 on the CPU, Python's sorted).
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import seer_oracle as O
+from workloads import WORKLOADS, make_case
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+# ---------------------------------------------------------------- kept counts
+
+def test_keep_counts_hand_table():
+    for c in GOLD["keep_counts"]["cases"]:
+        n = c["n"]
+        if "top_k" in c:
+            got = O.clamp_count(c["top_k"], n)
+        elif "keep" in c:
+            got = O.keep_count(n, *c["keep"])
+        else:
+            got = O.budget_count(n, c["budget_tokens"], c["block_size"])
+        assert got == c["expected"], c
+
+
+@pytest.mark.parametrize("frac", [(1, 10), (1, 20), (1, 4), (3, 10), (7, 8), (1, 1)])
+def test_keep_count_is_smallest_cover(frac):
+    a, b = frac
+    f = Fraction(a, b)
+    for n in range(1, 2049):
+        k = O.keep_count(n, a, b)
+        assert 1 <= k <= n
+        assert Fraction(k, n) >= f or k == n
+        if k > 1:
+            assert Fraction(k - 1, n) < f
+
+
+def test_block_partition():
+    for S in (64, 128):
+        for L in (1, 2, S - 1, S, S + 1, 5 * S, 5 * S + 7, 1024 * S + 1):
+            n = O.block_count(L, S)
+            ranges = [O.block_range(j, L, S) for j in range(n)]
+            assert ranges[0][0] == 0 and ranges[-1][1] == L
+            assert all(ranges[i][1] == ranges[i + 1][0] for i in range(n - 1))
+            assert all(1 <= hi - lo <= S for lo, hi in ranges)
+            assert all(hi - lo == S for lo, hi in ranges[:-1])
+
+
+# ---------------------------------------------------------------- pooling
+
+def test_pool_hand_mean_partial_block():
+    c = GOLD["pool_mean_partial_block"]
+    keys = np.array(c["keys"], dtype=np.float64)
+    p32, p64, open_sum = O.pool_keys(keys, c["length"], c["block_size"])
+    assert np.array_equal(p64, np.array(c["expected_pooled"], dtype=np.float64))
+    assert np.array_equal(p32, np.array(c["expected_pooled"], dtype=np.float32))
+    assert np.array_equal(open_sum, np.array([60.0, -12.0]))
+
+
+def test_pool_sequential_order():
+    c = GOLD["pool_sequential_fp64"]
+    col = np.array(c["keys_col0"], dtype=np.float64)
+    keys = np.stack([col, np.ones_like(col)], axis=1)
+    _, p64, _ = O.pool_keys(keys, c["length"], c["block_size"])
+    assert p64[0, 0] == c["expected_pooled_col0"]
+    assert p64[0, 1] == 1.0
+
+
+def test_pool_fp32_round_to_nearest_even():
+    for c in GOLD["pool_fp32_rne"]["cases"]:
+        keys = np.array(c["keys"], dtype=np.float64)[:, None]
+        p32, p64, _ = O.pool_keys(keys, 2, 2)
+        assert p64[0, 0] == c["expected_fp64_mean"]
+        assert p32.dtype == np.float32 and float(p32[0, 0]) == c["expected_fp32"]
+
+
+def test_pool_identical_rows_give_that_row():
+    rng = np.random.default_rng(1)
+    d, S = 16, 64
+    for L in (1, 7, 64, 65, 200):
+        n = O.block_count(L, S)
+        rows = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+        keys = np.repeat(rows, S, axis=0)
+        p32, p64, _ = O.pool_keys(keys, L, S)
+        # a block of c identical rows x sums to c*x exactly only when exact; use
+        # small dyadic rows so every sum is exact
+        small = np.round(rows * 8) / 8
+        p32s, p64s, _ = O.pool_keys(np.repeat(small, S, axis=0), L, S)
+        assert np.array_equal(p64s, small)
+        assert np.allclose(p64, rows, rtol=1e-15, atol=0)
+
+
+def test_pool_incremental_equals_rebuild_bitwise():
+    rng = np.random.default_rng(2)
+    d, S = 8, 16
+    keys = rng.standard_t(3, size=(200, d)).astype(np.float32).astype(np.float64)
+    L0 = 37
+    p32, _, acc = O.pool_keys(keys, L0, S)
+    L = L0
+    for step in (1, 1, 10, 11, 1, 16, 31, 1, 60):
+        p32, acc = O.pool_keys_append(p32, acc, keys, L, L + step, S)
+        L += step
+        r32, _, racc = O.pool_keys(keys, L, S)
+        assert p32.shape == r32.shape
+        assert np.array_equal(p32.view(np.uint32), r32.view(np.uint32))
+        assert np.array_equal(acc.view(np.uint64), racc.view(np.uint64))
+
+
+# ---------------------------------------------------------------- gate scores
+
+def test_gate_scores_hand_case():
+    c = GOLD["gate_scores_group_sum"]
+    s = O.gate_scores(np.array(c["q_group"], float), np.array(c["pooled"], np.float32), c["head_dim"])
+    assert np.array_equal(s, np.array(c["expected_scores"]))
+
+
+def test_gate_scores_group_mapping_through_decode_step():
+    c = GOLD["gqa_group_mapping"]
+    d = c["head_dim"]
+    q = np.array(c["q"], float)[None]
+    k = np.zeros((1, c["num_kv_heads"], 2, d))
+    v = np.zeros_like(k)
+    pooled = [[np.zeros((2, d), np.float32), np.array(c["pooled_kv1"], np.float32)]]
+    res = O.decode_step(q, k, v, [2], 1, pooled=pooled, top_k=[1])
+    assert np.array_equal(res["scores"][(0, 1)], np.array(c["expected_scores_kv1"]))
+    assert list(res["sel"][(0, 1)]) == [0]
+
+
+def test_gate_scores_zero_query_and_linearity():
+    rng = np.random.default_rng(3)
+    P = rng.standard_normal((50, 32)).astype(np.float32)
+    q = rng.standard_normal((4, 32))
+    assert np.array_equal(O.gate_scores(np.zeros((4, 32)), P, 32), np.zeros(50))
+    assert np.array_equal(O.gate_scores(2.0 * q, P, 32), 2.0 * O.gate_scores(q, P, 32))
+    # G = 1 is a plain dot product over sqrt(d); 1/sqrt(64) = 1/8 exactly
+    s = O.gate_scores(q[:1], P, 64)
+    assert np.allclose(s * 8.0, P.astype(float) @ q[0], rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------- selection
+
+def _brute_select(s, k):
+    order = sorted(range(len(s)), key=lambda j: (-(s[j] + 0.0), j))
+    return sorted(order[:k])
+
+
+def test_select_matches_full_sort_brute_force():
+    rng = np.random.default_rng(4)
+    for trial in range(300):
+        n = int(rng.integers(1, 80))
+        k = int(rng.integers(1, n + 1))
+        if trial % 3 == 0:
+            s = rng.integers(-3, 4, size=n).astype(float)      # many ties
+        else:
+            s = rng.standard_normal(n)
+        got = O.select_top_blocks(s, k)
+        assert list(got) == _brute_select(list(s), k)
+        assert all(got[i] < got[i + 1] for i in range(len(got) - 1))
+
+
+def test_select_special_cases():
+    assert list(O.select_top_blocks(np.zeros(10), 3)) == [0, 1, 2]
+    assert list(O.select_top_blocks(np.array([-0.0, 0.0, -0.0]), 1)) == [0]
+    assert list(O.select_top_blocks(np.array([0.0, -0.0]), 1)) == [0]
+    assert list(O.select_top_blocks(np.arange(7.0), 7)) == list(range(7))
+    assert list(O.select_top_blocks(np.array([1.0, 5.0, 3.0, 5.0]), 1)) == [1]
+    assert list(O.select_top_blocks(np.array([1.0, 5.0, 3.0, 5.0]), 3)) == [1, 2, 3]
+
+
+def test_duplicate_block_loses_to_lower_twin():
+    rng = np.random.default_rng(5)
+    P = rng.standard_normal((20, 16)).astype(np.float32)
+    q = rng.standard_normal((2, 16))
+    s = O.gate_scores(q, P, 16)
+    top = int(np.argmax(s))
+    P2 = P.copy()
+    P2[19] = P2[top]
+    s2 = O.gate_scores(q, P2, 16)
+    assert s2[19] == s2[top]
+    assert list(O.select_top_blocks(s2, 1)) == [top]
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_dense(q, k, v, L, G):
+    """torch's fp64 scaled_dot_product_attention over the first L keys."""
+    qt = torch.from_numpy(q)[:, :, None, :]                     # B, Hq, 1, d
+    kt = torch.from_numpy(k[:, :, :L]).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(v[:, :, :L]).repeat_interleave(G, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, :, 0].numpy()
+
+
+@pytest.mark.parametrize("G,L,S,d", [(4, 1000, 64, 64), (5, 130, 64, 32), (1, 129, 128, 16), (8, 17, 16, 8)])
+def test_dense_equals_sdpa_and_logsumexp(G, L, S, d):
+    rng = np.random.default_rng(6)
+    B, Hkv = 2, 2
+    Hq = G * Hkv
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, L + 5, d))
+    v = rng.standard_normal((B, Hkv, L + 5, d))
+    res = O.decode_step(q, k, v, [L, L], S, dense=True)
+    ref = _sdpa_dense(q, k, v, L, G)
+    assert np.allclose(res["out"], ref, rtol=0, atol=1e-12)
+    kt = torch.from_numpy(k[:, :, :L]).repeat_interleave(G, dim=1)
+    logits = torch.einsum("bhd,bhtd->bht", torch.from_numpy(q), kt) / math.sqrt(d)
+    assert np.allclose(res["lse"], torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_gather_equals_masked_brute_force():
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        S = int(rng.choice([4, 8]))
+        L = int(rng.integers(1, 60))
+        d = 8
+        n = O.block_count(L, S)
+        k = int(rng.integers(1, n + 1))
+        sel = np.sort(rng.choice(n, size=k, replace=False))
+        keys = rng.standard_normal((n * S, d))
+        vals = rng.standard_normal((n * S, d))
+        q = rng.standard_normal(d)
+        toks = O.selected_tokens(sel, L, S)
+        mask = np.zeros(n * S, bool)
+        mask[toks] = True
+        o1, l1, w = O.attend(q, keys, vals, toks)
+        o2, l2 = O.attend_masked(q, keys, vals, mask)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-13)
+        assert abs(l1 - l2) < 1e-13
+        assert abs(w.sum() - 1.0) < 1e-12 and (w >= 0).all()
+        # the partial last block contributes only its valid tokens
+        assert toks.max() < L
+
+
+def test_attention_order_invariance():
+    rng = np.random.default_rng(8)
+    L, S, d = 500, 32, 16
+    keys = rng.standard_normal((L, d))
+    vals = rng.standard_normal((L, d))
+    q = rng.standard_normal(d)
+    sel = np.array([0, 3, 7, 15])
+    o1, l1, _ = O.attend(q, keys, vals, O.selected_tokens(sel, L, S))
+    o2, l2, _ = O.attend(q, keys, vals, O.selected_tokens(sel[::-1], L, S))
+    assert np.allclose(o1, o2, rtol=0, atol=1e-14) and abs(l1 - l2) < 1e-13
+
+
+def test_attention_closed_forms():
+    c = GOLD["attention_two_tokens"]
+    e = math.e
+    o, l, w = O.attend(np.array(c["q"], float), np.array(c["keys"], float),
+                       np.array(c["values"], float), np.array([0, 1]))
+    assert np.allclose(o, [e / (e + 1), 1 / (e + 1), 0, 0], rtol=0, atol=1e-15)
+    assert abs(l - math.log(e + 1)) < 1e-15
+    rng = np.random.default_rng(9)
+    keys = rng.standard_normal((10, 4))
+    vals = rng.standard_normal((10, 4))
+    q = rng.standard_normal(4)
+    # one token: the output is its value, the lse its logit
+    o, l, _ = O.attend(q, keys, vals, np.array([3]))
+    assert np.array_equal(o, vals[3]) and abs(l - keys[3] @ q / 2.0) < 1e-15
+    # constant values: the output is that constant
+    o, _, _ = O.attend(q, keys, np.tile(vals[:1], (10, 1)), np.arange(10))
+    assert np.allclose(o, vals[0], rtol=0, atol=1e-14)
+    # equal keys: uniform weights, the output is the mean value
+    o, _, w = O.attend(q, np.tile(keys[:1], (10, 1)), vals, np.arange(10))
+    assert np.allclose(w, 0.1, rtol=0, atol=1e-16) and np.allclose(o, vals.mean(0), atol=1e-14)
+
+
+# ---------------------------------------------------------------- paging
+
+def test_paged_gather_round_trip_and_poison():
+    rng = np.random.default_rng(10)
+    B, Hkv, S, d = 3, 2, 8, 4
+    lens = [17, 8, 30]
+    nb = [O.block_count(x, S) for x in lens]
+    kc = rng.standard_normal((B, Hkv, 4 * S, d))
+    perm = rng.permutation(sum(nb))
+    pool = np.full((sum(nb), Hkv, S, d), np.nan)
+    table = -np.ones((B, 4), int)
+    nxt = 0
+    for b in range(B):
+        for j in range(nb[b]):
+            table[b, j] = perm[nxt]
+            pool[perm[nxt]] = kc[b, :, j * S:(j + 1) * S]
+            nxt += 1
+    for b in range(B):
+        g = O.gather_paged(pool, table, b, nb[b])
+        assert np.array_equal(g, kc[b, :, : nb[b] * S])
+    # NaN past the length never reaches the output
+    kp = kc.copy()
+    vp = rng.standard_normal(kc.shape)
+    q = rng.standard_normal((B, 2 * Hkv, d))
+    base = O.decode_step(q, kp, vp, lens, S, top_k=[2, 2, 2])
+    for b in range(B):
+        kp[b, :, lens[b]:] = np.nan
+        vp[b, :, lens[b]:] = np.nan
+    pois = O.decode_step(q, kp, vp, lens, S, top_k=[2, 2, 2])
+    assert np.array_equal(base["out"], pois["out"])
+
+
+# ---------------------------------------------------------------- workloads
+
+def _np(t):
+    return t.double().numpy()
+
+
+def test_planted_blocks_are_selected():
+    """Planted blocks (about 16 standard deviations above the rest) are kept."""
+    wl = WORKLOADS["planted_8k"].with_(batch=1)
+    c = make_case(wl)
+    res = O.decode_step(_np(c.q), _np(c.k), _np(c.v), c.lens.tolist(), wl.block_size, keep=wl.keep)
+    for g in range(wl.num_kv_heads):
+        sel = set(res["sel"][(0, g)].tolist())
+        assert len(sel) == 13
+        assert set(c.planted[0, g].tolist()) <= sel
+
+
+def test_tiny_workload_selection_and_dense_limit():
+    wl = WORKLOADS["tiny_1k"]
+    c = make_case(wl)
+    q, k, v = _np(c.q), _np(c.k), _np(c.v)
+    res = O.decode_step(q, k, v, c.lens.tolist(), wl.block_size, top_k=c.top_k.tolist())
+    assert len(res["sel"][(0, 0)]) == 4
+    full = O.decode_step(q, k, v, c.lens.tolist(), wl.block_size, top_k=[16])
+    ref = _sdpa_dense(q, k, v, 1024, 4)
+    assert np.allclose(full["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_generator_is_deterministic():
+    wl = WORKLOADS["paged_var"].with_(batch=3, variable_context=(100, 300))
+    a = make_case(wl)
+    b = make_case(wl)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.lens, b.lens), (a.page_table, b.page_table)):
+        assert torch.equal(x, y)
+
+
+def test_pool_signed_zero_sum_of_valid_keys_only():
+    """A block whose valid keys are all -0.0 pools to -0.0: only valid keys are summed."""
+    keys = np.zeros((8, 2))
+    keys[4:6] = -0.0
+    p32, p64, _ = O.pool_keys(keys, 6, 4)
+    assert np.signbit(p64[1]).all() and np.signbit(p32[1]).all()
+    assert not np.signbit(p64[0]).any()

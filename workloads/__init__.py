@@ -1,0 +1,12 @@
+"""Seeded synthetic decode workloads.
+
+This package is shared by the fp64 oracle tests, the GPU parity tests and the
+benchmark.  It only draws random inputs and lays them out in memory; it holds
+none of the method's arithmetic (no pooling, no gate score, no selection, no
+attention).
+"""
+
+from .configs import WORKLOADS, Workload, get_workload
+from .gen import Case, make_case
+
+__all__ = ["WORKLOADS", "Workload", "get_workload", "Case", "make_case"]
