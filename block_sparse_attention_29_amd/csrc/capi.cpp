@@ -1,0 +1,289 @@
+// C-ABI of libseer: host-side validation and launch of the gfx950 kernels.
+// The public contract of every entry point is documented in include/seer.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "seer.h"
+#include "seer_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+seer_status fail(seer_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+seer_status fail(seer_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+seer_status ok() {
+  g_err[0] = '\0';
+  return SEER_OK;
+}
+
+seer_status hip_fail(hipError_t e, const char* what) {
+  return fail(SEER_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxBlocks = 8192;
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+
+seer_status check_shape(const seer_shape* s) {
+  if (!s) return fail(SEER_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
+      s->block_size < 1 || s->max_blocks < 1)
+    return fail(SEER_ERR_INVALID_ARG, "shape fields must be positive");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(SEER_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->dtype != SEER_F32 && s->dtype != SEER_BF16)
+    return fail(SEER_ERR_INVALID_ARG, "dtype %d is not a seer_dtype", s->dtype);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G > 8) return fail(SEER_ERR_UNSUPPORTED, "query heads per KV head %d > 8", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SEER_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
+  if (s->block_size != 64 && s->block_size != 128)
+    return fail(SEER_ERR_UNSUPPORTED, "block_size %d not in {64, 128}", s->block_size);
+  if ((int64_t)s->batch * s->num_kv_heads > SEER_MAX_UNITS)
+    return fail(SEER_ERR_UNSUPPORTED, "batch * num_kv_heads = %lld > %d",
+                (long long)s->batch * s->num_kv_heads, SEER_MAX_UNITS);
+  if (s->max_blocks > kMaxBlocks)
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d > %d", s->max_blocks, kMaxBlocks);
+  if ((int64_t)s->max_blocks * s->block_size > kMaxTokens)
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks * block_size exceeds 2^30 tokens");
+  return SEER_OK;
+}
+
+seer_status check_kv(const seer_kv* kv) {
+  if (!kv) return fail(SEER_ERR_INVALID_ARG, "kv is NULL");
+  if (!kv->k || !kv->v) return fail(SEER_ERR_INVALID_ARG, "kv.k or kv.v is NULL");
+  if (kv->page_table && kv->num_pages < 1)
+    return fail(SEER_ERR_INVALID_ARG, "paged cache with num_pages < 1");
+  return SEER_OK;
+}
+
+int wave_cap(const seer_shape* s) {
+  return seer::decode_max_waves(s->dtype, s->head_dim, s->num_q_heads / s->num_kv_heads);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* seer_status_str(int32_t st) {
+  switch (st) {
+    case SEER_OK: return "SEER_OK";
+    case SEER_ERR_INVALID_ARG: return "SEER_ERR_INVALID_ARG";
+    case SEER_ERR_UNSUPPORTED: return "SEER_ERR_UNSUPPORTED";
+    case SEER_ERR_WORKSPACE: return "SEER_ERR_WORKSPACE";
+    case SEER_ERR_HIP: return "SEER_ERR_HIP";
+  }
+  return "SEER_STATUS_UNKNOWN";
+}
+
+const char* seer_last_error(void) { return g_err; }
+
+int32_t seer_keep_blocks(int32_t n, int32_t num, int32_t den) {
+  if (n < 1 || num < 1 || den < num) return -1;
+  const int64_t k = ((int64_t)n * num + den - 1) / den;
+  return (int32_t)(k < 1 ? 1 : (k > n ? n : k));
+}
+
+seer_status seer_block_pool_keys(const seer_shape* shape, const seer_kv* kv,
+                                 const int32_t* lens_old, const int32_t* lens_new,
+                                 float* pooled, double* open_sum, hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_kv(kv))) return st;
+  if (!lens_new) return fail(SEER_ERR_INVALID_ARG, "lens_new is NULL");
+  if (!pooled || !open_sum) return fail(SEER_ERR_INVALID_ARG, "pooled or open_sum is NULL");
+  seer::PoolArgs a{};
+  a.k = kv->k;
+  a.page_table = kv->page_table;
+  a.num_pages = kv->num_pages;
+  a.lens_old = lens_old;
+  a.lens_new = lens_new;
+  a.B = shape->batch;
+  a.Hkv = shape->num_kv_heads;
+  a.D = shape->head_dim;
+  a.NB = shape->max_blocks;
+  a.S = shape->block_size;
+  a.dtype = shape->dtype;
+  a.pooled = pooled;
+  a.open_sum = open_sum;
+  const hipError_t e = seer::launch_pool_keys(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
+  return ok();
+}
+
+seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const float* pooled,
+                                  const int32_t* lens, const int32_t* top_k, int32_t keep_num,
+                                  int32_t keep_den, int32_t k_max, double* scores,
+                                  int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if (!q || !pooled || !lens || !scores || !sel_idx || !sel_cnt)
+    return fail(SEER_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (k_max < 1 || k_max > shape->max_blocks)
+    return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
+                shape->max_blocks);
+  if (!top_k) {
+    const int32_t kk = seer_keep_blocks(shape->max_blocks, keep_num, keep_den);
+    if (kk < 0)
+      return fail(SEER_ERR_INVALID_ARG, "keep rule %d/%d invalid (need 1 <= num <= den)",
+                  keep_num, keep_den);
+    if (kk > k_max)
+      return fail(SEER_ERR_INVALID_ARG, "keep rule keeps %d of max_blocks=%d blocks > k_max=%d",
+                  kk, shape->max_blocks, k_max);
+  }
+  seer::GateArgs a{};
+  a.q = q;
+  a.pooled = pooled;
+  a.lens = lens;
+  a.top_k = top_k;
+  a.keep_num = keep_num;
+  a.keep_den = keep_den;
+  a.k_max = k_max;
+  a.B = shape->batch;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.D = shape->head_dim;
+  a.NB = shape->max_blocks;
+  a.S = shape->block_size;
+  a.dtype = shape->dtype;
+  a.scores = scores;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  const hipError_t e = seer::launch_gate_topk(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "gate_topk launch");
+  return ok();
+}
+
+seer_status seer_sparse_decode_workspace_size(const seer_shape* shape, size_t* bytes) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if (!bytes) return fail(SEER_ERR_INVALID_ARG, "bytes is NULL");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  *bytes = seer::decode_workspace_bytes(shape->batch, shape->num_kv_heads,
+                                        shape->num_q_heads / shape->num_kv_heads,
+                                        shape->head_dim, wmax);
+  return ok();
+}
+
+seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
+                                       const int32_t* lens, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t k_max,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_kv(kv))) return st;
+  if (!q || !lens) return fail(SEER_ERR_INVALID_ARG, "q or lens is NULL");
+  if (sel_idx) {
+    if (!sel_cnt) return fail(SEER_ERR_INVALID_ARG, "sel_idx given without sel_cnt");
+    if (k_max < 1 || k_max > shape->max_blocks)
+      return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
+                  shape->max_blocks);
+  }
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(SEER_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  const int U = shape->batch * shape->num_kv_heads;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const size_t need = seer::decode_workspace_bytes(shape->batch, shape->num_kv_heads, G,
+                                                   shape->head_dim, wmax);
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+  // Waves: all resident slots, but no more than an upper bound of the tiles.
+  const int64_t blocks_bound =
+      (int64_t)U * (sel_idx ? k_max : shape->max_blocks);
+  const int64_t tiles_bound = blocks_bound * (shape->block_size / 16);  // 16-token tiles
+  int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
+  W = (W + 3) / 4 * 4;
+
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale
+                                           : 1.0 / sqrt((double)shape->head_dim);
+  seer::DecodeArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.num_pages = kv->num_pages;
+  a.lens = lens;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.B = shape->batch;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.D = shape->head_dim;
+  a.NB = shape->max_blocks;
+  a.S = shape->block_size;
+  a.k_max = sel_idx ? k_max : shape->max_blocks;
+  a.dtype = shape->dtype;
+  a.W = (int32_t)W;
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  char* ws = (char*)workspace;
+  a.hdr = (int32_t*)ws;
+  a.prefix = (int32_t*)(ws + 64);
+  a.part = (float*)(ws + seer::decode_part_offset(U));
+  const hipError_t e = seer::launch_decode_partial(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+  return ok();
+}
+
+seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
+                                       const void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  const int U = shape->batch * shape->num_kv_heads;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const size_t need = seer::decode_workspace_bytes(shape->batch, shape->num_kv_heads, G,
+                                                   shape->head_dim, wmax);
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const char* ws = (const char*)workspace;
+  seer::CombineArgs c{};
+  c.B = shape->batch;
+  c.Hq = shape->num_q_heads;
+  c.Hkv = shape->num_kv_heads;
+  c.D = shape->head_dim;
+  c.S = shape->block_size;
+  c.hdr = (const int32_t*)ws;
+  c.prefix = (const int32_t*)(ws + 64);
+  c.part = (const float*)(ws + seer::decode_part_offset(U));
+  c.out = out;
+  c.lse = lse;
+  const hipError_t e = seer::launch_decode_combine(c, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
+  return ok();
+}
+
+seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
+                               const int32_t* lens, const int32_t* sel_idx,
+                               const int32_t* sel_cnt, int32_t k_max, float softmax_scale,
+                               float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  seer_status st = seer_sparse_decode_partial(shape, q, kv, lens, sel_idx, sel_cnt, k_max,
+                                              softmax_scale, workspace, workspace_bytes, stream);
+  if (st) return st;
+  return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

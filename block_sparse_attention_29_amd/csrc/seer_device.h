@@ -1,0 +1,122 @@
+// Device-side helpers shared by the gfx950 kernels of libseer.
+//
+// Wavefronts are 64 lanes wide.  A "row" is a group of 16 consecutive lanes,
+// the unit that gfx9 DPP row operations work on and the unit in which a
+// 16x16 MFMA result is laid out.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seer {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e of a 16-byte chunk holding bf16 (T = uint16_t) or fp32 (T = float).
+template <typename T>
+__device__ __forceinline__ float chunk_elem(const uint4& c, int e);
+
+template <>
+__device__ __forceinline__ float chunk_elem<uint16_t>(const uint4& c, int e) {
+  const uint32_t w = (e >> 1) == 0 ? c.x : (e >> 1) == 1 ? c.y : (e >> 1) == 2 ? c.z : c.w;
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+template <>
+__device__ __forceinline__ float chunk_elem<float>(const uint4& c, int e) {
+  const uint32_t w = e == 0 ? c.x : e == 1 ? c.y : e == 2 ? c.z : c.w;
+  return __uint_as_float(w);
+}
+
+// ---------------------------------------------------------------- DPP
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Every control used here names an in-row source lane for every lane, so the
+// plain move form (no "old" operand) is exact.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
+// IEEE max and + are commutative, so every lane computes the same value.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppRowHalfMirror>(x);
+  x += dpp_f32<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// ---------------------------------------------------------------- scans
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64, at most
+// 1024).  `scratch` holds NT/64 + 1 ints of shared memory.  Returns the
+// exclusive prefix; *total gets the block total.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, int* scratch, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(x);
+  if (lane == 63) scratch[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int s = scratch[i];
+    base += (i < wv) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+// ---------------------------------------------------------------- fp64 order key
+
+// Order-preserving map of a finite double to uint64 (larger value -> larger
+// key), with -0.0 and +0.0 mapped to the same key.
+__device__ __forceinline__ uint64_t order_key(double s) {
+  if (s == 0.0) s = 0.0;  // folds -0.0 into +0.0
+  const uint64_t bits = (uint64_t)__double_as_longlong(s);
+  return (bits >> 63) ? ~bits : (bits | 0x8000000000000000ull);
+}
+
+}  // namespace seer

@@ -1,0 +1,82 @@
+// Internal launch interface between the C-ABI layer (capi.cpp) and the
+// kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace seer {
+
+// ---------------------------------------------------------------- decode
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  int64_t num_pages;
+  const int32_t* lens;
+  const int32_t* sel_idx;  // nullptr: dense
+  const int32_t* sel_cnt;
+  int32_t B, Hq, Hkv, D, NB, S, k_max;
+  int32_t dtype;          // 0 fp32, 1 bf16
+  int32_t W;              // waves of the partial kernel (multiple of 4)
+  float scale_log2;       // softmax scale * log2(e)
+  int32_t* hdr;           // workspace header: [0] = W
+  int32_t* prefix;        // [U + 1] block prefix over units
+  float* part;            // [(U + Wmax)][G*D + 16] partial records
+};
+
+struct CombineArgs {
+  int32_t B, Hq, Hkv, D, S;
+  const int32_t* hdr;
+  const int32_t* prefix;
+  const float* part;
+  float* out;
+  float* lse;
+};
+
+// Workspace layout: [hdr: 64 bytes][prefix: (U+1) int32, padded to 256][part].
+size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int wmax);
+size_t decode_part_offset(int U);
+
+// Number of resident waves of the partial kernel on the current device for
+// this instantiation (0 if the instantiation does not exist).
+int decode_max_waves(int dtype, int D, int G);
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- gate
+
+struct GateArgs {
+  const void* q;
+  const float* pooled;
+  const int32_t* lens;
+  const int32_t* top_k;  // nullptr: keep rule
+  int32_t keep_num, keep_den, k_max;
+  int32_t B, Hq, Hkv, D, NB, S, dtype;
+  double* scores;
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+};
+
+hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- pooling
+
+struct PoolArgs {
+  const void* k;
+  const int32_t* page_table;
+  int64_t num_pages;
+  const int32_t* lens_old;  // nullptr: bulk
+  const int32_t* lens_new;
+  int32_t B, Hkv, D, NB, S, dtype;
+  float* pooled;
+  double* open_sum;
+};
+
+hipError_t launch_pool_keys(const PoolArgs& a, hipStream_t stream);
+
+}  // namespace seer

@@ -1,0 +1,542 @@
+// Split-KV block-sparse decode attention for gfx950.
+//
+// Computes, for every query head h of sequence b (g = h / G its KV head),
+// softmax(q_h . k_t * scale) v_t over the valid tokens t of the kept blocks
+// only -- the masked attention of "Sparse Attention Reasoning", Step 4, where
+// every key outside the kept blocks is -inf -- without touching any other key
+// ("SeerAttention-R", Abstract: a sparse decoding kernel whose time follows the
+// KV bytes it reads).
+//
+// Work split.  A "unit" is one (sequence, KV head); its kept blocks are cut
+// into 32-token tiles.  The tiles of all units are concatenated (unit-major,
+// then kept-block order, then tile) and the W waves of the launch take equal
+// contiguous ranges of that list, so every wave streams the same number of KV
+// bytes whatever the per-sequence lengths and counts.  A wave keeps one
+// online-softmax state per unit segment it covers and writes it as a partial
+// record to slot (unit + wave), which is unique because both coordinates only
+// grow along the list.  The combine kernel merges a unit's records by
+// log-sum-exp in wave order, so the result does not depend on timing.
+//
+// Per 32-token tile a wave:
+//  * loads K as the B operand of v_mfma_f32_16x16x32_bf16 (bf16) or
+//    v_mfma_f32_16x16x4_f32 (fp32): lane (r, n), r = lane/16, n = lane%16,
+//    holds 16 bytes of token n's row at byte offset c*64 + r*16 for load c.
+//    The query group is the A operand with the same lane mapping (head n, zero
+//    rows for n >= G), so both operands share one k-index assignment and the
+//    product is q . k whatever order the unit uses internally.  The 16x16
+//    result holds logit (head 4*r + i, token n) in lane (r, n), register i.
+//  * takes the tile max per head with DPP row reductions, rescales, and
+//    writes exp2 probabilities to a 1 KiB LDS buffer per wave;
+//  * streams V rows fully coalesced (16 bytes per lane, whole rows per
+//    instruction) and accumulates p * v in fp32 on the VALU; probabilities stay
+//    in fp32 (no rounding to bf16 before the product).
+// The K registers are refilled with the next tile right after the QK product
+// and the V registers right after the PV product, so each wave keeps about one
+// tile of loads in flight while it computes.
+#include "seer_device.h"
+#include "seer_kernels.h"
+
+namespace seer {
+namespace {
+
+constexpr int kTile = 16;          // tokens per tile (one 16-wide MFMA column)
+constexpr int kCols = kTile / 16;  // 16-token MFMA columns per tile
+constexpr int kWavesPerWG = 4;
+constexpr int kThreads = kWavesPerWG * kWave;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <typename T, int D>
+struct Geo {
+  static constexpr int EB = sizeof(T);
+  static constexpr int ROWB = D * EB;      // bytes per token row
+  static constexpr int E = 16 / EB;        // elements per 16-byte chunk
+  static constexpr int NKL = ROWB / 64;    // K chunks per lane per 16-token column
+  static constexpr int LPR = ROWB / 16;    // lanes per V row
+  static constexpr int RPI = kWave / LPR;  // V rows per load instruction
+  static constexpr int NVL = kTile / RPI;  // V chunks per lane per tile
+};
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int lane) {
+  const int lo = readlane_i((int)(uint32_t)(uint64_t)x, lane);
+  const int hi = readlane_i((int)(uint32_t)((uint64_t)x >> 32), lane);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// Blocks a unit contributes: its kept count, or all its blocks when dense.
+__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int u) {
+  if (a.sel_idx) {
+    const int c = a.sel_cnt[u];
+    return c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
+  }
+  const int L = a.lens[u / a.Hkv];
+  if (L <= 0) return 0;
+  const int n = (int)(((int64_t)L + a.S - 1) / a.S);
+  return n > a.NB ? a.NB : n;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_partial_kernel(DecodeArgs a) {
+  using GE = Geo<T, D>;
+  constexpr int EB = GE::EB, ROWB = GE::ROWB, E = GE::E, NKL = GE::NKL;
+  constexpr int LPR = GE::LPR, RPI = GE::RPI, NVL = GE::NVL;
+  constexpr int REC = G * D + 16;  // partial record: acc[G][D], m[8], l[8] (floats)
+
+  __shared__ __align__(16) float s_p[kWavesPerWG][kTile * 16];
+  extern __shared__ int s_dyn[];
+
+  const int U = a.B * a.Hkv;
+  const int tid = threadIdx.x;
+  int* s_prefix = s_dyn;          // [U + 1]
+  int* s_scan = s_dyn + U + 1;    // [kWavesPerWG + 1]
+
+  // ---- plan: block prefix over units (every workgroup computes the same) ----
+  {
+    const int per = (U + kThreads - 1) / kThreads;
+    const int u_lo = min(U, tid * per), u_hi = min(U, u_lo + per);
+    int local = 0;
+    for (int u = u_lo; u < u_hi; ++u) {
+      const int c = unit_blocks(a, u);
+      s_prefix[u] = c;
+      local += c;
+    }
+    int total;
+    int base = block_excl_scan<kThreads>(local, s_scan, &total);
+    for (int u = u_lo; u < u_hi; ++u) {
+      const int c = s_prefix[u];
+      s_prefix[u] = base;
+      base += c;
+    }
+    if (tid == 0) s_prefix[U] = total;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int u = tid; u <= U; u += kThreads) a.prefix[u] = s_prefix[u];
+      if (tid == 0) a.hdr[0] = a.W;
+    }
+  }
+
+  const int lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane >> 4, n16 = lane & 15;
+  // The wave index is uniform per wave; say so, so that everything derived
+  // from it (the tile range, the loop counters) lives in scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + wv);
+  // Tile coordinates fit in 32 bits: units * blocks * tiles per block < 2^31.
+  const int tsh = 31 - __builtin_clz(a.S / kTile);  // log2(tiles per block)
+  const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
+  const int y0 = (int)((int64_t)w * Tot / a.W);
+  const int y1 = (int)((int64_t)(w + 1) * Tot / a.W);
+  if (y0 >= y1) return;
+
+  const bool sparse = a.sel_idx != nullptr;
+  const int Hkv = a.Hkv, S = a.S, NB = a.NB;
+  const char* kbase = (const char*)a.k;
+  const char* vbase = (const char*)a.v;
+  float* pw = s_p[wv];
+  const float sl = a.scale_log2;
+
+  // First unit of the range: largest u with s_prefix[u] <= block of y0.
+  int u;
+  {
+    int lo = 0, hi = U - 1;
+    const int x0 = y0 >> tsh;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= x0) lo = mid; else hi = mid - 1;
+    }
+    u = __builtin_amdgcn_readfirstlane(lo);
+  }
+
+  int y = y0;
+  while (y < y1) {
+    // ---- one segment: the tiles of unit u inside [y, y1) ----
+    while ((__builtin_amdgcn_readfirstlane(s_prefix[u + 1]) << tsh) <= y) ++u;  // skips units without blocks
+    const int Yu = __builtin_amdgcn_readfirstlane(s_prefix[u]) << tsh;
+    const int ye = min(y1, __builtin_amdgcn_readfirstlane(s_prefix[u + 1]) << tsh);
+    const int b = u / Hkv, g = u - b * Hkv;
+    const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
+
+    // Per-lane descriptors of 64 consecutive kept blocks (slots) of unit u.
+    int cs = -(1 << 30);
+    int ci_nv = 0;
+    int64_t ci_off = 0;
+    auto load_chunk = [&](int slot0) {
+      cs = slot0;
+      const int slot = slot0 + lane;
+      int nv = 0;
+      int64_t off = 0;
+      if (slot < s_prefix[u + 1] - s_prefix[u]) {
+        const int j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
+        if (j >= 0 && j < NB && (int64_t)j * S < L) {
+          nv = min(S, L - j * S);
+          if (a.page_table) {
+            const int pg = a.page_table[(int64_t)b * NB + j];
+            if (pg >= 0 && pg < a.num_pages) off = ((int64_t)pg * Hkv + g) * S * D;
+            else nv = 0;
+          } else {
+            off = (((int64_t)b * Hkv + g) * NB + j) * (int64_t)S * D;
+          }
+        }
+      }
+      ci_nv = nv;
+      ci_off = off;
+    };
+    // Tile t of the segment: valid tokens and the element offset of the rows to
+    // load.  Empty tiles re-read their block's last valid tile (in bounds).
+    auto describe = [&](int yt, int& tv, int64_t& row0) {
+      const int rel = yt - Yu;
+      const int slot = rel >> tsh;
+      const int tib = rel - (slot << tsh);
+      const int li = slot - cs;  // within the loaded chunk by construction
+      const int nv = readlane_i(ci_nv, li);
+      const int64_t off = readlane64(ci_off, li);
+      tv = min(kTile, max(0, nv - tib * kTile));
+      const int tl = nv > 0 ? min(tib, (nv - 1) / kTile) : 0;
+      row0 = off + (int64_t)tl * kTile * D;
+    };
+
+    // Unit state: the query group as the MFMA A operand, softmax state, acc.
+    uint4 qa[NKL];
+    {
+      const char* qb = (const char*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * ROWB;
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+        uint4 z = make_uint4(0, 0, 0, 0);
+        if (n16 < G) z = *(const uint4*)(qb + n16 * ROWB + c * 64 + r16 * 16);
+        qa[c] = z;
+      }
+    }
+    float m_run[4], l_run[4];
+    float acc[G][E];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = kNegInf; l_run[i] = 0.f; }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+
+    uint4 kr[kCols][NKL];
+    uint4 vr[NVL];
+    auto issue_k = [&](int64_t row0) {
+      const char* kb = kbase + row0 * EB;
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct)
+#pragma unroll
+        for (int c = 0; c < NKL; ++c)
+          kr[ct][c] = *(const uint4*)(kb + (ct * 16 + n16) * ROWB + c * 64 + r16 * 16);
+    };
+    auto issue_v = [&](int64_t row0) {
+      const char* vb = vbase + row0 * EB;
+#pragma unroll
+      for (int rr = 0; rr < NVL; ++rr)
+        vr[rr] = *(const uint4*)(vb + (rr * RPI + lane / LPR) * ROWB + (lane % LPR) * 16);
+    };
+
+    // S = Q K^T for the tile's two 16-token columns.
+    auto qk = [&](f32x4 (&sc)[kCols]) {
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct) sc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          if constexpr (EB == 2) {
+            sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                             __builtin_bit_cast(bf16x8, kr[ct][c]),
+                                                             sc[ct], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_elem<float>(qa[c], e),
+                                                            chunk_elem<float>(kr[ct][c], e),
+                                                            sc[ct], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    // Online softmax (log2 domain).  Lane (r16, n16) register i holds head
+    // 4*r16 + i at tokens n16 and 16 + n16.  Publishes p to LDS and rescales acc.
+    auto softmax = [&](const f32x4 (&sc)[kCols], int tv) {
+      float x[kCols][4], alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          x[ct][i] = (ct * 16 + n16 < tv) ? sc[ct][i] * sl : kNegInf;
+          mx = fmaxf(mx, x[ct][i]);
+        }
+        mx = row_max16(mx);
+        const float mn = fmaxf(m_run[i], mx);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        // Arguments are <= 0 (or -inf): the hardware exp2 is accurate there.
+        alpha[i] = __builtin_amdgcn_exp2f(m_run[i] - mu);
+        float ps = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          x[ct][i] = __builtin_amdgcn_exp2f(x[ct][i] - mu);
+          ps += x[ct][i];
+        }
+        l_run[i] = l_run[i] * alpha[i] + ps;
+        m_run[i] = mn;
+      }
+      // Every lane writes (rows of heads >= G are never read): no branch.
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct)
+        *(float4*)(pw + (ct * 16 + n16) * 16 + r16 * 4) =
+            make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+      // Rescale acc (alpha is exactly 1 for a head whose max did not move).
+      // Unconditional: a branch here splits acc's live range into copies.
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= ah;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // O += P V with V rows streamed row-major, p from LDS, fp32 FMAs.  One row
+    // step at a time (its p read one step ahead) keeps the temporaries small.
+    auto read_p = [&](int rr, float (&pr)[G]) {
+      const int trow = rr * RPI + lane / LPR;
+      const float4 plo = *(const float4*)(pw + trow * 16);
+      float4 phi = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (G > 4) phi = *(const float4*)(pw + trow * 16 + 4);
+      const float all[8] = {plo.x, plo.y, plo.z, plo.w, phi.x, phi.y, phi.z, phi.w};
+#pragma unroll
+      for (int h = 0; h < G; ++h) pr[h] = all[h];
+    };
+    auto pv = [&](int tv) {
+      float pn[G];
+      read_p(0, pn);
+#pragma unroll
+      for (int rr = 0; rr < NVL; ++rr) {
+        float pc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pc[h] = pn[h];
+        if (rr + 1 < NVL) read_p(rr + 1, pn);
+        const int trow = rr * RPI + lane / LPR;
+        // Rows past the length may hold anything (even NaN): zero them.
+        const bool live = trow < tv;
+        uint4 vv = vr[rr];
+        vv.x = live ? vv.x : 0u;
+        vv.y = live ? vv.y : 0u;
+        vv.z = live ? vv.z : 0u;
+        vv.w = live ? vv.w : 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float ve = chunk_elem<T>(vv, e);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pc[h], ve, acc[h][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    // ---- tiles: K and V each re-issued as soon as their registers are consumed.
+    // The segment is walked in chunks of at most 64 kept blocks, one block
+    // descriptor per lane, so the steady-state loop has no branches.
+    while (y < ye) {
+      const int slot0 = (y - Yu) >> tsh;
+      load_chunk(slot0);
+      const int yc = min(ye, Yu + ((slot0 + kWave) << tsh));
+      int tv;
+      int64_t row0;
+      describe(y, tv, row0);
+      issue_k(row0);
+      issue_v(row0);
+      for (; y + 1 < yc; ++y) {
+        int tv_n;
+        int64_t row_n;
+        describe(y + 1, tv_n, row_n);
+        f32x4 sc[kCols];
+        qk(sc);
+        // Keep the scheduler from hoisting the refills above the products that
+        // free their registers (that would double the live K/V registers).
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(row_n);
+        softmax(sc, tv);
+        pv(tv);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(row_n);
+        tv = tv_n;
+      }
+      {
+        f32x4 sc[kCols];
+        qk(sc);
+        softmax(sc, tv);
+        pv(tv);
+      }
+      y = yc;
+    }
+
+    // ---- segment result: partial record (u, w) at slot u + w ----
+    float lt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lt[i] = row_sum16(l_run[i]);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float x = acc[h][e];
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+        acc[h][e] = x;
+      }
+    float* rec = a.part + (int64_t)(u + w) * REC;
+    if (lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *(float4*)(rec + h * D + lane * E + e) =
+              make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+    }
+    if (n16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = r16 * 4 + i;
+        if (h < G) {
+          rec[G * D + h] = m_run[i];
+          rec[G * D + 8 + h] = lt[i];
+        }
+      }
+    }
+  }
+}
+
+// Merges the partial records of one unit per workgroup.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
+  const int u = blockIdx.x;
+  const int U = a.B * a.Hkv;
+  const int TPB = a.S / kTile;
+  const int W = a.hdr[0];
+  const int64_t Tot = (int64_t)a.prefix[U] * TPB;
+  const int64_t ylo = (int64_t)a.prefix[u] * TPB, yhi = (int64_t)a.prefix[u + 1] * TPB;
+  int wlo = 0, whi = -1;
+  if (yhi > ylo) {
+    wlo = (int)(((ylo + 1) * W - 1) / Tot);
+    whi = (int)((yhi * W - 1) / Tot);
+  }
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  constexpr int REC = G * D + 16;
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, i = idx - h * D;
+    float M = kNegInf;
+    for (int w = wlo; w <= whi; ++w) {
+      if ((int64_t)w * Tot / W == (int64_t)(w + 1) * Tot / W) continue;  // empty wave
+      M = fmaxf(M, a.part[(int64_t)(u + w) * REC + G * D + h]);
+    }
+    float ls = 0.f, o = 0.f;
+    if (M != kNegInf) {
+      for (int w = wlo; w <= whi; ++w) {
+        if ((int64_t)w * Tot / W == (int64_t)(w + 1) * Tot / W) continue;
+        const float* rec = a.part + (int64_t)(u + w) * REC;
+        const float mw = rec[G * D + h];
+        if (mw == kNegInf) continue;
+        const float sc = exp2f(mw - M);
+        ls += rec[G * D + 8 + h] * sc;
+        o += rec[h * D + i] * sc;
+      }
+    }
+    const int64_t head = (int64_t)b * a.Hq + (int64_t)g * G + h;
+    a.out[head * D + i] = ls > 0.f ? o / ls : 0.f;
+    if (i == 0 && a.lse) a.lse[head] = ls > 0.f ? (M + log2f(ls)) * 0.69314718055994530942f : kNegInf;
+  }
+}
+
+template <typename T, int D, int G>
+const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G>; }
+
+using KernelFn = const void* (*)();
+
+template <typename T, int D>
+KernelFn pick_g(int G) {
+  switch (G) {
+    case 1: return &partial_fn<T, D, 1>;
+    case 2: return &partial_fn<T, D, 2>;
+    case 3: return &partial_fn<T, D, 3>;
+    case 4: return &partial_fn<T, D, 4>;
+    case 5: return &partial_fn<T, D, 5>;
+    case 6: return &partial_fn<T, D, 6>;
+    case 7: return &partial_fn<T, D, 7>;
+    case 8: return &partial_fn<T, D, 8>;
+  }
+  return nullptr;
+}
+
+const void* partial_kernel(int dtype, int D, int G) {
+  KernelFn f = nullptr;
+  if (dtype == 1) f = D == 64 ? pick_g<uint16_t, 64>(G) : D == 128 ? pick_g<uint16_t, 128>(G) : nullptr;
+  else f = D == 64 ? pick_g<float, 64>(G) : D == 128 ? pick_g<float, 128>(G) : nullptr;
+  return f ? f() : nullptr;
+}
+
+template <int D>
+const void* combine_g(int G) {
+  switch (G) {
+    case 1: return (const void*)&decode_combine_kernel<D, 1>;
+    case 2: return (const void*)&decode_combine_kernel<D, 2>;
+    case 3: return (const void*)&decode_combine_kernel<D, 3>;
+    case 4: return (const void*)&decode_combine_kernel<D, 4>;
+    case 5: return (const void*)&decode_combine_kernel<D, 5>;
+    case 6: return (const void*)&decode_combine_kernel<D, 6>;
+    case 7: return (const void*)&decode_combine_kernel<D, 7>;
+    case 8: return (const void*)&decode_combine_kernel<D, 8>;
+  }
+  return nullptr;
+}
+
+size_t prefix_smem_bytes(int U) { return (size_t)(U + 1 + kWavesPerWG + 1) * sizeof(int); }
+
+}  // namespace
+
+size_t decode_part_offset(int U) {
+  const size_t head = 64 + (size_t)(U + 1) * sizeof(int32_t);
+  return (head + 255) & ~(size_t)255;
+}
+
+size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int wmax) {
+  const int U = B * Hkv;
+  return decode_part_offset(U) + (size_t)(U + wmax) * (G * D + 16) * sizeof(float);
+}
+
+int decode_max_waves(int dtype, int D, int G) {
+  const void* fn = partial_kernel(dtype, D, G);
+  if (!fn) return 0;
+  int dev = 0, cus = 0, blocks = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  // Occupancy with the largest plan buffer, so that the count is an upper bound.
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess) return 0;
+  if (blocks < 1) blocks = 1;
+  return cus * blocks * kWavesPerWG;
+}
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const void* fn = partial_kernel(a.dtype, a.D, G);
+  if (!fn) return hipErrorInvalidValue;
+  const int U = a.B * a.Hkv;
+  DecodeArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(fn, dim3(a.W / kWavesPerWG), dim3(kThreads), params,
+                         prefix_smem_bytes(U), stream);
+}
+
+hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const void* fn = a.D == 64 ? combine_g<64>(G) : a.D == 128 ? combine_g<128>(G) : nullptr;
+  if (!fn) return hipErrorInvalidValue;
+  CombineArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(256), params, 0, stream);
+}
+
+}  // namespace seer

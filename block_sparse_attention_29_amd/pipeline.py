@@ -1,0 +1,82 @@
+"""One gated block-sparse decode step, wired from the libseer calls.
+
+``DecodeState`` owns the device buffers of one attention layer (pooled-key
+table, open-block sums, scores, selection, outputs, workspace) and enqueues:
+
+    build_pool(lens)             bulk key pooling after prefill
+    append(lens_old, lens_new)   incremental pooling of newly cached tokens
+    select(q, lens)              gate scores + top-k block selection
+    attend(q, lens)              sparse (or dense) decode attention
+
+all on torch's current stream, with no host synchronisation.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import seer
+
+
+class DecodeState:
+    def __init__(self, *, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, max_blocks: int, dtype: torch.dtype, k: torch.Tensor,
+                 v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                 k_max: Optional[int] = None, keep: Optional[tuple] = None,
+                 top_k: Optional[torch.Tensor] = None):
+        self.shape = seer.make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks, dtype)
+        self.k, self.v, self.page_table = k, v, page_table
+        self.kv = seer.make_kv(k, v, page_table)
+        self.keep = keep
+        self.top_k = top_k
+        if k_max is None:
+            if keep is not None:
+                k_max = seer.keep_blocks(max_blocks, keep[0], keep[1])
+            else:
+                k_max = max_blocks
+        self.k_max = int(k_max)
+        dev = k.device
+        U = batch * num_kv_heads
+        self.pooled = torch.zeros(U * head_dim * max_blocks, dtype=torch.float32, device=dev)
+        self.open_sum = torch.zeros(U * head_dim, dtype=torch.float64, device=dev)
+        self.scores = torch.zeros(U * max_blocks, dtype=torch.float64, device=dev)
+        self.sel_idx = torch.full((U, self.k_max), -1, dtype=torch.int32, device=dev)
+        self.sel_cnt = torch.zeros(U, dtype=torch.int32, device=dev)
+        self.out = torch.zeros((batch, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+        self.lse = torch.zeros((batch, num_q_heads), dtype=torch.float32, device=dev)
+        self.workspace = seer.alloc_workspace(self.shape, dev)
+
+    # pooling ---------------------------------------------------------------
+    def build_pool(self, lens: torch.Tensor):
+        seer.block_pool_keys(self.shape, self.kv, None, lens, self.pooled, self.open_sum)
+
+    def append(self, lens_old: torch.Tensor, lens_new: torch.Tensor):
+        seer.block_pool_keys(self.shape, self.kv, lens_old, lens_new, self.pooled, self.open_sum)
+
+    # selection -------------------------------------------------------------
+    def select(self, q: torch.Tensor, lens: torch.Tensor):
+        num, den = self.keep if self.keep is not None else (1, 1)
+        seer.gate_scores_topk(self.shape, q, self.pooled, lens, self.top_k, num, den, self.k_max,
+                              self.scores, self.sel_idx, self.sel_cnt)
+
+    # attention -------------------------------------------------------------
+    def attend(self, q: torch.Tensor, lens: torch.Tensor, dense: bool = False,
+               sel_idx: Optional[torch.Tensor] = None, sel_cnt: Optional[torch.Tensor] = None,
+               k_max: Optional[int] = None):
+        if dense:
+            si, sc, km = None, None, self.shape.max_blocks
+        elif sel_idx is not None:
+            si, sc, km = sel_idx, sel_cnt, int(k_max if k_max is not None else sel_idx.shape[-1])
+        else:
+            si, sc, km = self.sel_idx, self.sel_cnt, self.k_max
+        seer.sparse_decode(self.shape, q, self.kv, lens, si, sc, km, self.out, self.lse,
+                           self.workspace)
+        return self.out, self.lse
+
+    def step(self, q: torch.Tensor, lens: torch.Tensor):
+        """Gate, select and attend: one decode step over a built pooled table."""
+        self.select(q, lens)
+        return self.attend(q, lens)

@@ -1,0 +1,191 @@
+/*
+ * libseer: gated block-sparse decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of one attention layer: every sequence has one new query
+ * token; its query heads attend, in groups of G = Hq / Hkv heads per KV head
+ * (grouped-query attention), to a KV cache cut into blocks of S tokens.  For
+ * every (sequence, KV head) the blocks are scored against the group's query
+ * through a pooled summary of each block's keys, the top-scoring blocks are
+ * kept, and exact softmax attention runs over the kept blocks only.
+ *
+ * Sources: "SeerAttention-R: Sparse Attention Adaptation for Long Reasoning"
+ * (Abstract; AI Summary) -- block-level gating on pooled keys with the query
+ * not pooled, block sizes 64/128, 90% sparsity or a token budget, a sparse
+ * decoding kernel; "Sparse Attention Reasoning" (Step 1: top-k selection from
+ * gate scores; Step 4: softmax(QK^T/sqrt(d)) with unselected keys masked).
+ * The gate is parameter free: the score of block j for KV head g is
+ *     s_j = sum_{h in group g} q_h . P_j / sqrt(d),
+ * P_j the fp32-stored mean of the block's valid keys.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every pointer except `shape`/`kv` structs and host-only helpers is a
+ *    device pointer.  The caller allocates and owns all memory; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` and is asynchronous; no call synchronises.
+ *  - Arguments are validated on the host before anything is enqueued: a bad
+ *    argument returns SEER_ERR_INVALID_ARG / SEER_ERR_UNSUPPORTED /
+ *    SEER_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *    SEER_ERR_HIP.  seer_last_error() describes the last failure of the
+ *    calling thread.  Nothing aborts and no exception crosses this interface.
+ *  - Values that live on the device (lengths, counts, block ids, page ids)
+ *    cannot be checked without a synchronisation.  Their contract is stated
+ *    per call; kernels skip out-of-range ids instead of reading out of bounds.
+ *  - Calls that share output or scratch buffers on one stream are ordered by
+ *    the stream; concurrent calls on different streams must not share them.
+ *
+ * Supported: head_dim d in {64, 128}; block_size S in {64, 128}; G = Hq/Hkv in
+ * 1..8; dtype fp32 or bf16 for q, k, v (one dtype for all three); at most
+ * SEER_MAX_UNITS (sequence, KV head) pairs.  Outputs are fp32.
+ */
+#ifndef SEER_H_
+#define SEER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SEER_MAX_UNITS 8192
+
+typedef enum seer_status {
+  SEER_OK = 0,
+  SEER_ERR_INVALID_ARG = 1,  /* null pointer, inconsistent sizes, bad rule */
+  SEER_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set above */
+  SEER_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  SEER_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} seer_status;
+
+typedef enum seer_dtype { SEER_F32 = 0, SEER_BF16 = 1 } seer_dtype;
+
+/* Problem shape, shared by all calls. */
+typedef struct seer_shape {
+  int32_t batch;        /* B: sequences */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv; Hq must be a multiple of Hkv */
+  int32_t head_dim;     /* d */
+  int32_t block_size;   /* S: tokens per block (= tokens per page when paged) */
+  int32_t max_blocks;   /* NB: blocks per sequence that the cache and tables hold */
+  int32_t dtype;        /* seer_dtype of q, k and v */
+} seer_shape;
+
+/* The KV cache.
+ *  page_table == NULL: contiguous, k and v are [B][Hkv][NB*S][d] (the
+ *    (batch, heads, key_len, head_dim) layout of "Sparse Attention
+ *    Reasoning", Step 4), row t of sequence b / head g at
+ *    ((b*Hkv + g)*NB*S + t)*d.
+ *  page_table != NULL: [B][NB] int32 page ids; k and v are pools
+ *    [num_pages][Hkv][S][d]; block j of sequence b lives in page
+ *    page_table[b*NB + j].  Ids outside [0, num_pages) make that block empty. */
+typedef struct seer_kv {
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  int64_t num_pages;
+} seer_kv;
+
+/* Pooled-key table layout used by the calls below (fp32, "d-major"):
+ *   pooled[((b*Hkv + g)*d + i)*NB + j] = mean over the valid tokens t of block j
+ *   of k[b][g][t][i], the sum taken in fp64 in token order, divided by the
+ *   block's token count and rounded to fp32 (nearest even).
+ * open_sum[(b*Hkv + g)*d + i] = the fp64 sum of the last block's keys.
+ * Keys are pooled per block; the query is not ("SeerAttention-R", Abstract). */
+
+/* seer_block_pool_keys -- builds or extends the pooled-key table.
+ *
+ *  lens_old == NULL: bulk build.  Writes pooled[..][j] for every block
+ *    j < ceil(lens_new[b] / S) and open_sum, from the first lens_new[b] tokens.
+ *  lens_old != NULL: incremental append of tokens lens_old[b] .. lens_new[b]-1
+ *    (their keys must already be in the cache).  The fp64 running sum in
+ *    open_sum restarts when a token opens a new block; the pooled column of
+ *    every block that gets a token is rewritten.  Bit-identical to a bulk build
+ *    over lens_new tokens.  Requires the table to be built up to lens_old.
+ *  Device contract: 1 <= lens_new[b] <= NB*S; lens_old[b] <= lens_new[b]
+ *  (sequences with lens_old[b] >= lens_new[b] are left unchanged).
+ *  pooled: [B][Hkv][d][NB] fp32; open_sum: [B][Hkv][d] fp64 (in/out). */
+seer_status seer_block_pool_keys(const seer_shape* shape, const seer_kv* kv,
+                                 const int32_t* lens_old, const int32_t* lens_new,
+                                 float* pooled, double* open_sum, hipStream_t stream);
+
+/* seer_gate_scores_topk -- gate scores and top-k block selection.
+ *
+ *  q: [B][Hq][d] (shape->dtype).  pooled: the table above.  lens: [B] tokens
+ *  per sequence including the new one (1 <= lens[b] <= NB*S); n_b =
+ *  ceil(lens[b] / S).
+ *  Kept count k_b ("Sparse Attention Reasoning", Step 1; "SeerAttention-R",
+ *  Abstract: 90% sparsity, 4K token budget):
+ *    top_k != NULL: k_b = clamp(top_k[b], 1, n_b) (a token budget T is
+ *      top_k = T / S), then at most k_max;
+ *    top_k == NULL: k_b = max(1, min(n_b, ceil(n_b * keep_num / keep_den)))
+ *      in integer arithmetic (90% sparsity: keep_num = 1, keep_den = 10);
+ *      requires 1 <= keep_num <= keep_den and that NB blocks keep <= k_max.
+ *  Order: score descending, ties to the lower block id, -0.0 == +0.0; scores
+ *  must be finite.
+ *  scores: [B][Hkv][NB] fp64 out, s_j for j < n_b (the rest untouched).
+ *  sel_idx: [B][Hkv][k_max] int32 out: the kept ids in ascending order, then -1.
+ *  sel_cnt: [B][Hkv] int32 out: k_b. */
+seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const float* pooled,
+                                  const int32_t* lens, const int32_t* top_k, int32_t keep_num,
+                                  int32_t keep_den, int32_t k_max, double* scores,
+                                  int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
+
+/* Bytes of workspace seer_sparse_decode needs for this shape on the current
+ * device (it depends on the device's compute-unit count). */
+seer_status seer_sparse_decode_workspace_size(const seer_shape* shape, size_t* bytes);
+
+/* seer_sparse_decode -- exact softmax attention over the kept blocks.
+ *
+ *  For every query head h of sequence b, with g = h / G:
+ *    T = { valid tokens t < lens[b] of the blocks sel_idx[b][g][0..sel_cnt[b][g]) },
+ *    out[b][h] = sum_{t in T} softmax_t(l) v_t,  l_t = scale * (q_h . k_t),
+ *    lse[b][h] = log sum_{t in T} exp(l_t)  (natural log),
+ *  the attention of "Sparse Attention Reasoning", Step 4, with every key
+ *  outside T masked to -inf, computed without touching keys outside T.
+ *  sel_idx == NULL: dense decode, T = all lens[b] tokens (sel_cnt unused).
+ *  sel_idx/sel_cnt: as written by seer_gate_scores_topk, or any ids in
+ *  [0, n_b) (order free, no duplicates); ids outside [0, n_b) and counts
+ *  outside [0, k_max] are skipped/clamped.  A head with no token gets out = 0
+ *  and lse = -inf.
+ *  softmax_scale <= 0 selects 1/sqrt(d).
+ *  out: [B][Hq][d] fp32; lse: [B][Hq] fp32 or NULL.
+ *  workspace: seer_sparse_decode_workspace_size bytes of device scratch; its
+ *  contents need no initialisation and are overwritten. */
+seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
+                               const int32_t* lens, const int32_t* sel_idx,
+                               const int32_t* sel_cnt, int32_t k_max, float softmax_scale,
+                               float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* The two stages of seer_sparse_decode, for callers that time or overlap them:
+ * _partial streams the kept K/V and leaves per-split partial results in the
+ * workspace (with the split plan); _combine reads them and merges them by
+ * log-sum-exp into out/lse.  _partial followed by _combine on the same
+ * workspace and stream is exactly seer_sparse_decode. */
+seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
+                                       const int32_t* lens, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t k_max,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
+                                       const void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* Host helper: max(1, min(n, ceil(n * keep_num / keep_den))), or -1 for bad
+ * arguments (n < 1, keep_num < 1, keep_den < keep_num). */
+int32_t seer_keep_blocks(int32_t n_blocks, int32_t keep_num, int32_t keep_den);
+
+/* Static name of a status code. */
+const char* seer_status_str(int32_t status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* seer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEER_H_ */

@@ -1,0 +1,126 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every entry point include/seer.h declares, and
+reject bad arguments with the documented status before any device work.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_29_amd import seer
+from oracle import seer_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seer_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(seer.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_keep_blocks_matches_oracle(lib):
+    for frac in ((1, 10), (1, 20), (1, 4), (3, 10), (1, 1)):
+        for n in list(range(1, 300)) + [1024, 1025, 1026, 8192]:
+            assert seer.keep_blocks(n, *frac) == O.keep_count(n, *frac)
+    assert seer.keep_blocks(0, 1, 10) == -1
+    assert seer.keep_blocks(10, 0, 10) == -1
+    assert seer.keep_blocks(10, 11, 10) == -1
+
+
+def test_status_strings(lib):
+    assert lib.seer_status_str(0) == b"SEER_OK"
+    assert lib.seer_status_str(3) == b"SEER_ERR_WORKSPACE"
+    assert lib.seer_status_str(99) == b"SEER_STATUS_UNKNOWN"
+
+
+def _shape(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
+                max_blocks=16, dtype=seer.SEER_BF16)
+    base.update(kw)
+    return seer.Shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), seer.SEER_ERR_INVALID_ARG),
+    (dict(num_q_heads=7), seer.SEER_ERR_INVALID_ARG),
+    (dict(dtype=5), seer.SEER_ERR_INVALID_ARG),
+    (dict(num_q_heads=18), seer.SEER_ERR_UNSUPPORTED),      # G = 9
+    (dict(head_dim=96), seer.SEER_ERR_UNSUPPORTED),
+    (dict(block_size=32), seer.SEER_ERR_UNSUPPORTED),
+    (dict(max_blocks=8193), seer.SEER_ERR_UNSUPPORTED),
+    (dict(batch=4097, num_q_heads=2, num_kv_heads=2), seer.SEER_ERR_UNSUPPORTED),
+])
+def test_shape_validation(lib, kw, status):
+    sh = _shape(**kw)
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), FAKE, FAKE, FAKE, None, 1, 10, 4, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == status, lib.seer_last_error()
+    assert lib.seer_last_error()
+
+
+def test_pointer_and_rule_validation(lib):
+    sh = _shape()
+    kv = seer.KV(0x1000, 0x1000, None, 0)
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), None, FAKE, FAKE, None, 1, 10, 4, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    # keep rule that keeps more blocks than k_max can hold
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), FAKE, FAKE, FAKE, None, 1, 2, 4, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"k_max" in lib.seer_last_error()
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), FAKE, FAKE, FAKE, None, 3, 2, 16, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), FAKE, FAKE, FAKE, None, 1, 10, 0, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    # pooling
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), None, None, FAKE, FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    bad_kv = seer.KV(0x1000, None, None, 0)
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), ctypes.byref(bad_kv), None, FAKE, FAKE,
+                                  FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    paged0 = seer.KV(0x1000, 0x1000, 0x1000, 0)
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), ctypes.byref(paged0), None, FAKE, FAKE,
+                                  FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), ctypes.byref(kv), None, None, FAKE, FAKE,
+                                  None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    # decode
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, FAKE, None, 4,
+                                ctypes.c_float(0.0), FAKE, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"sel_cnt" in lib.seer_last_error()
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, FAKE, FAKE, 17,
+                                ctypes.c_float(0.0), FAKE, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, 0,
+                                ctypes.c_float(float("nan")), FAKE, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, 0,
+                                ctypes.c_float(0.0), FAKE, None, None, 1 << 20, None)
+    assert st == seer.SEER_ERR_WORKSPACE
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, 0,
+                                ctypes.c_float(0.0), None, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG
+    st = lib.seer_sparse_decode_combine(ctypes.byref(sh), None, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG

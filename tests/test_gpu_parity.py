@@ -1,0 +1,358 @@
+"""GPU parity of the libseer kernels against the fp64 oracle (run on an MI355X).
+
+Bars: pooled keys, open sums, block ids and kept counts are bit-exact; gate
+scores agree to 1e-12 of the unit's largest score; outputs and log-sum-exps
+agree to max-abs 2e-3 for bf16 inputs and 1e-5 for fp32 inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_29_amd import seer
+from block_sparse_attention_29_amd.pipeline import DecodeState
+from oracle import seer_oracle as O
+from tests.gpu_util import TOL, f64, oracle_unit, unit_kv
+from workloads import WORKLOADS, make_case
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def state_for(case, **kw):
+    wl = case.wl
+    return DecodeState(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                       head_dim=wl.head_dim, block_size=wl.block_size, max_blocks=wl.max_blocks,
+                       dtype=DT[wl.dtype], k=case.k, v=case.v, page_table=case.page_table,
+                       keep=wl.keep, top_k=case.top_k, **kw)
+
+
+def gpu_pooled(st, wl, b, g, n):
+    D, NB = wl.head_dim, wl.max_blocks
+    u = b * wl.num_kv_heads + g
+    t = st.pooled.view(-1, D, NB)[u, :, :n]
+    return t.t().contiguous().cpu().numpy()
+
+
+def units_of(wl, limit=None, seed=0):
+    all_u = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    if limit is None or limit >= len(all_u):
+        return all_u
+    rng = np.random.default_rng(seed)
+    idx = sorted(rng.choice(len(all_u), size=limit, replace=False).tolist())
+    # always include the first and the last unit
+    return sorted(set([all_u[0], all_u[-1]] + [all_u[i] for i in idx]))
+
+
+def check_unit(st, case, q, lens_host, b, g, *, sel_only=False, tag=""):
+    wl = case.wl
+    L = int(lens_host[b])
+    n = O.block_count(L, wl.block_size)
+    ref = oracle_unit(case, b, g, q, L, keep=wl.keep, top_k=wl.top_k)
+    u = b * wl.num_kv_heads + g
+    # pooled keys: bit-exact
+    got_p = gpu_pooled(st, wl, b, g, n)
+    assert np.array_equal(got_p.view(np.uint32), ref["pooled"].view(np.uint32)), f"{tag} pooled {b},{g}"
+    # scores
+    got_s = st.scores.view(-1, wl.max_blocks)[u, :n].cpu().numpy()
+    scale = max(np.abs(ref["scores"]).max(), 1e-300)
+    assert np.abs(got_s - ref["scores"]).max() <= 1e-12 * scale, f"{tag} scores {b},{g}"
+    # selection: bit-exact ids and count
+    cnt = int(st.sel_cnt[u])
+    ids = st.sel_idx[u].cpu().numpy()
+    assert cnt == len(ref["sel"]), f"{tag} count {b},{g}: {cnt} vs {len(ref['sel'])}"
+    assert np.array_equal(ids[:cnt], ref["sel"]), f"{tag} ids {b},{g}"
+    assert (ids[cnt:] == -1).all()
+    if sel_only:
+        return ref
+    G = wl.group
+    out = st.out[b, g * G:(g + 1) * G].cpu().double().numpy()
+    lse = st.lse[b, g * G:(g + 1) * G].cpu().double().numpy()
+    tol = TOL[wl.dtype]
+    assert np.abs(out - ref["out"]).max() <= tol, f"{tag} out {b},{g}: {np.abs(out - ref['out']).max()}"
+    assert np.abs(lse - ref["lse"]).max() <= tol, f"{tag} lse {b},{g}"
+    return ref
+
+
+# ------------------------------------------------------------------ small configs
+
+SMALL = {
+    "tiny_1k": WORKLOADS["tiny_1k"],
+    "planted_b2": WORKLOADS["planted_8k"].with_(batch=2),
+    "paged_small": WORKLOADS["paged_var"].with_(batch=5, variable_context=(1, 700)),
+    "long_small": WORKLOADS["long_131k"].with_(batch=2, context=3000, decode_steps=0),
+    "f32_d128_s128_g1": WORKLOADS["tiny_1k"].with_(num_q_heads=2, num_kv_heads=2, head_dim=128,
+                                                  block_size=128, context=1300, top_k=3),
+    "bf16_d64_g8": WORKLOADS["tiny_1k"].with_(dtype="bf16", num_q_heads=16, num_kv_heads=2,
+                                              context=777, top_k=5),
+    "bf16_g3_keep": WORKLOADS["planted_8k"].with_(batch=3, num_q_heads=6, num_kv_heads=2,
+                                                 context=641, planted_fraction=None,
+                                                 keep=(3, 10)),
+    "f32_g5_paged": WORKLOADS["paged_var"].with_(dtype="f32", batch=3, num_q_heads=10,
+                                                num_kv_heads=2, variable_context=(60, 400)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_full_chain_small(name):
+    wl = SMALL[name]
+    print(f"[case] full chain {name}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    lens = case.lens.tolist()
+    for (b, g) in units_of(wl):
+        check_unit(st, case, case.q, lens, b, g, tag=name)
+
+
+@pytest.mark.parametrize("name", ["tiny_1k", "paged_small", "bf16_d64_g8"])
+def test_dense_matches_oracle(name):
+    wl = SMALL[name]
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.attend(case.q, case.lens, dense=True)
+    torch.cuda.synchronize()
+    G = wl.group
+    for (b, g) in units_of(wl):
+        L = int(case.lens[b])
+        ref = oracle_unit(case, b, g, case.q, L, dense=True)
+        out = st.out[b, g * G:(g + 1) * G].cpu().double().numpy()
+        lse = st.lse[b, g * G:(g + 1) * G].cpu().double().numpy()
+        assert np.abs(out - ref["out"]).max() <= TOL[wl.dtype]
+        assert np.abs(lse - ref["lse"]).max() <= TOL[wl.dtype]
+
+
+def test_decode_with_oracle_selection():
+    """Attention fed the oracle's ids (random subsets, any order) matches the oracle."""
+    wl = SMALL["planted_b2"]
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    rng = np.random.default_rng(3)
+    U = wl.batch * wl.num_kv_heads
+    n = O.block_count(wl.context, wl.block_size)
+    k_max = 20
+    sel = np.full((U, k_max), -1, np.int32)
+    cnt = np.zeros(U, np.int32)
+    chosen = {}
+    for u in range(U):
+        c = int(rng.integers(1, k_max + 1))
+        ids = rng.choice(n, size=c, replace=False)
+        sel[u, :c] = ids          # deliberately unsorted
+        cnt[u] = c
+        chosen[u] = ids
+    st.attend(case.q, case.lens, sel_idx=torch.from_numpy(sel).cuda(),
+              sel_cnt=torch.from_numpy(cnt).cuda(), k_max=k_max)
+    torch.cuda.synchronize()
+    G = wl.group
+    for u in range(U):
+        b, g = divmod(u, wl.num_kv_heads)
+        ref = oracle_unit(case, b, g, case.q, wl.context, sel=chosen[u])
+        out = st.out[b, g * G:(g + 1) * G].cpu().double().numpy()
+        assert np.abs(out - ref["out"]).max() <= TOL["bf16"]
+
+
+def test_paged_equals_contiguous_bitwise():
+    wl = SMALL["paged_small"]
+    case = make_case(wl, "cuda")
+    flat = wl.with_(paged=False)
+    case_c = make_case(flat, "cuda")
+    # same draws: the paged pools hold exactly the contiguous rows
+    st_p, st_c = state_for(case), state_for(case_c)
+    for st, c in ((st_p, case), (st_c, case_c)):
+        st.build_pool(c.lens)
+        st.step(c.q, c.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(st_p.pooled, st_c.pooled)
+    assert torch.equal(st_p.sel_idx, st_c.sel_idx)
+    assert torch.equal(st_p.out, st_c.out) and torch.equal(st_p.lse, st_c.lse)
+
+
+@pytest.mark.parametrize("name", ["paged_small", "long_small", "tiny_1k"])
+def test_nan_poison_never_reaches_outputs(name):
+    wl = SMALL[name]
+    clean, dirty = make_case(wl, "cuda"), make_case(wl, "cuda", poison=True)
+    outs = []
+    for c in (clean, dirty):
+        st = state_for(c)
+        st.out.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        st.build_pool(c.lens)
+        st.step(c.q, c.lens)
+        torch.cuda.synchronize()
+        assert torch.isfinite(st.out).all() and torch.isfinite(st.lse).all()
+        outs.append((st.pooled.clone(), st.sel_idx.clone(), st.out.clone(), st.lse.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_repeatable_bitwise():
+    wl = SMALL["paged_small"]
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    ref = None
+    for _ in range(10):
+        st.step(case.q, case.lens)
+        cur = (st.sel_idx.clone(), st.out.clone(), st.lse.clone())
+        if ref is None:
+            ref = cur
+        else:
+            for a, b in zip(ref, cur):
+                assert torch.equal(a, b)
+
+
+def test_split_stages_equal_fused():
+    wl = SMALL["bf16_g3_keep"]
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    out1, lse1 = st.out.clone(), st.lse.clone()
+    st.out.zero_()
+    seer.sparse_decode_partial(st.shape, case.q, st.kv, case.lens, st.sel_idx, st.sel_cnt,
+                               st.k_max, st.workspace)
+    seer.sparse_decode_combine(st.shape, st.out, st.lse, st.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, st.out) and torch.equal(lse1, st.lse)
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # (name, overrides): lengths 1, S+1, k = 1, k = n, G = 1, d/S/dtype corners
+    ("len1", dict(context=1, top_k=1)),
+    ("len_s_plus_1", dict(context=65, top_k=1)),
+    ("k1", dict(context=1000, top_k=1)),
+    ("k_all", dict(context=1000, top_k=16)),
+    ("k_over", dict(context=1000, top_k=99)),
+    ("g1_bf16", dict(dtype="bf16", num_q_heads=1, num_kv_heads=1, context=513, top_k=2)),
+    ("d128_s128_bf16", dict(dtype="bf16", head_dim=128, block_size=128, context=1025, top_k=3)),
+    ("d64_s128_f32", dict(block_size=128, context=1000, top_k=2)),
+    ("g8_d128_f32", dict(num_q_heads=8, head_dim=128, context=700, top_k=4)),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(name, kw):
+    wl = WORKLOADS["tiny_1k"].with_(**kw)
+    print(f"[case] edge {name}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case, k_max=min(wl.max_blocks, max(1, wl.top_k)))
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    for (b, g) in units_of(wl):
+        check_unit(st, case, case.q, case.lens.tolist(), b, g, tag=name)
+
+
+def test_ties_and_zero_query():
+    """Duplicated blocks and a zero query: ties go to the lower block id."""
+    wl = WORKLOADS["planted_8k"].with_(batch=1, planted_fraction=None, context=2048)
+    case = make_case(wl, "cuda")
+    S = wl.block_size
+    # blocks 5 and 20 identical (keys and values), and block 7 == block 3
+    for dst, src in ((20, 5), (7, 3)):
+        case.k[:, :, dst * S:(dst + 1) * S] = case.k[:, :, src * S:(src + 1) * S]
+        case.v[:, :, dst * S:(dst + 1) * S] = case.v[:, :, src * S:(src + 1) * S]
+    case.q[:, :8] = 0          # KV heads 0 and 1 see a zero query: scores all zero
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    for g in range(wl.num_kv_heads):
+        ref = check_unit(st, case, case.q, case.lens.tolist(), 0, g, tag="ties")
+        if g < 2:
+            assert list(ref["sel"]) == list(range(len(ref["sel"])))
+
+
+# ------------------------------------------------------------------ pooling
+
+def test_incremental_pooling_bitwise():
+    wl = WORKLOADS["long_131k"].with_(batch=3, context=200, decode_steps=700)
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    L0 = wl.context
+    lens = torch.full((wl.batch,), L0, dtype=torch.int32, device="cuda")
+    st.build_pool(lens)
+    steps = [1, 1, 55, 1, 127, 128, 1, 200, 1, 1, 180]
+    cur = L0
+    for inc in steps:
+        new = torch.full_like(lens, cur + inc)
+        st.append(lens, new)
+        lens, cur = new, cur + inc
+    torch.cuda.synchronize()
+    fresh = state_for(case)
+    fresh.build_pool(lens)
+    torch.cuda.synchronize()
+    assert torch.equal(st.pooled, fresh.pooled)
+    assert torch.equal(st.open_sum, fresh.open_sum)
+    for b in range(wl.batch):
+        for g in (0, wl.num_kv_heads - 1):
+            k, _ = unit_kv(case, b, g, cur)
+            p32, _, open_sum = O.pool_keys(k, cur, wl.block_size)
+            n = O.block_count(cur, wl.block_size)
+            assert np.array_equal(gpu_pooled(st, wl, b, g, n).view(np.uint32), p32.view(np.uint32))
+            u = b * wl.num_kv_heads + g
+            got_open = st.open_sum.view(-1, wl.head_dim)[u].cpu().numpy()
+            assert np.array_equal(got_open.view(np.uint64), open_sum.view(np.uint64))
+
+
+# ------------------------------------------------------------------ full sizes
+
+@pytest.mark.parametrize("name", ["planted_8k", "budget_32k", "sparse90_32k", "paged_var"])
+def test_full_size_workloads(name):
+    wl = WORKLOADS[name]
+    print(f"[case] full size {name}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    lens = case.lens.tolist()
+    for (b, g) in units_of(wl, limit=6, seed=1):
+        check_unit(st, case, case.q, lens, b, g, tag=name)
+    if case.planted is not None:
+        U = wl.batch * wl.num_kv_heads
+        sel = st.sel_idx.cpu().numpy()
+        pl = case.planted.view(U, -1).cpu().numpy()
+        for u in range(U):
+            assert set(pl[u].tolist()) <= set(sel[u].tolist())
+    # every kept count follows the rule for its sequence
+    cnt = st.sel_cnt.view(wl.batch, wl.num_kv_heads).cpu().numpy()
+    for b in range(wl.batch):
+        n = O.block_count(lens[b], wl.block_size)
+        want = O.clamp_count(wl.top_k, n) if wl.top_k else O.keep_count(n, *wl.keep)
+        assert (cnt[b] == want).all()
+
+
+def test_long_decode_loop():
+    """256 decode steps at 131K context: pooling append + gate + sparse decode."""
+    wl = WORKLOADS["long_131k"]
+    print("[case] long decode loop", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    L0 = wl.context
+    lens = torch.full((wl.batch,), L0, dtype=torch.int32, device="cuda")
+    st.build_pool(lens)
+    check_steps = {0, 1, 126, 127, 128, 255}
+    sample = [(0, 0), (wl.batch - 1, wl.num_kv_heads - 1), (1, 3)]
+    for i in range(wl.decode_steps):
+        new = lens + 1
+        st.append(lens, new)
+        q = case.q[i]
+        st.step(q, new)
+        lens = new
+        if i in check_steps:
+            torch.cuda.synchronize()
+            lh = lens.tolist()
+            for (b, g) in sample:
+                check_unit(st, case, q, lh, b, g, tag=f"step{i}")
+    torch.cuda.synchronize()
+    fresh = state_for(case)
+    fresh.build_pool(lens)
+    torch.cuda.synchronize()
+    assert torch.equal(st.pooled, fresh.pooled)
+    assert torch.equal(st.open_sum, fresh.open_sum)
