@@ -8,6 +8,9 @@ is built once beforehand (after prefill).  The timed loop cycles through
 ``--layers`` independent caches (one per attention layer of a model), so no
 step finds its KV bytes in the 256 MB last-level cache.
 
+Timed regions are replays of HIP graphs captured from the library's launches
+(as a serving loop would run them), bracketed by events on the launch stream.
+
 Prints one JSON line.  ``value`` is decode tokens/s (sequences x steps / time);
 ``roofline`` reports the partial-decode kernel's algorithmic bytes per launch
 over its mean launch time (HIP events on the launch stream) against the 8 TB/s
@@ -90,43 +93,62 @@ def main():
                                    st.k_max, st.workspace)
         seer.sparse_decode_combine(st.shape, st.out, st.lse, st.workspace)
 
-    # ---- whole-step timing ----
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def partial_only(i):
+        st, case = states[i % args.layers], cases[i % args.layers]
+        seer.sparse_decode_partial(st.shape, case.q, st.kv, case.lens, st.sel_idx, st.sel_cnt,
+                                   st.k_max, st.workspace)
+
+    def dense_step(i):
+        st, case = states[i % args.layers], cases[i % args.layers]
+        st.attend(case.q, case.lens, dense=True)
+
+    def capture(fn, n):
+        """One HIP graph of n consecutive calls of fn (launch gaps off the host)."""
+        for i in range(min(n, 2 * args.layers)):   # eager warm-up before capture
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        return graph
+
+    def timed(graph, reps=1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        e0.record(cur)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # ---- whole-step timing: K steps in one graph, W warm-up steps before ----
+    g_steps = capture(step, args.steps)
+    if args.warmup > 0:
+        g_warm = capture(step, args.warmup)
+        timed(g_warm)
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
+    ms_total = timed(g_steps)
     wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
     ms_per_step = ms_total / args.steps
     tokens_per_s = wl.batch * args.steps / (ms_total / 1e3)
 
-    # ---- partial-kernel timing (events around each launch, same stream) ----
-    n_k = max(20, args.steps // 2)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_k)]
-    for i in range(n_k):
-        st, case = states[i % args.layers], cases[i % args.layers]
-        st.select(case.q, case.lens)
-        evs[i][0].record(stream)
-        seer.sparse_decode_partial(st.shape, case.q, st.kv, case.lens, st.sel_idx, st.sel_cnt,
-                                   st.k_max, st.workspace)
-        evs[i][1].record(stream)
-        seer.sparse_decode_combine(st.shape, st.out, st.lse, st.workspace)
-    torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # ---- partial-kernel timing: back-to-back launches in one graph, events
+    # around it on the launch stream (selections computed beforehand) ----
+    for i in range(args.layers):
+        states[i].select(cases[i].q, cases[i].lens)
+    n_k = max(4 * args.layers, args.steps // 2)
+    g_part = capture(partial_only, n_k)
+    timed(g_part)
+    k_ms = timed(g_part, 3) / (3 * n_k)
 
     # algorithmic bytes of one partial launch (layer 0): valid K/V tokens of the
     # kept blocks (bf16 K and V rows) plus the query
     st0, case0 = states[0], cases[0]
-    st0.select(case0.q, case0.lens)
     torch.cuda.synchronize()
     e = 2 if wl.dtype == "bf16" else 4
     S, d = wl.block_size, wl.head_dim
@@ -151,19 +173,9 @@ def main():
     # ---- dense decode at the same shape (speedup denominator) ----
     dense = None
     if args.dense_steps > 0:
-        for i in range(3):
-            st, case = states[i % args.layers], cases[i % args.layers]
-            st.attend(case.q, case.lens, dense=True)
-        torch.cuda.synchronize()
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for i in range(args.dense_steps):
-            st, case = states[i % args.layers], cases[i % args.layers]
-            st.attend(case.q, case.lens, dense=True)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = d0.elapsed_time(d1) / args.dense_steps
+        g_dense = capture(dense_step, args.dense_steps)
+        timed(g_dense)
+        dense_ms = timed(g_dense) / args.dense_steps
         dense_bytes = int(lens.sum()) * wl.num_kv_heads * d * e * 2 + q_bytes
         dense = {"ms_per_step": dense_ms,
                  "tokens_per_s": wl.batch / (dense_ms * 1e-3),

@@ -210,7 +210,7 @@ seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, c
       (int64_t)U * (sel_idx ? k_max : shape->max_blocks);
   const int64_t tiles_bound = blocks_bound * (shape->block_size / 16);  // 16-token tiles
   int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
-  W = (W + 3) / 4 * 4;
+  W = (W + seer::kDecodeWavesPerWG - 1) / seer::kDecodeWavesPerWG * seer::kDecodeWavesPerWG;
 
   const double scale = softmax_scale > 0.f ? (double)softmax_scale
                                            : 1.0 / sqrt((double)shape->head_dim);

@@ -8,21 +8,18 @@
 // Step 1: top-k over the gate's scores), ties to the lower block id, and
 // written in ascending id order.
 //
-// Two kernels:
-//  * gate_scores_kernel: one thread per block, grid (block chunks, units).  The
-//    pooled table is d-major, so the 64 lanes of a wave read 64 consecutive
-//    blocks' entries for one dimension per load (256 contiguous bytes).
-//  * topk_kernel: one workgroup per unit.  Exact radix select of the k-th
-//    largest order key (8 passes of 8 bits, LDS histogram), then the kept set
-//    is {key > tau} plus the lowest-indexed keys equal to tau, compacted in id
-//    order with block-wide scans.  Deterministic; no sorting network needed.
+// One kernel, one 1024-thread workgroup per unit: the scores (the pooled table
+// is d-major, so the 64 lanes of a wave read 64 consecutive blocks' entries
+// of one dimension per load, 256 contiguous bytes), then an exact radix select
+// of the kept set in LDS, compacted in id order with block-wide scans.
+// Deterministic; no sorting network needed.
 #include "seer_device.h"
 #include "seer_kernels.h"
 
 namespace seer {
 namespace {
 
-constexpr int kGateThreads = 256;
+constexpr int kTopkThreads = 1024;
 
 __device__ __forceinline__ int unit_nblocks(int L, int S, int NB) {
   if (L <= 0) return 0;
@@ -43,123 +40,165 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
   return (double)p[i];
 }
 
+// One workgroup per unit: scores for all blocks, then the selection.
+//
+// Scores (all 16 waves): block j's dot product is split over 4 thread
+// quarters of D/4 dimensions each (each a sequential fp64 FMA chain whose
+// loads are all issued up front), and the 4 partial sums are added in a fixed
+// order, so equal blocks get bit-identical scores.
+//
+// Selection (wave 0 alone, no block barriers): exact radix select over 64-bit
+// order keys, 8 bits per pass from the top, with an LDS histogram.  After a
+// pass only the keys matching the chosen prefix remain candidates; once all of
+// them are needed (or all 64 bits are used) the kept set is every key with a
+// larger prefix plus the first `krem` matching keys in id order.  Random scores
+// usually settle after 3 passes.  Lane l owns the contiguous ids
+// [l*m, l*m + m), so a wave prefix scan compacts the kept ids in id order.
 template <typename T, int D>
-__global__ __launch_bounds__(kGateThreads) void gate_scores_kernel(GateArgs a) {
+__global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
+  constexpr int DQ = D / 4;  // dimensions per quarter
+  extern __shared__ uint64_t s_key[];  // [NB]
   __shared__ double s_q[D];
-  const int u = blockIdx.y;
+  __shared__ double s_part[4][256];
+  __shared__ int s_hist[256];
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int n = unit_nblocks(a.lens[b], a.S, a.NB);
-  const int j0 = blockIdx.x * kGateThreads;
-  if (j0 >= n) return;
   const int G = a.Hq / a.Hkv;
+  int32_t* out = a.sel_idx + (int64_t)u * a.k_max;
+
+  // ---- group-summed query, fp64, head order ----
   const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
-  for (int i = threadIdx.x; i < D; i += kGateThreads) {
-    double s = load_as_double<T>(q, i);
-    for (int h = 1; h < G; ++h) s += load_as_double<T>(q, (int64_t)h * D + i);
+  for (int i = tid; i < D; i += kTopkThreads) {
+    // All 8 possible heads are loaded (clamped to the group) before summing the
+    // first G in head order, so the loads are in flight together.
+    double x[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) x[h] = load_as_double<T>(q, (int64_t)min(h, G - 1) * D + i);
+    double s = x[0];
+#pragma unroll
+    for (int h = 1; h < 8; ++h) s = h < G ? s + x[h] : s;
     s_q[i] = s;
   }
   __syncthreads();
-  const int j = j0 + threadIdx.x;
-  if (j >= n) return;
-  const float* p = a.pooled + (int64_t)u * D * a.NB + j;
-  double s = 0.0;
-#pragma unroll 16
-  for (int i = 0; i < D; ++i) s = fma(s_q[i], (double)p[(int64_t)i * a.NB], s);
-  a.scores[(int64_t)u * a.NB + j] = s / sqrt((double)D);
-}
 
-__global__ __launch_bounds__(kGateThreads) void topk_kernel(GateArgs a) {
-  extern __shared__ uint64_t s_key[];  // [NB]
-  __shared__ int s_hist[256];
-  __shared__ int s_scan[kGateThreads / 64 + 1];
-  __shared__ int s_pick[2];
+  // ---- scores ----
+  const float* pu = a.pooled + (int64_t)u * D * a.NB;
+  const double inv = 1.0 / sqrt((double)D);
+  const int jl = tid & 255, qd = tid >> 8;
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    const int j = j0 + jl;
+    double s = 0.0;
+    if (j < n) {
+      // 32-bit offsets from the unit's (uniform) base; every load is issued
+      // before the FMA chain waits on the first one.
+      float pv[DQ];
+      int off = qd * DQ * a.NB + j;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i, off += a.NB) pv[i] = pu[off];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) s = fma(s_q[qd * DQ + i], (double)pv[i], s);
+    }
+    s_part[qd][jl] = s;
+    __syncthreads();
+    if (qd == 0 && j < n) {
+      const double sc = ((s_part[0][jl] + s_part[1][jl]) + s_part[2][jl]) + s_part[3][jl];
+      const double score = sc * inv;
+      a.scores[(int64_t)u * a.NB + j] = score;
+      s_key[j] = order_key(score);
+    }
+    __syncthreads();
+  }
+  if (tid >= 64) return;
 
-  const int u = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int b = u / a.Hkv;
-  const int n = unit_nblocks(a.lens[b], a.S, a.NB);
-  int32_t* out = a.sel_idx + (int64_t)u * a.k_max;
-
+  // ---- wave 0: kept count ----
   int k = 0;
   if (n > 0) {
-    if (a.top_k) {
-      k = a.top_k[b];
-    } else {
-      k = (int)(((int64_t)n * a.keep_num + a.keep_den - 1) / a.keep_den);
-    }
+    k = a.top_k ? a.top_k[b] : (int)(((int64_t)n * a.keep_num + a.keep_den - 1) / a.keep_den);
     k = k < 1 ? 1 : (k > n ? n : k);
     k = k > a.k_max ? a.k_max : k;
   }
   if (k >= n) {  // every block kept (or none when n == 0)
-    for (int j = tid; j < a.k_max; j += kGateThreads) out[j] = j < n ? j : -1;
-    if (tid == 0) a.sel_cnt[u] = n;
+    for (int j = lane; j < a.k_max; j += 64) out[j] = j < n ? j : -1;
+    if (lane == 0) a.sel_cnt[u] = n;
     return;
   }
 
-  const double* sc = a.scores + (int64_t)u * a.NB;
-  for (int j = tid; j < n; j += kGateThreads) s_key[j] = order_key(sc[j]);
-  __syncthreads();
-
-  // Radix select of tau, the k-th largest key.  Invariant: krem of the keys
-  // that match `prefix` on the bits in `mask` belong to the top k.
+  // ---- wave 0: radix select ----
+  const int m = (n + 63) / 64;
+  const int lo = min(n, lane * m), hi = min(n, lo + m);
   uint64_t prefix = 0, mask = 0;
   int krem = k;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += kGateThreads) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_hist[lane * 4 + r] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = lo; j < hi; ++j) {
       const uint64_t key = s_key[j];
       if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 255)], 1);
     }
-    __syncthreads();
-    // Digit dv with (#keys of larger digit) < krem <= (#keys of digit >= dv).
-    const int digit = 255 - tid;
-    const int c = s_hist[digit];
-    int tot;
-    const int larger = block_excl_scan<kGateThreads>(c, s_scan, &tot);
-    if (larger < krem && krem <= larger + c) {
-      s_pick[0] = digit;
-      s_pick[1] = krem - larger;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane l holds digits 255-4l .. 252-4l (descending)
+    int c[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { c[r] = s_hist[255 - 4 * lane - r]; sum += c[r]; }
+    const int incl = wave_incl_scan(sum);
+    int larger = incl - sum;  // keys with a larger digit than this lane's first
+    int pick = -1, nk = 0, pc = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (larger < krem && krem <= larger + c[r]) {
+        pick = 255 - 4 * lane - r;
+        nk = krem - larger;
+        pc = c[r];
+      }
+      larger += c[r];
     }
-    __syncthreads();
-    prefix |= (uint64_t)s_pick[0] << shift;
+    // exactly one lane picked: broadcast its digit, new krem and candidate count
+    const uint64_t who = __builtin_amdgcn_ballot_w64(pick >= 0);
+    const int src = (int)__builtin_ctzll(who);
+    const int dv = readlane_i(pick, src);
+    krem = readlane_i(nk, src);
+    const int cnt = readlane_i(pc, src);
+    prefix |= (uint64_t)dv << shift;
     mask |= (uint64_t)255 << shift;
-    krem = s_pick[1];
-    __syncthreads();
+    if (cnt == krem) break;  // every remaining candidate is kept
   }
-  const uint64_t tau = prefix;
 
-  // Keep every key > tau and the first krem keys == tau in id order; emit ids
-  // in ascending order.  Thread t owns the contiguous ids [lo, hi).
-  const int per = (n + kGateThreads - 1) / kGateThreads;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  // ---- wave 0: kept ids in id order (larger prefix, then first krem equal) ----
   int eq = 0;
-  for (int j = lo; j < hi; ++j) eq += s_key[j] == tau;
-  int tot;
-  const int eq_base = block_excl_scan<kGateThreads>(eq, s_scan, &tot);
+  for (int j = lo; j < hi; ++j) eq += (s_key[j] & mask) == prefix;
+  const int eq_base = wave_incl_scan(eq) - eq;
   int kept = 0;
   {
     int er = eq_base;
     for (int j = lo; j < hi; ++j) {
-      const uint64_t key = s_key[j];
-      const bool is_eq = key == tau;
-      kept += (key > tau) || (is_eq && er < krem);
+      const uint64_t mk = s_key[j] & mask;
+      const bool is_eq = mk == prefix;
+      kept += (mk > prefix) || (is_eq && er < krem);
       er += is_eq;
     }
   }
-  int pos = block_excl_scan<kGateThreads>(kept, s_scan, &tot);
+  int pos = wave_incl_scan(kept) - kept;
   {
     int er = eq_base;
     for (int j = lo; j < hi; ++j) {
-      const uint64_t key = s_key[j];
-      const bool is_eq = key == tau;
-      if ((key > tau) || (is_eq && er < krem)) out[pos++] = j;
+      const uint64_t mk = s_key[j] & mask;
+      const bool is_eq = mk == prefix;
+      if ((mk > prefix) || (is_eq && er < krem)) out[pos++] = j;
       er += is_eq;
     }
   }
-  for (int j = k + tid; j < a.k_max; j += kGateThreads) out[j] = -1;
-  if (tid == 0) a.sel_cnt[u] = k;
+  for (int j = k + lane; j < a.k_max; j += 64) out[j] = -1;
+  if (lane == 0) a.sel_cnt[u] = k;
 }
 
 }  // namespace
@@ -169,14 +208,11 @@ hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
   GateArgs args = a;
   void* params[] = {&args};
   const void* fn = nullptr;
-  if (a.dtype == 1) fn = a.D == 64 ? (const void*)&gate_scores_kernel<uint16_t, 64>
-                                   : (const void*)&gate_scores_kernel<uint16_t, 128>;
-  else fn = a.D == 64 ? (const void*)&gate_scores_kernel<float, 64>
-                      : (const void*)&gate_scores_kernel<float, 128>;
-  const dim3 grid1((a.NB + kGateThreads - 1) / kGateThreads, U);
-  hipError_t e = hipLaunchKernel(fn, grid1, dim3(kGateThreads), params, 0, stream);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)&topk_kernel, dim3(U), dim3(kGateThreads), params,
+  if (a.dtype == 1) fn = a.D == 64 ? (const void*)&gate_topk_kernel<uint16_t, 64>
+                                   : (const void*)&gate_topk_kernel<uint16_t, 128>;
+  else fn = a.D == 64 ? (const void*)&gate_topk_kernel<float, 64>
+                      : (const void*)&gate_topk_kernel<float, 128>;
+  return hipLaunchKernel(fn, dim3(U), dim3(kTopkThreads), params,
                          (size_t)a.NB * sizeof(uint64_t), stream);
 }
 

@@ -10,6 +10,11 @@ namespace seer {
 
 // ---------------------------------------------------------------- decode
 
+// Waves per workgroup of the partial-decode kernel.  One workgroup per CU: the
+// co-resident waves are then the same age, and the hardware's oldest-first
+// arbitration does not starve a second, younger workgroup on the same CU.
+constexpr int kDecodeWavesPerWG = 8;
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -21,7 +26,7 @@ struct DecodeArgs {
   const int32_t* sel_cnt;
   int32_t B, Hq, Hkv, D, NB, S, k_max;
   int32_t dtype;          // 0 fp32, 1 bf16
-  int32_t W;              // waves of the partial kernel (multiple of 4)
+  int32_t W;              // waves of the partial kernel (multiple of kDecodeWavesPerWG)
   float scale_log2;       // softmax scale * log2(e)
   int32_t* hdr;           // workspace header: [0] = W
   int32_t* prefix;        // [U + 1] block prefix over units

@@ -33,15 +33,17 @@
 // The K registers are refilled with the next tile right after the QK product
 // and the V registers right after the PV product, so each wave keeps about one
 // tile of loads in flight while it computes.
+#include <atomic>
+
 #include "seer_device.h"
 #include "seer_kernels.h"
 
 namespace seer {
 namespace {
 
-constexpr int kTile = 16;          // tokens per tile (one 16-wide MFMA column)
+constexpr int kTile = 32;          // tokens per tile (two 16-wide MFMA columns)
 constexpr int kCols = kTile / 16;  // 16-token MFMA columns per tile
-constexpr int kWavesPerWG = 4;
+constexpr int kWavesPerWG = kDecodeWavesPerWG;
 constexpr int kThreads = kWavesPerWG * kWave;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -198,11 +200,14 @@ void decode_partial_kernel(DecodeArgs a) {
     uint4 qa[NKL];
     {
       const char* qb = (const char*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * ROWB;
+      // Rows n16 >= G of the A operand are zero; their (clamped, in-bounds)
+      // loads are issued anyway so that no load sits behind a branch.
+      const bool qrow = n16 < G;
+      const char* qr = qb + min(n16, G - 1) * ROWB + r16 * 16;
 #pragma unroll
       for (int c = 0; c < NKL; ++c) {
-        uint4 z = make_uint4(0, 0, 0, 0);
-        if (n16 < G) z = *(const uint4*)(qb + n16 * ROWB + c * 64 + r16 * 16);
-        qa[c] = z;
+        const uint4 z = *(const uint4*)(qr + c * 64);
+        qa[c] = qrow ? z : make_uint4(0, 0, 0, 0);
       }
     }
     float m_run[4], l_run[4];
@@ -350,14 +355,13 @@ void decode_partial_kernel(DecodeArgs a) {
       describe(y, tv, row0);
       issue_k(row0);
       issue_v(row0);
-      for (; y + 1 < yc; ++y) {
+      for (; y < yc; ++y) {
+        // The last tile prefetches itself again (in bounds, cache-hot, unused).
         int tv_n;
         int64_t row_n;
-        describe(y + 1, tv_n, row_n);
+        describe(min(y + 1, yc - 1), tv_n, row_n);
         f32x4 sc[kCols];
         qk(sc);
-        // Keep the scheduler from hoisting the refills above the products that
-        // free their registers (that would double the live K/V registers).
         __builtin_amdgcn_sched_barrier(0);
         issue_k(row_n);
         softmax(sc, tv);
@@ -365,12 +369,6 @@ void decode_partial_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         issue_v(row_n);
         tv = tv_n;
-      }
-      {
-        f32x4 sc[kCols];
-        qk(sc);
-        softmax(sc, tv);
-        pv(tv);
       }
       y = yc;
     }
@@ -410,44 +408,102 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Merges the partial records of one unit per workgroup.
+// Merges the partial records of one unit per workgroup, in wave order.
+//
+// The waves that wrote a record for unit u are the non-empty waves among
+// [wlo, whi], the first and last waves whose tile ranges meet the unit's
+// tiles.  Records are merged in wave order with a running maximum:
+//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l,
+// and out = o / l.  The order is fixed, so the result is deterministic.
+// Loads: the records' (m, l) pairs go through LDS, each thread's acc elements
+// are fetched 16 records at a time, so a unit takes about two round trips.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass
+constexpr int kCombineBatch = 16;   // acc loads in flight per thread
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
-  const int u = blockIdx.x;
-  const int U = a.B * a.Hkv;
-  const int TPB = a.S / kTile;
-  const int W = a.hdr[0];
-  const int64_t Tot = (int64_t)a.prefix[U] * TPB;
-  const int64_t ylo = (int64_t)a.prefix[u] * TPB, yhi = (int64_t)a.prefix[u + 1] * TPB;
-  int wlo = 0, whi = -1;
-  if (yhi > ylo) {
-    wlo = (int)(((ylo + 1) * W - 1) / Tot);
-    whi = (int)((yhi * W - 1) / Tot);
-  }
-  const int b = u / a.Hkv, g = u - b * a.Hkv;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
   constexpr int REC = G * D + 16;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D, i = idx - h * D;
-    float M = kNegInf;
-    for (int w = wlo; w <= whi; ++w) {
-      if ((int64_t)w * Tot / W == (int64_t)(w + 1) * Tot / W) continue;  // empty wave
-      M = fmaxf(M, a.part[(int64_t)(u + w) * REC + G * D + h]);
-    }
-    float ls = 0.f, o = 0.f;
-    if (M != kNegInf) {
-      for (int w = wlo; w <= whi; ++w) {
-        if ((int64_t)w * Tot / W == (int64_t)(w + 1) * Tot / W) continue;
-        const float* rec = a.part + (int64_t)(u + w) * REC;
-        const float mw = rec[G * D + h];
-        if (mw == kNegInf) continue;
-        const float sc = exp2f(mw - M);
-        ls += rec[G * D + 8 + h] * sc;
-        o += rec[h * D + i] * sc;
+  constexpr int PER = (G * D + kCombineThreads - 1) / kCombineThreads;
+  __shared__ float s_mw[kCombineChunk][G];  // record maxima (-inf: empty wave)
+  __shared__ float s_lw[kCombineChunk][G];  // record sums
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int U = a.B * a.Hkv;
+  const int tsh = 31 - __builtin_clz(a.S / kTile);
+  const int W = a.hdr[0];
+  const int64_t Tot = (int64_t)a.prefix[U] << tsh;
+  const int64_t ylo = (int64_t)a.prefix[u] << tsh, yhi = (int64_t)a.prefix[u + 1] << tsh;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  if (yhi <= ylo) {  // no tokens: out = 0, lse = -inf
+    for (int idx = tid; idx < G * D; idx += kCombineThreads) a.out[head0 * D + idx] = 0.f;
+    if (a.lse && tid < G) a.lse[head0 + tid] = kNegInf;
+    return;
+  }
+  const int wlo = (int)(((ylo + 1) * W - 1) / Tot);
+  const int whi = (int)((yhi * W - 1) / Tot);
+  const int nw = whi - wlo + 1;
+  const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
+
+  float o[PER], M[PER], l[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) { o[r] = 0.f; M[r] = kNegInf; l[r] = 0.f; }
+
+  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, nw - c0);
+    if (c0 > 0) __syncthreads();  // previous chunk's (m, l) fully consumed
+    for (int t = tid; t < cn; t += kCombineThreads) {
+      const int64_t w = wlo + c0 + t;
+      const bool empty = w * Tot / W == (w + 1) * Tot / W;  // wrote no record
+      const float* r = part + (int64_t)(c0 + t) * REC;
+      // Loads are unconditional (the slot is in the workspace either way) and
+      // the empty records are selected away, so all loads are in flight at once.
+      float mv[G], lv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) { mv[h] = r[G * D + h]; lv[h] = r[G * D + 8 + h]; }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_mw[t][h] = empty ? kNegInf : mv[h];
+        s_lw[t][h] = empty ? 0.f : lv[h];
       }
     }
-    const int64_t head = (int64_t)b * a.Hq + (int64_t)g * G + h;
-    a.out[head * D + i] = ls > 0.f ? o / ls : 0.f;
-    if (i == 0 && a.lse) a.lse[head] = ls > 0.f ? (M + log2f(ls)) * 0.69314718055994530942f : kNegInf;
+    __syncthreads();
+    for (int t0 = 0; t0 < cn; t0 += kCombineBatch) {
+      const int tn = min(kCombineBatch, cn - t0);
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int idx = r * kCombineThreads + tid;
+        if (idx >= G * D) continue;
+        const int h = idx / D;
+        const float* base = part + (int64_t)(c0 + t0) * REC;  // uniform
+        float x[kCombineBatch];
+        // Past the chunk's end re-read its last record (in bounds, unused).
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t) x[t] = base[min(t, tn - 1) * REC + idx];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t) {
+          if (t >= tn) break;
+          const float mw = s_mw[t0 + t][h];
+          if (mw == kNegInf) continue;  // empty record or no valid token: skipped
+          const float mn = fmaxf(M[r], mw);
+          const float sa = exp2f(M[r] - mn), sb = exp2f(mw - mn);
+          o[r] = o[r] * sa + x[t] * sb;
+          l[r] = l[r] * sa + s_lw[t0 + t][h] * sb;
+          M[r] = mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = r * kCombineThreads + tid;
+    if (idx >= G * D) continue;
+    a.out[head0 * D + idx] = l[r] > 0.f ? o[r] / l[r] : 0.f;
+    if (a.lse && (idx % D) == 0)
+      a.lse[head0 + idx / D] = l[r] > 0.f ? (M[r] + log2f(l[r])) * 0.69314718055994530942f : kNegInf;
   }
 }
 
@@ -512,11 +568,23 @@ int decode_max_waves(int dtype, int D, int G) {
   if (!fn) return 0;
   int dev = 0, cus = 0, blocks = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  // Cached per (device, instantiation): later calls (for example under stream
+  // capture) make no device queries.
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev][2][2][9];
+  std::atomic<int>* slot = nullptr;
+  if (dev >= 0 && dev < kMaxDev) {
+    slot = &cache[dev][dtype == 1][D == 128][G];
+    const int c = slot->load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   // Occupancy with the largest plan buffer, so that the count is an upper bound.
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess) return 0;
   if (blocks < 1) blocks = 1;
-  return cus * blocks * kWavesPerWG;
+  const int waves = cus * blocks * kWavesPerWG;
+  if (slot) slot->store(waves, std::memory_order_relaxed);
+  return waves;
 }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
@@ -536,7 +604,7 @@ hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
   if (!fn) return hipErrorInvalidValue;
   CombineArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(256), params, 0, stream);
+  return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(kCombineThreads), params, 0, stream);
 }
 
 }  // namespace seer

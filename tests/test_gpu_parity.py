@@ -356,3 +356,27 @@ def test_long_decode_loop():
     torch.cuda.synchronize()
     assert torch.equal(st.pooled, fresh.pooled)
     assert torch.equal(st.open_sum, fresh.open_sum)
+
+
+def test_graph_replay_matches_eager():
+    """A captured decode step replays bit-identically, with eager work in between."""
+    wl = SMALL["paged_small"]
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    ref = (st.sel_idx.clone(), st.sel_cnt.clone(), st.out.clone(), st.lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.step(case.q, case.lens)
+    for _ in range(3):
+        st.out.zero_()
+        st.lse.zero_()
+        st.sel_idx.fill_(-7)
+        st.sel_cnt.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (st.sel_idx, st.sel_cnt, st.out, st.lse)):
+            assert torch.equal(a, b)
