@@ -418,11 +418,13 @@ void decode_partial_kernel(DecodeArgs a) {
 // Loads: the records' (m, l) pairs go through LDS, each thread's acc elements
 // are fetched 16 records at a time, so a unit takes about two round trips.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass
-constexpr int kCombineBatch = 16;   // acc loads in flight per thread
+constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass (general path)
+constexpr int kCombineBatch = 16;   // acc loads in flight per thread (general path)
+constexpr int kCombineFast = 32;    // units with at most this many records: one-shot path
 
 template <int D, int G>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void decode_combine_kernel(CombineArgs a) {
   constexpr int REC = G * D + 16;
   constexpr int PER = (G * D + kCombineThreads - 1) / kCombineThreads;
   __shared__ float s_mw[kCombineChunk][G];  // record maxima (-inf: empty wave)
@@ -446,7 +448,59 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   const int whi = (int)((yhi * W - 1) / Tot);
   const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
+  auto empty = [&](int t) {
+    const int64_t w = wlo + t;
+    return w * Tot / W == (w + 1) * Tot / W;  // wrote no record
+  };
 
+  if (nw <= kCombineFast) {
+    // One shot: thread tid owns the EPT consecutive elements tid*EPT.. of one
+    // head (EPT a power of two, so it divides D); every value it needs from
+    // every record is loaded before any use.
+    constexpr int EPT = G * D <= kCombineThreads ? 1 : G * D <= 2 * kCombineThreads ? 2 : 4;
+    if (tid * EPT >= G * D) return;
+    const int idx0 = tid * EPT, h = idx0 / D;
+    float x[kCombineFast][EPT], mv[kCombineFast], lv[kCombineFast];
+#pragma unroll
+    for (int t = 0; t < kCombineFast; ++t) {
+      const float* r = part + (int64_t)min(t, nw - 1) * REC;  // past nw: re-read, unused
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) x[t][e] = r[idx0 + e];
+      mv[t] = r[G * D + h];
+      lv[t] = r[G * D + 8 + h];
+    }
+    // Waves are only ever empty when there are fewer tiles than waves; the
+    // 64-bit divisions that tell are kept out of the merge loop.
+    uint32_t skip = 0;
+    if (Tot < W) {
+      for (int t = 0; t < nw; ++t) skip |= empty(t) ? (1u << t) : 0u;
+    }
+    float M = kNegInf, l = 0.f, o[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kCombineFast; ++t) {
+      const float mw = mv[t];
+      const bool use = t < nw && mw != kNegInf && !((skip >> t) & 1u);
+      const float mn = use ? fmaxf(M, mw) : M;
+      // M == -inf only before the first used record, when o and l are still 0.
+      // Arguments are <= 0: the hardware exp2 is accurate there.
+      const float sa = use ? (M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - mn)) : 1.f;
+      const float sb = use ? __builtin_amdgcn_exp2f(mw - mn) : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) o[e] = use ? o[e] * sa + x[t][e] * sb : o[e];
+      l = use ? l * sa + lv[t] * sb : l;
+      M = mn;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) a.out[head0 * D + idx0 + e] = l > 0.f ? o[e] / l : 0.f;
+    if (a.lse && (idx0 % D) == 0)
+      a.lse[head0 + h] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+    return;
+  }
+
+  // General path (many records per unit): (m, l) staged through LDS in chunks,
+  // acc loads batched; same in-order running merge.
   float o[PER], M[PER], l[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) { o[r] = 0.f; M[r] = kNegInf; l[r] = 0.f; }
@@ -455,18 +509,15 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
     const int cn = min(kCombineChunk, nw - c0);
     if (c0 > 0) __syncthreads();  // previous chunk's (m, l) fully consumed
     for (int t = tid; t < cn; t += kCombineThreads) {
-      const int64_t w = wlo + c0 + t;
-      const bool empty = w * Tot / W == (w + 1) * Tot / W;  // wrote no record
+      const bool e = empty(c0 + t);
       const float* r = part + (int64_t)(c0 + t) * REC;
-      // Loads are unconditional (the slot is in the workspace either way) and
-      // the empty records are selected away, so all loads are in flight at once.
       float mv[G], lv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) { mv[h] = r[G * D + h]; lv[h] = r[G * D + 8 + h]; }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s_mw[t][h] = empty ? kNegInf : mv[h];
-        s_lw[t][h] = empty ? 0.f : lv[h];
+        s_mw[t][h] = e ? kNegInf : mv[h];
+        s_lw[t][h] = e ? 0.f : lv[h];
       }
     }
     __syncthreads();
@@ -479,7 +530,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
         const int h = idx / D;
         const float* base = part + (int64_t)(c0 + t0) * REC;  // uniform
         float x[kCombineBatch];
-        // Past the chunk's end re-read its last record (in bounds, unused).
 #pragma unroll
         for (int t = 0; t < kCombineBatch; ++t) x[t] = base[min(t, tn - 1) * REC + idx];
         __builtin_amdgcn_sched_barrier(0);
@@ -489,7 +539,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
           const float mw = s_mw[t0 + t][h];
           if (mw == kNegInf) continue;  // empty record or no valid token: skipped
           const float mn = fmaxf(M[r], mw);
-          const float sa = exp2f(M[r] - mn), sb = exp2f(mw - mn);
+          const float sa = __builtin_amdgcn_exp2f(M[r] - mn), sb = __builtin_amdgcn_exp2f(mw - mn);
           o[r] = o[r] * sa + x[t] * sb;
           l[r] = l[r] * sa + s_lw[t0 + t][h] * sb;
           M[r] = mn;
