@@ -76,14 +76,23 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 
 // ---------------------------------------------------------------- scans
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Adds the DPP-moved value of x; lanes without a source lane add 0 (the
+// "old" operand), since bound_ctrl is off and every row/bank is enabled.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2, 4,
+// 8 within each 16-lane row, then row 0's and row 2's totals (lane 15, 47) are
+// broadcast into rows 1 and 3, then lane 31's total into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
