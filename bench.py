@@ -31,6 +31,42 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), 90% sparsity, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
+# Measured HBM bytes per launch of the partial kernel (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE, calibrated on a plain copy), valid only for the kernel sources
+# whose digest the file records.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_sparse90_32k_hbm_traffic.txt")
+KERNEL_SOURCES = ["block_sparse_attention_29_amd/csrc/sparse_decode.hip",
+                  "block_sparse_attention_29_amd/csrc/seer_device.h",
+                  "block_sparse_attention_29_amd/csrc/seer_kernels.h",
+                  "block_sparse_attention_29_amd/build.py"]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Counter-measured bytes per partial launch, or None when the counters were
+    taken on other kernel sources (or another workload)."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "|", "#")):
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("workload") != workload:
+            return None
+        if fields.get("source_sha256") != kernel_source_digest():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -217,7 +253,7 @@ def main():
         "step_pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel<bf16,128,4>",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},
         "dense": dense,
         "cpu_baseline": cpu,
