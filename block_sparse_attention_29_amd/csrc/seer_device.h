@@ -128,4 +128,10 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (bits >> 63) ? ~bits : (bits | 0x8000000000000000ull);
 }
 
+// Inverse of order_key (a -0.0 score comes back as +0.0).
+__device__ __forceinline__ double key_score(uint64_t key) {
+  const uint64_t bits = (key >> 63) ? (key & 0x7FFFFFFFFFFFFFFFull) : ~key;
+  return __longlong_as_double((long long)bits);
+}
+
 }  // namespace seer

@@ -248,9 +248,13 @@ def test_edge_shapes(name, kw):
         check_unit(st, case, case.q, case.lens.tolist(), b, g, tag=name)
 
 
-def test_ties_and_zero_query():
-    """Duplicated blocks and a zero query: ties go to the lower block id."""
-    wl = WORKLOADS["planted_8k"].with_(batch=1, planted_fraction=None, context=2048)
+@pytest.mark.parametrize("context", [2048, 32768, 32769, 40000])
+def test_ties_and_zero_query(context):
+    """Duplicated blocks and a zero query: ties go to the lower block id (block
+    counts 32 and 512 take the rank-counting selection, 513 and 625 the radix
+    selection)."""
+    wl = WORKLOADS["planted_8k"].with_(batch=1, planted_fraction=None, context=context)
+    print(f"[case] ties context {context}", flush=True)
     case = make_case(wl, "cuda")
     S = wl.block_size
     # blocks 5 and 20 identical (keys and values), and block 7 == block 3
