@@ -10,6 +10,8 @@
 #include "seer.h"
 #include "seer_kernels.h"
 
+static_assert(seer::kMaxUnits == SEER_MAX_UNITS, "unit limit mismatch");
+
 namespace {
 
 thread_local char g_err[512] = "";

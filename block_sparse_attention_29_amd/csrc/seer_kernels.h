@@ -10,10 +10,15 @@ namespace seer {
 
 // ---------------------------------------------------------------- decode
 
-// Waves per workgroup of the partial-decode kernel.  One workgroup per CU: the
-// co-resident waves are then the same age, and the hardware's oldest-first
-// arbitration does not starve a second, younger workgroup on the same CU.
-constexpr int kDecodeWavesPerWG = 8;
+// Waves per workgroup of the partial-decode kernel: one wave per SIMD, and one
+// workgroup per CU.  A second wave on a SIMD (or a second workgroup on a CU)
+// is younger, and the hardware's oldest-first arbitration serves its loads
+// last: it starts later and streams slower than its older neighbour, which
+// leaves a long tail of half-occupied CUs.
+constexpr int kDecodeWavesPerWG = 4;
+
+// Largest number of (sequence, KV head) units a call may have.
+constexpr int kMaxUnits = 8192;
 
 struct DecodeArgs {
   const void* q;

@@ -629,10 +629,12 @@ int decode_max_waves(int dtype, int D, int G) {
     if (c > 0) return c;
   }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  // Occupancy with the largest plan buffer, so that the count is an upper bound.
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess) return 0;
-  if (blocks < 1) blocks = 1;
-  const int waves = cus * blocks * kWavesPerWG;
+  // The kernel must fit on a CU with the largest plan buffer; it then runs
+  // one workgroup per CU (see kDecodeWavesPerWG).
+  const size_t smem = (size_t)(kMaxUnits + 1 + kWavesPerWG + 1) * sizeof(int);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, smem) != hipSuccess) return 0;
+  if (blocks < 1) return 0;
+  const int waves = cus * kWavesPerWG;
   if (slot) slot->store(waves, std::memory_order_relaxed);
   return waves;
 }
