@@ -408,19 +408,83 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
+// Whether wave w of W owns no tile when Tot tiles are split in equal ranges.
+__device__ __forceinline__ bool wave_empty(int64_t w, int W, int64_t Tot) {
+  return w * Tot / W == (w + 1) * Tot / W;
+}
+
 // Merges the partial records of one unit per workgroup, in wave order.
 //
 // The waves that wrote a record for unit u are the non-empty waves among
 // [wlo, whi], the first and last waves whose tile ranges meet the unit's
-// tiles.  Records are merged in wave order with a running maximum:
-//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l,
-// and out = o / l.  The order is fixed, so the result is deterministic.
-// Loads: the records' (m, l) pairs go through LDS, each thread's acc elements
-// are fetched 16 records at a time, so a unit takes about two round trips.
+// tiles.  Up to 32 records: one shot, every load up front, then the maximum
+// of the records' maxima and the scaled sums in record order.  More records:
+// (m, l) pairs staged through LDS in chunks, acc elements fetched 16 records
+// at a time, merged with a running maximum
+//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l.
+// Either way out = o / l and the order is fixed, so the result is
+// deterministic.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass (general path)
 constexpr int kCombineBatch = 16;   // acc loads in flight per thread (general path)
 constexpr int kCombineFast = 32;    // units with at most this many records: one-shot path
+
+// One-shot merge of a unit with at most NWB records: thread tid owns the EPT
+// consecutive elements tid*EPT.. of one head (EPT a power of two, so it
+// divides D) and loads every value it needs from every record before any use.
+// Two passes: the maximum M of the records' maxima, then the sums
+//   o = sum_w acc_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M)
+// in record order, so the only dependency chain is the fma chain.
+template <int D, int G, int NWB>
+__device__ __forceinline__ void combine_shot(const CombineArgs& a, const float* part, int nw,
+                                             int wlo, int W, int64_t Tot, int64_t head0) {
+  constexpr int REC = G * D + 16;
+  constexpr int EPT = G * D <= kCombineThreads ? 1 : G * D <= 2 * kCombineThreads ? 2 : 4;
+  const int tid = threadIdx.x;
+  if (tid * EPT >= G * D) return;
+  const int idx0 = tid * EPT, h = idx0 / D;
+  float x[NWB][EPT], mv[NWB], lv[NWB];
+#pragma unroll
+  for (int t = 0; t < NWB; ++t) {
+    const float* r = part + (int64_t)min(t, nw - 1) * REC;  // past nw: re-read, unused
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) x[t][e] = r[idx0 + e];
+    mv[t] = r[G * D + h];
+    lv[t] = r[G * D + 8 + h];
+  }
+  // Waves are only ever empty when there are fewer tiles than waves; the
+  // 64-bit divisions that tell are kept out of the merge.
+  uint32_t skip = 0;
+  if (Tot < W) {
+    for (int t = 0; t < nw; ++t) skip |= wave_empty(wlo + t, W, Tot) ? (1u << t) : 0u;
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int t = 0; t < NWB; ++t) {
+    const bool use = t < nw && !((skip >> t) & 1u);
+    M = use ? fmaxf(M, mv[t]) : M;
+  }
+  float l = 0.f, o[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int t = 0; t < NWB; ++t) {
+      // Records without a valid token (m = -inf) and skipped slots add nothing;
+      // stale slots may hold anything, so they are selected away, not scaled.
+      const bool use = t < nw && !((skip >> t) & 1u) && mv[t] != kNegInf;
+      // Arguments are <= 0: the hardware exp2 is accurate there.
+      const float sc = __builtin_amdgcn_exp2f(mv[t] - M);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) o[e] = use ? fmaf(x[t][e], sc, o[e]) : o[e];
+      l = use ? fmaf(lv[t], sc, l) : l;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) a.out[head0 * D + idx0 + e] = l > 0.f ? o[e] / l : 0.f;
+  if (a.lse && (idx0 % D) == 0)
+    a.lse[head0 + h] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
@@ -448,56 +512,11 @@ void decode_combine_kernel(CombineArgs a) {
   const int whi = (int)((yhi * W - 1) / Tot);
   const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
-  auto empty = [&](int t) {
-    const int64_t w = wlo + t;
-    return w * Tot / W == (w + 1) * Tot / W;  // wrote no record
-  };
+  auto empty = [&](int t) { return wave_empty(wlo + t, W, Tot); };  // wrote no record
 
-  if (nw <= kCombineFast) {
-    // One shot: thread tid owns the EPT consecutive elements tid*EPT.. of one
-    // head (EPT a power of two, so it divides D); every value it needs from
-    // every record is loaded before any use.
-    constexpr int EPT = G * D <= kCombineThreads ? 1 : G * D <= 2 * kCombineThreads ? 2 : 4;
-    if (tid * EPT >= G * D) return;
-    const int idx0 = tid * EPT, h = idx0 / D;
-    float x[kCombineFast][EPT], mv[kCombineFast], lv[kCombineFast];
-#pragma unroll
-    for (int t = 0; t < kCombineFast; ++t) {
-      const float* r = part + (int64_t)min(t, nw - 1) * REC;  // past nw: re-read, unused
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) x[t][e] = r[idx0 + e];
-      mv[t] = r[G * D + h];
-      lv[t] = r[G * D + 8 + h];
-    }
-    // Waves are only ever empty when there are fewer tiles than waves; the
-    // 64-bit divisions that tell are kept out of the merge loop.
-    uint32_t skip = 0;
-    if (Tot < W) {
-      for (int t = 0; t < nw; ++t) skip |= empty(t) ? (1u << t) : 0u;
-    }
-    float M = kNegInf, l = 0.f, o[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int t = 0; t < kCombineFast; ++t) {
-      const float mw = mv[t];
-      const bool use = t < nw && mw != kNegInf && !((skip >> t) & 1u);
-      const float mn = use ? fmaxf(M, mw) : M;
-      // M == -inf only before the first used record, when o and l are still 0.
-      // Arguments are <= 0: the hardware exp2 is accurate there.
-      const float sa = use ? (M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - mn)) : 1.f;
-      const float sb = use ? __builtin_amdgcn_exp2f(mw - mn) : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) o[e] = use ? o[e] * sa + x[t][e] * sb : o[e];
-      l = use ? l * sa + lv[t] * sb : l;
-      M = mn;
-    }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) a.out[head0 * D + idx0 + e] = l > 0.f ? o[e] / l : 0.f;
-    if (a.lse && (idx0 % D) == 0)
-      a.lse[head0 + h] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
-    return;
-  }
+  if (nw <= 8) return combine_shot<D, G, 8>(a, part, nw, wlo, W, Tot, head0);
+  if (nw <= 16) return combine_shot<D, G, 16>(a, part, nw, wlo, W, Tot, head0);
+  if (nw <= kCombineFast) return combine_shot<D, G, kCombineFast>(a, part, nw, wlo, W, Tot, head0);
 
   // General path (many records per unit): (m, l) staged through LDS in chunks,
   // acc loads batched; same in-order running merge.
