@@ -75,6 +75,103 @@ int wave_cap(const seer_shape* s) {
   return seer::decode_max_waves(s->dtype, s->head_dim, s->num_q_heads / s->num_kv_heads);
 }
 
+// Validates a decode call and fills the partial kernel's arguments.
+seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
+                           const int32_t* lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                           int32_t k_max, float softmax_scale, void* workspace,
+                           size_t workspace_bytes, seer::DecodeArgs* out_args) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_kv(kv))) return st;
+  if (!q || !lens) return fail(SEER_ERR_INVALID_ARG, "q or lens is NULL");
+  if (sel_idx) {
+    if (!sel_cnt) return fail(SEER_ERR_INVALID_ARG, "sel_idx given without sel_cnt");
+    if (k_max < 1 || k_max > shape->max_blocks)
+      return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
+                  shape->max_blocks);
+  }
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(SEER_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  const int U = shape->batch * shape->num_kv_heads;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const size_t need = seer::decode_workspace_bytes(shape->batch, shape->num_kv_heads, G,
+                                                   shape->head_dim, wmax);
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+  // Waves: all resident slots, but no more than an upper bound of the tiles.
+  const int64_t blocks_bound =
+      (int64_t)U * (sel_idx ? k_max : shape->max_blocks);
+  const int64_t tiles_bound = blocks_bound * (shape->block_size / 16);  // 16-token tiles
+  int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
+  W = (W + seer::kDecodeWavesPerWG - 1) / seer::kDecodeWavesPerWG * seer::kDecodeWavesPerWG;
+
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale
+                                           : 1.0 / sqrt((double)shape->head_dim);
+  seer::DecodeArgs& a = *out_args;
+  a = seer::DecodeArgs{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.num_pages = kv->num_pages;
+  a.lens = lens;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.B = shape->batch;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.D = shape->head_dim;
+  a.NB = shape->max_blocks;
+  a.S = shape->block_size;
+  a.k_max = sel_idx ? k_max : shape->max_blocks;
+  a.dtype = shape->dtype;
+  a.W = (int32_t)W;
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  char* ws = (char*)workspace;
+  a.hdr = (int32_t*)ws;
+  a.prefix = (int32_t*)(ws + 64);
+  a.part = (float*)(ws + seer::decode_part_offset(U));
+  return SEER_OK;
+}
+
+// Validates the gate's arguments.
+seer_status check_gate(const seer_shape* shape, const void* q, const float* pooled,
+                       const int32_t* lens, const int32_t* top_k, int32_t keep_num,
+                       int32_t keep_den, int32_t k_max, const double* scores,
+                       const int32_t* sel_idx, const int32_t* sel_cnt) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if (!q || !pooled || !lens || !scores || !sel_idx || !sel_cnt)
+    return fail(SEER_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (k_max < 1 || k_max > shape->max_blocks)
+    return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
+                shape->max_blocks);
+  if (!top_k) {
+    const int32_t kk = seer_keep_blocks(shape->max_blocks, keep_num, keep_den);
+    if (kk < 0)
+      return fail(SEER_ERR_INVALID_ARG, "keep rule %d/%d invalid (need 1 <= num <= den)",
+                  keep_num, keep_den);
+    if (kk > k_max)
+      return fail(SEER_ERR_INVALID_ARG, "keep rule keeps %d of max_blocks=%d blocks > k_max=%d",
+                  kk, shape->max_blocks, k_max);
+  }
+  return SEER_OK;
+}
+
+// Largest dynamic LDS one workgroup may use on the current device.
+size_t max_block_smem() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return 0;
+  return (size_t)v;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -129,22 +226,9 @@ seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const 
                                   const int32_t* lens, const int32_t* top_k, int32_t keep_num,
                                   int32_t keep_den, int32_t k_max, double* scores,
                                   int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
-  seer_status st = check_shape(shape);
+  const seer_status st = check_gate(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max,
+                                    scores, sel_idx, sel_cnt);
   if (st) return st;
-  if (!q || !pooled || !lens || !scores || !sel_idx || !sel_cnt)
-    return fail(SEER_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (k_max < 1 || k_max > shape->max_blocks)
-    return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
-                shape->max_blocks);
-  if (!top_k) {
-    const int32_t kk = seer_keep_blocks(shape->max_blocks, keep_num, keep_den);
-    if (kk < 0)
-      return fail(SEER_ERR_INVALID_ARG, "keep rule %d/%d invalid (need 1 <= num <= den)",
-                  keep_num, keep_den);
-    if (kk > k_max)
-      return fail(SEER_ERR_INVALID_ARG, "keep rule keeps %d of max_blocks=%d blocks > k_max=%d",
-                  kk, shape->max_blocks, k_max);
-  }
   seer::GateArgs a{};
   a.q = q;
   a.pooled = pooled;
@@ -185,63 +269,71 @@ seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, c
                                        const int32_t* sel_cnt, int32_t k_max,
                                        float softmax_scale, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
-  seer_status st = check_shape(shape);
+  seer::DecodeArgs a;
+  const seer_status st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max,
+                                        softmax_scale, workspace, workspace_bytes, &a);
   if (st) return st;
-  if ((st = check_kv(kv))) return st;
-  if (!q || !lens) return fail(SEER_ERR_INVALID_ARG, "q or lens is NULL");
-  if (sel_idx) {
-    if (!sel_cnt) return fail(SEER_ERR_INVALID_ARG, "sel_idx given without sel_cnt");
-    if (k_max < 1 || k_max > shape->max_blocks)
-      return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
-                  shape->max_blocks);
-  }
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
-    return fail(SEER_ERR_INVALID_ARG, "softmax_scale is not finite");
-  if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
-  const int wmax = wave_cap(shape);
-  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
-  const int U = shape->batch * shape->num_kv_heads;
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  const size_t need = seer::decode_workspace_bytes(shape->batch, shape->num_kv_heads, G,
-                                                   shape->head_dim, wmax);
-  if (workspace_bytes < need)
-    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-
-  // Waves: all resident slots, but no more than an upper bound of the tiles.
-  const int64_t blocks_bound =
-      (int64_t)U * (sel_idx ? k_max : shape->max_blocks);
-  const int64_t tiles_bound = blocks_bound * (shape->block_size / 16);  // 16-token tiles
-  int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
-  W = (W + seer::kDecodeWavesPerWG - 1) / seer::kDecodeWavesPerWG * seer::kDecodeWavesPerWG;
-
-  const double scale = softmax_scale > 0.f ? (double)softmax_scale
-                                           : 1.0 / sqrt((double)shape->head_dim);
-  seer::DecodeArgs a{};
-  a.q = q;
-  a.k = kv->k;
-  a.v = kv->v;
-  a.page_table = kv->page_table;
-  a.num_pages = kv->num_pages;
-  a.lens = lens;
-  a.sel_idx = sel_idx;
-  a.sel_cnt = sel_cnt;
-  a.B = shape->batch;
-  a.Hq = shape->num_q_heads;
-  a.Hkv = shape->num_kv_heads;
-  a.D = shape->head_dim;
-  a.NB = shape->max_blocks;
-  a.S = shape->block_size;
-  a.k_max = sel_idx ? k_max : shape->max_blocks;
-  a.dtype = shape->dtype;
-  a.W = (int32_t)W;
-  a.scale_log2 = (float)(scale * 1.4426950408889634074);
-  char* ws = (char*)workspace;
-  a.hdr = (int32_t*)ws;
-  a.prefix = (int32_t*)(ws + 64);
-  a.part = (float*)(ws + seer::decode_part_offset(U));
   const hipError_t e = seer::launch_decode_partial(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   return ok();
+}
+
+seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void* q,
+                                             const seer_kv* kv, const int32_t* lens,
+                                             const float* pooled, const int32_t* top_k,
+                                             int32_t keep_num, int32_t keep_den, int32_t k_max,
+                                             float softmax_scale, double* scores,
+                                             int32_t* sel_idx, int32_t* sel_cnt,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  seer_status st = check_gate(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max, scores,
+                              sel_idx, sel_cnt);
+  if (st) return st;
+  seer::DecodeArgs a;
+  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
+                           workspace, workspace_bytes, &a)))
+    return st;
+  const int U = shape->batch * shape->num_kv_heads;
+  const int ids_cap = seer::gated_decode_ids_cap(U, k_max, a.W);
+  const size_t smem = seer::gated_decode_smem_bytes(U, shape->max_blocks, ids_cap);
+  if (smem <= max_block_smem()) {
+    a.sel_idx = nullptr;
+    a.sel_cnt = nullptr;
+    a.pooled = pooled;
+    a.top_k = top_k;
+    a.keep_num = keep_num;
+    a.keep_den = keep_den;
+    a.scores = scores;
+    a.sel_idx_out = sel_idx;
+    a.sel_cnt_out = sel_cnt;
+    a.ids_cap = ids_cap;
+    const hipError_t e = seer::launch_gated_decode_partial(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
+  } else {
+    // The selections of one workgroup's units do not fit in its LDS: the gate
+    // kernel, then the partial kernel on its selection (same results).
+    if ((st = seer_gate_scores_topk(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max,
+                                    scores, sel_idx, sel_cnt, stream)))
+      return st;
+    const hipError_t e = seer::launch_decode_partial(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+  }
+  return ok();
+}
+
+seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
+                                     const int32_t* lens, const float* pooled,
+                                     const int32_t* top_k, int32_t keep_num, int32_t keep_den,
+                                     int32_t k_max, float softmax_scale, double* scores,
+                                     int32_t* sel_idx, int32_t* sel_cnt, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  const seer_status st = seer_gated_sparse_decode_partial(
+      shape, q, kv, lens, pooled, top_k, keep_num, keep_den, k_max, softmax_scale, scores,
+      sel_idx, sel_cnt, workspace, workspace_bytes, stream);
+  if (st) return st;
+  return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
 }
 
 seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,

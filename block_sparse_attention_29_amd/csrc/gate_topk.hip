@@ -15,17 +15,12 @@
 // Deterministic; no sorting network needed.
 #include "seer_device.h"
 #include "seer_kernels.h"
+#include "select_device.h"
 
 namespace seer {
 namespace {
 
 constexpr int kTopkThreads = 1024;
-
-__device__ __forceinline__ int unit_nblocks(int L, int S, int NB) {
-  if (L <= 0) return 0;
-  const int n = (int)(((int64_t)L + S - 1) / S);
-  return n > NB ? NB : n;
-}
 
 template <typename T>
 __device__ __forceinline__ double load_as_double(const T* p, int64_t i);
@@ -49,13 +44,7 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
 // first 256 blocks are issued before the query loads, so the two round trips
 // overlap.
 //
-// Selection: exact radix select over 64-bit order keys (-0 folded into +0),
-// 8 bits per pass from the top, by the whole workgroup with an LDS histogram.
-// After a pass only the keys matching the chosen prefix remain candidates;
-// once all of them are needed (or all 64 bits are used) the kept set is every
-// key with a larger prefix plus the first `krem` matching keys in id order,
-// which is the top k by (score desc, id asc).  Random scores usually settle
-// after 3 passes.
+// Selection: block_topk_ids (an exact radix select by the whole workgroup).
 template <typename T, int D>
 __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
   constexpr int DQ = D / 4;  // dimensions per quarter
@@ -67,9 +56,9 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
   __shared__ int s_scan[kTopkThreads / 64 + 1];
 
   const int u = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
-  const int n = unit_nblocks(a.lens[b], a.S, a.NB);
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
   const int G = a.Hq / a.Hkv;
   int32_t* out = a.sel_idx + (int64_t)u * a.k_max;
 
@@ -123,13 +112,7 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
     score_chunk(j0);
   }
 
-  // ---- kept count ----
-  int k = 0;
-  if (n > 0) {
-    k = a.top_k ? a.top_k[b] : (int)(((int64_t)n * a.keep_num + a.keep_den - 1) / a.keep_den);
-    k = k < 1 ? 1 : (k > n ? n : k);
-    k = k > a.k_max ? a.k_max : k;
-  }
+  const int k = kept_count(n, a.top_k, b, a.keep_num, a.keep_den, a.k_max);
   // The scores go out last (rebuilt from the order keys): a pending store
   // would hold its data registers and stall the selection behind it.
   auto write_scores = [&](int j0, int stride) {
@@ -143,82 +126,7 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
     return;
   }
 
-  // ---- block radix select ----
-  // Thread t owns the contiguous ids [t*m, t*m + m).  Each pass histograms
-  // the next 8 bits of the candidates' keys (double-buffered LDS histogram,
-  // the next one cleared during the current pass), wave 0 scans the 256 bins
-  // from the top and publishes the digit that holds the krem-th largest key.
-  const int m = (n + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(n, tid * m), hi = min(n, lo + m);
-  uint64_t prefix = 0, mask = 0;
-  int krem = k;
-  if (tid < 256) s_hist[0][tid] = 0;
-  __syncthreads();
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    int* hist = s_hist[pass & 1];
-    for (int j = lo; j < hi; ++j) {
-      const uint64_t key = s_key[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
-    }
-    if (tid < 256) s_hist[(pass & 1) ^ 1][tid] = 0;
-    __syncthreads();
-    if (tid < 64) {
-      // lane l holds digits 255-4l .. 252-4l (descending)
-      int c[4], sum = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * lane - r]; sum += c[r]; }
-      int larger = wave_incl_scan(sum) - sum;  // keys with a larger digit than this lane's first
-      int pick = -1, nk = 0, pc = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (larger < krem && krem <= larger + c[r]) {
-          pick = 255 - 4 * lane - r;
-          nk = krem - larger;
-          pc = c[r];
-        }
-        larger += c[r];
-      }
-      // exactly one lane picked: it publishes its digit, new krem and count
-      if (pick >= 0) {
-        s_pick[0] = pick;
-        s_pick[1] = nk;
-        s_pick[2] = pc;
-      }
-    }
-    __syncthreads();
-    const int dv = s_pick[0], cnt = s_pick[2];
-    krem = s_pick[1];
-    prefix |= (uint64_t)dv << shift;
-    mask |= (uint64_t)255 << shift;
-    if (cnt == krem) break;  // every remaining candidate is kept
-  }
-
-  // ---- kept ids in id order: every key above the prefix, then the first
-  // krem keys equal to it.  One block scan of packed (above, equal) counts
-  // gives each thread the counts before its first id. ----
-  int gt = 0, eq = 0;
-  for (int j = lo; j < hi; ++j) {
-    const uint64_t mk = s_key[j] & mask;
-    gt += mk > prefix;
-    eq += mk == prefix;
-  }
-  int total;
-  const int packed = block_excl_scan<kTopkThreads>(gt | (eq << 16), s_scan, &total);
-  int gb = packed & 0xFFFF, eb = packed >> 16;
-  for (int j = lo; j < hi; ++j) {
-    const uint64_t mk = s_key[j] & mask;
-    // (positions are < k by construction; the checks keep every store inside
-    // this unit's row whatever the keys hold)
-    if (mk > prefix) {
-      const int pos = gb + min(eb, krem);
-      if (pos < k) out[pos] = j;
-      ++gb;
-    } else if (mk == prefix) {
-      if (eb < krem && gb + eb < k) out[gb + eb] = j;
-      ++eb;
-    }
-  }
+  block_topk_ids<kTopkThreads>(s_key, n, k, &s_hist[0][0], s_pick, s_scan, out);
   for (int j = k + tid; j < a.k_max; j += kTopkThreads) out[j] = -1;
   if (tid == 0) a.sel_cnt[u] = k;
   write_scores(tid, kTopkThreads);

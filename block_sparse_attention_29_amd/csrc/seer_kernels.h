@@ -36,6 +36,15 @@ struct DecodeArgs {
   int32_t* hdr;           // workspace header: [0] = W
   int32_t* prefix;        // [U + 1] block prefix over units
   float* part;            // [(U + Wmax)][G*D + 16] partial records
+  // Fused gate (gated kernel only): each workgroup selects the blocks of the
+  // units it streams.  sel_idx/sel_cnt above are unused then.
+  const float* pooled;    // [B][Hkv][D][NB]
+  const int32_t* top_k;   // [B] or nullptr (then keep_num / keep_den)
+  int32_t keep_num, keep_den;
+  double* scores;         // [B][Hkv][NB] out
+  int32_t* sel_idx_out;   // [B][Hkv][k_max] out
+  int32_t* sel_cnt_out;   // [B][Hkv] out
+  int32_t ids_cap;        // kept ids one workgroup holds in LDS
 };
 
 struct CombineArgs {
@@ -56,6 +65,11 @@ size_t decode_part_offset(int U);
 int decode_max_waves(int dtype, int D, int G);
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+// The same kernel with the gate and top-k fused in (a.pooled set).
+hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream);
+// Dynamic LDS bytes the gated kernel needs, and the ids one workgroup must hold.
+size_t gated_decode_smem_bytes(int U, int NB, int ids_cap);
+int gated_decode_ids_cap(int U, int k_max, int W);
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- gate

@@ -37,11 +37,13 @@
 
 #include "seer_device.h"
 #include "seer_kernels.h"
+#include "select_device.h"
 
 namespace seer {
 namespace {
 
 constexpr int kTile = 32;          // tokens per tile (two 16-wide MFMA columns)
+constexpr int kXcds = 8;           // XCDs (each with its own L2) of an MI355X
 constexpr int kCols = kTile / 16;  // 16-token MFMA columns per tile
 constexpr int kWavesPerWG = kDecodeWavesPerWG;
 constexpr int kThreads = kWavesPerWG * kWave;
@@ -64,19 +66,140 @@ __device__ __forceinline__ int64_t readlane64(int64_t x, int lane) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
-// Blocks a unit contributes: its kept count, or all its blocks when dense.
-__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int u) {
+// Wave owning tile y when Tot tiles are split over W waves in equal ranges.
+__device__ __forceinline__ int tile_owner(int64_t y, int W, int64_t Tot) {
+  return (int)(((y + 1) * W - 1) / Tot);
+}
+
+// Blocks a unit contributes: its kept count (given, or from the keep rule when
+// the gate is fused in), or all its blocks when dense.
+// L: the unit's sequence length.
+template <bool GATED>
+__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int u, int L) {
+  if constexpr (GATED) {
+    return kept_count(seq_blocks(L, a.S, a.NB), a.top_k, u / a.Hkv, a.keep_num, a.keep_den,
+                      a.k_max);
+  }
   if (a.sel_idx) {
     const int c = a.sel_cnt[u];
     return c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
   }
-  const int L = a.lens[u / a.Hkv];
-  if (L <= 0) return 0;
-  const int n = (int)(((int64_t)L + a.S - 1) / a.S);
-  return n > a.NB ? a.NB : n;
+  return seq_blocks(L, a.S, a.NB);
 }
 
+// VEC consecutive pooled values of one dimension row (one 4*VEC-byte load).
+template <int VEC>
+__device__ __forceinline__ void load_pooled_vec(const float* p, float (&x)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else if constexpr (VEC == 2) {
+    const float2 v = *(const float2*)p;
+    x[0] = v.x; x[1] = v.y;
+  } else {
+    x[0] = *p;
+  }
+}
+
+// Scores of unit (b, g)'s n blocks into s_key (order keys), VEC blocks per
+// lane per load: wave qd of the workgroup sums the dimensions qd*D/4 ..
+// qd*D/4 + D/4 - 1 of 64*VEC blocks per pass (one sequential fp64 FMA chain
+// per block), and the four partial sums of a block are added in quarter order
+// through LDS:
+//   s_j = (((c0 + c1) + c2) + c3) / sqrt(D),  c_q = sum_i qbar_i P_ij over quarter q,
+// qbar = sum of the group's query heads in head order (fp64): the same
+// arithmetic as the gate kernel.  The first pass's pooled loads go out before
+// the query's, so both round trips overlap.  VEC consecutive blocks are one
+// aligned load when NB is a multiple of VEC (no load crosses the table's end).
+template <typename T, int D, int G, int VEC>
+__device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, const float* pu,
+                                             int n, double* s_q, double* s_part,
+                                             uint64_t* s_key) {
+  constexpr int DQ = D / 4, PASS = 64 * VEC;
+  const int NB = a.NB;
+  const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
+  const double inv = 1.0 / sqrt((double)D);
+  for (int j0 = 0; j0 < n; j0 += PASS) {
+    // block ids past n are clamped to a valid, aligned group (read, unused)
+    const int jg = min(j0 + VEC * jq, ((n - 1) / VEC) * VEC);
+    float pv[DQ][VEC];
+    const float* row = pu + (int64_t)qd * DQ * NB + jg;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) load_pooled_vec<VEC>(row + (int64_t)i * NB, pv[i]);
+    if (j0 == 0) {
+      if (tid < D) {
+        const T* qg = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D + tid;
+        double x[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if constexpr (sizeof(T) == 2) x[h] = (double)__uint_as_float((uint32_t)qg[h * D] << 16);
+          else x[h] = (double)qg[h * D];
+        }
+        double sq = x[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) sq = sq + x[h];
+        s_q[tid] = sq;
+      }
+      __syncthreads();
+    }
+    // every load is in flight before the chains; values widen only where used
+    __builtin_amdgcn_sched_barrier(0);
+    double c[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) c[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) c[e] = fma(s_q[qd * DQ + i], (double)pv[i][e], c[e]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s_part[qd * PASS + VEC * jq + e] = c[e];
+    __syncthreads();
+    for (int t = tid; t < PASS; t += kThreads) {
+      const int j = j0 + t;
+      if (j < n) {
+        const double sc = ((s_part[t] + s_part[PASS + t]) + s_part[2 * PASS + t]) +
+                          s_part[3 * PASS + t];
+        s_key[j] = order_key(sc * inv);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Gate of unit u inside a decode workgroup (the fused mode): the fp64 scores
+// of its n blocks (fused_scores), then its k kept ids, ascending, into dst
+// (LDS).  The owner workgroup of the unit also writes the scores, ids and
+// count out.
 template <typename T, int D, int G>
+__device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
+                                                int32_t* dst,
+                                                bool owner, uint64_t* s_key, double* s_q,
+                                                double* s_part, int* s_hist, int* s_pick,
+                                                int* s_scan) {
+  const int tid = threadIdx.x;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int NB = a.NB;
+  const float* pu = a.pooled + (int64_t)u * D * NB;
+  if (NB % 4 == 0) fused_scores<T, D, G, 4>(a, b, g, pu, n, s_q, s_part, s_key);
+  else if (NB % 2 == 0) fused_scores<T, D, G, 2>(a, b, g, pu, n, s_q, s_part, s_key);
+  else fused_scores<T, D, G, 1>(a, b, g, pu, n, s_q, s_part, s_key);
+  if (k >= n) {
+    for (int i = tid; i < n; i += kThreads) dst[i] = i;
+  } else {
+    block_topk_ids<kThreads>(s_key, n, k, s_hist, s_pick, s_scan, dst);
+  }
+  __syncthreads();
+  if (owner) {
+    int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
+    for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
+    if (tid == 0) a.sel_cnt_out[u] = k;
+    double* sc = a.scores + (int64_t)u * NB;
+    for (int j = tid; j < n; j += kThreads) sc[j] = key_score(s_key[j]);
+  }
+  __syncthreads();  // s_key, s_q and s_part are reused by the next unit
+}
+
+template <typename T, int D, int G, bool GATED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partial_kernel(DecodeArgs a) {
   using GE = Geo<T, D>;
@@ -89,8 +212,9 @@ void decode_partial_kernel(DecodeArgs a) {
 
   const int U = a.B * a.Hkv;
   const int tid = threadIdx.x;
-  int* s_prefix = s_dyn;          // [U + 1]
-  int* s_scan = s_dyn + U + 1;    // [kWavesPerWG + 1]
+  int* s_prefix = s_dyn;                      // [U + 1]
+  int* s_scan = s_dyn + U + 1;                // [kWavesPerWG + 1]
+  int* s_len = s_dyn + U + 1 + kWavesPerWG + 1;  // [U] sequence length of each unit
 
   // ---- plan: block prefix over units (every workgroup computes the same) ----
   {
@@ -98,7 +222,9 @@ void decode_partial_kernel(DecodeArgs a) {
     const int u_lo = min(U, tid * per), u_hi = min(U, u_lo + per);
     int local = 0;
     for (int u = u_lo; u < u_hi; ++u) {
-      const int c = unit_blocks(a, u);
+      const int L = a.lens[u / a.Hkv];
+      const int c = unit_blocks<GATED>(a, u, L);
+      s_len[u] = L;
       s_prefix[u] = c;
       local += c;
     }
@@ -119,12 +245,73 @@ void decode_partial_kernel(DecodeArgs a) {
 
   const int lane = tid & 63, wv = tid >> 6;
   const int r16 = lane >> 4, n16 = lane & 15;
+  // Workgroups are dealt to the XCDs round-robin (workgroup i runs on XCD
+  // i % 8), each XCD with its own L2.  Consecutive tile ranges go to the
+  // workgroups of one XCD, so the workgroups that share a unit mostly share an
+  // L2 (its pooled table, read by each of them in the fused gate, comes from
+  // HBM once).  Any other placement is still correct.
+  const int nwg = (int)gridDim.x;
+  const int wg = (nwg % kXcds == 0)
+      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
+      : (int)blockIdx.x;
   // The wave index is uniform per wave; say so, so that everything derived
   // from it (the tile range, the loop counters) lives in scalar registers.
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + wv);
+  const int w = __builtin_amdgcn_readfirstlane(wg * kWavesPerWG + wv);
   // Tile coordinates fit in 32 bits: units * blocks * tiles per block < 2^31.
   const int tsh = 31 - __builtin_clz(a.S / kTile);  // log2(tiles per block)
   const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
+
+  // Largest unit whose first tile is <= y (units without blocks share their
+  // first tile with the next unit and are skipped by the callers).
+  auto unit_at = [&](int y) {
+    int lo = 0, hi = U - 1;
+    const int x = y >> tsh;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  // ---- fused gate: the selections of every unit this workgroup streams, into
+  // LDS (each workgroup selects on its own; a unit shared by workgroups is
+  // selected by each of them, bit-identically) ----
+  int32_t* s_ids = s_len + U;  // [ids_cap] kept ids of this workgroup's units, slot - ids_base
+  int ids_base = 0;
+  if constexpr (GATED) {
+    __shared__ double s_q[D];
+    __shared__ double s_part[4 * 256];  // quarter sums of one pass (4 x 64*VEC)
+    __shared__ int s_hist[512];
+    __shared__ int s_pick[3];
+    __shared__ int s_sel_scan[kWavesPerWG + 1];
+    uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
+    const int wg0 = wg * kWavesPerWG;
+    const int Y0 = (int)((int64_t)wg0 * Tot / a.W);
+    const int Y1 = (int)((int64_t)(wg0 + kWavesPerWG) * Tot / a.W);
+    if (Y0 < Y1) {
+      const int u0 = unit_at(Y0), u1 = unit_at(Y1 - 1);
+      ids_base = s_prefix[u0];
+      for (int u = u0; u <= u1; ++u) {
+        const int k = s_prefix[u + 1] - s_prefix[u];
+        if (k == 0) continue;
+        // the owner holds the unit's first tile
+        const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
+        fused_gate_unit<T, D, G>(a, u, seq_blocks(s_len[u], a.S, a.NB), k,
+                                 s_ids + (s_prefix[u] - ids_base),
+                                 owner == wg, s_key, s_q, s_part, s_hist,
+                                 s_pick, s_sel_scan);
+      }
+    }
+    // Units without a kept block (a sequence of length 0) belong to nobody:
+    // workgroup 0 writes their (empty) selection.
+    if (blockIdx.x == 0) {
+      for (int u = tid; u < U; u += kThreads) {
+        if (s_prefix[u] != s_prefix[u + 1]) continue;
+        for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)u * a.k_max + i] = -1;
+        a.sel_cnt_out[u] = 0;
+      }
+    }
+  }
   const int y0 = (int)((int64_t)w * Tot / a.W);
   const int y1 = (int)((int64_t)(w + 1) * Tot / a.W);
   if (y0 >= y1) return;
@@ -137,16 +324,7 @@ void decode_partial_kernel(DecodeArgs a) {
   const float sl = a.scale_log2;
 
   // First unit of the range: largest u with s_prefix[u] <= block of y0.
-  int u;
-  {
-    int lo = 0, hi = U - 1;
-    const int x0 = y0 >> tsh;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= x0) lo = mid; else hi = mid - 1;
-    }
-    u = __builtin_amdgcn_readfirstlane(lo);
-  }
+  int u = __builtin_amdgcn_readfirstlane(unit_at(y0));
 
   int y = y0;
   while (y < y1) {
@@ -155,7 +333,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int Yu = __builtin_amdgcn_readfirstlane(s_prefix[u]) << tsh;
     const int ye = min(y1, __builtin_amdgcn_readfirstlane(s_prefix[u + 1]) << tsh);
     const int b = u / Hkv, g = u - b * Hkv;
-    const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[u]);
 
     // Per-lane descriptors of 64 consecutive kept blocks (slots) of unit u.
     int cs = -(1 << 30);
@@ -167,7 +345,9 @@ void decode_partial_kernel(DecodeArgs a) {
       int nv = 0;
       int64_t off = 0;
       if (slot < s_prefix[u + 1] - s_prefix[u]) {
-        const int j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
+        int j;
+        if constexpr (GATED) j = s_ids[s_prefix[u] - ids_base + slot];
+        else j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
         if (j >= 0 && j < NB && (int64_t)j * S < L) {
           nv = min(S, L - j * S);
           if (a.page_table) {
@@ -576,32 +756,38 @@ void decode_combine_kernel(CombineArgs a) {
   }
 }
 
-template <typename T, int D, int G>
-const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G>; }
+template <typename T, int D, int G, bool GATED>
+const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G, GATED>; }
 
 using KernelFn = const void* (*)();
 
-template <typename T, int D>
+template <typename T, int D, bool GATED>
 KernelFn pick_g(int G) {
   switch (G) {
-    case 1: return &partial_fn<T, D, 1>;
-    case 2: return &partial_fn<T, D, 2>;
-    case 3: return &partial_fn<T, D, 3>;
-    case 4: return &partial_fn<T, D, 4>;
-    case 5: return &partial_fn<T, D, 5>;
-    case 6: return &partial_fn<T, D, 6>;
-    case 7: return &partial_fn<T, D, 7>;
-    case 8: return &partial_fn<T, D, 8>;
+    case 1: return &partial_fn<T, D, 1, GATED>;
+    case 2: return &partial_fn<T, D, 2, GATED>;
+    case 3: return &partial_fn<T, D, 3, GATED>;
+    case 4: return &partial_fn<T, D, 4, GATED>;
+    case 5: return &partial_fn<T, D, 5, GATED>;
+    case 6: return &partial_fn<T, D, 6, GATED>;
+    case 7: return &partial_fn<T, D, 7, GATED>;
+    case 8: return &partial_fn<T, D, 8, GATED>;
   }
   return nullptr;
 }
 
-const void* partial_kernel(int dtype, int D, int G) {
+template <bool GATED>
+const void* pick_kernel(int dtype, int D, int G) {
   KernelFn f = nullptr;
-  if (dtype == 1) f = D == 64 ? pick_g<uint16_t, 64>(G) : D == 128 ? pick_g<uint16_t, 128>(G) : nullptr;
-  else f = D == 64 ? pick_g<float, 64>(G) : D == 128 ? pick_g<float, 128>(G) : nullptr;
+  if (dtype == 1)
+    f = D == 64 ? pick_g<uint16_t, 64, GATED>(G) : D == 128 ? pick_g<uint16_t, 128, GATED>(G) : nullptr;
+  else
+    f = D == 64 ? pick_g<float, 64, GATED>(G) : D == 128 ? pick_g<float, 128, GATED>(G) : nullptr;
   return f ? f() : nullptr;
 }
+
+const void* partial_kernel(int dtype, int D, int G) { return pick_kernel<false>(dtype, D, G); }
+const void* gated_kernel(int dtype, int D, int G) { return pick_kernel<true>(dtype, D, G); }
 
 template <int D>
 const void* combine_g(int G) {
@@ -618,7 +804,8 @@ const void* combine_g(int G) {
   return nullptr;
 }
 
-size_t prefix_smem_bytes(int U) { return (size_t)(U + 1 + kWavesPerWG + 1) * sizeof(int); }
+// Plan buffer: unit prefix [U + 1], scan scratch, unit lengths [U].
+size_t prefix_smem_bytes(int U) { return (size_t)(2 * U + 1 + kWavesPerWG + 1) * sizeof(int); }
 
 }  // namespace
 
@@ -650,7 +837,7 @@ int decode_max_waves(int dtype, int D, int G) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   // The kernel must fit on a CU with the largest plan buffer; it then runs
   // one workgroup per CU (see kDecodeWavesPerWG).
-  const size_t smem = (size_t)(kMaxUnits + 1 + kWavesPerWG + 1) * sizeof(int);
+  const size_t smem = prefix_smem_bytes(kMaxUnits);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, smem) != hipSuccess) return 0;
   if (blocks < 1) return 0;
   const int waves = cus * kWavesPerWG;
@@ -667,6 +854,31 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   void* params[] = {&args};
   return hipLaunchKernel(fn, dim3(a.W / kWavesPerWG), dim3(kThreads), params,
                          prefix_smem_bytes(U), stream);
+}
+
+size_t gated_decode_smem_bytes(int U, int NB, int ids_cap) {
+  const size_t ints = prefix_smem_bytes(U) + (size_t)ids_cap * sizeof(int32_t);
+  return ((ints + 7) & ~(size_t)7) + (size_t)NB * sizeof(uint64_t);
+}
+
+int gated_decode_ids_cap(int U, int k_max, int W) {
+  // A workgroup's tile range holds at most ceil(total / workgroups) tiles; the
+  // units it meets add at most the rest of the first and the last unit.
+  const int64_t wgs = W / kWavesPerWG;
+  const int64_t blocks = (int64_t)U * k_max;
+  const int64_t cap = (blocks + wgs - 1) / wgs + 2 * (int64_t)k_max + 2;
+  return (int)(cap < blocks ? cap : blocks);
+}
+
+hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const void* fn = gated_kernel(a.dtype, a.D, G);
+  if (!fn) return hipErrorInvalidValue;
+  const int U = a.B * a.Hkv;
+  DecodeArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(fn, dim3(a.W / kWavesPerWG), dim3(kThreads), params,
+                         gated_decode_smem_bytes(U, a.NB, a.ids_cap), stream);
 }
 
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream) {

@@ -7,6 +7,9 @@ table, open-block sums, scores, selection, outputs, workspace) and enqueues:
     append(lens_old, lens_new)   incremental pooling of newly cached tokens
     select(q, lens)              gate scores + top-k block selection
     attend(q, lens)              sparse (or dense) decode attention
+    step(q, lens)                select + attend, the gate fused into the attention
+                                 kernel (two launches)
+    step_unfused(q, lens)        select, then attend (three launches)
 
 all on torch's current stream, with no host synchronisation.
 """
@@ -77,6 +80,15 @@ class DecodeState:
         return self.out, self.lse
 
     def step(self, q: torch.Tensor, lens: torch.Tensor):
-        """Gate, select and attend: one decode step over a built pooled table."""
+        """Gate, select and attend: one decode step over a built pooled table
+        (the gate fused into the attention kernel)."""
+        num, den = self.keep if self.keep is not None else (1, 1)
+        seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.top_k, num, den,
+                                 self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,
+                                 self.lse, self.workspace)
+        return self.out, self.lse
+
+    def step_unfused(self, q: torch.Tensor, lens: torch.Tensor):
+        """The same step as three launches: gate kernel, then attention."""
         self.select(q, lens)
         return self.attend(q, lens)

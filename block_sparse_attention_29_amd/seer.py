@@ -34,6 +34,8 @@ EXPORTS = (
     "seer_sparse_decode",
     "seer_sparse_decode_partial",
     "seer_sparse_decode_combine",
+    "seer_gated_sparse_decode",
+    "seer_gated_sparse_decode_partial",
     "seer_keep_blocks",
     "seer_status_str",
     "seer_last_error",
@@ -97,6 +99,12 @@ def load(path: str = LIB_PATH):
     lib.seer_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, _P, _I32, ctypes.c_float, _P,
                                                ctypes.c_size_t, _P]
     lib.seer_sparse_decode_combine.argtypes = [SP, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, _P, _I32, _I32, _I32,
+                                             ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]
+    lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, _P, _I32, _I32, _I32,
+                                                     ctypes.c_float, _P, _P, _P, _P,
+                                                     ctypes.c_size_t, _P]
     lib.seer_keep_blocks.argtypes = [_I32, _I32, _I32]
     lib.seer_keep_blocks.restype = _I32
     lib.seer_status_str.argtypes = [_I32]
@@ -105,7 +113,8 @@ def load(path: str = LIB_PATH):
     lib.seer_last_error.restype = ctypes.c_char_p
     for name in ("seer_block_pool_keys", "seer_gate_scores_topk",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
-                 "seer_sparse_decode_partial", "seer_sparse_decode_combine"):
+                 "seer_sparse_decode_partial", "seer_sparse_decode_combine",
+                 "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial"):
         getattr(lib, name).restype = _I32
     _lib = lib
     return lib
@@ -217,3 +226,35 @@ def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.T
     _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
     _check(lib.seer_sparse_decode_combine(ctypes.byref(shape), _ptr(out), _ptr(lse),
                                           _ptr(workspace), workspace.numel(), _stream()))
+
+
+def gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
+                        pooled: torch.Tensor, top_k: Optional[torch.Tensor], keep_num: int,
+                        keep_den: int, k_max: int, scores: torch.Tensor, sel_idx: torch.Tensor,
+                        sel_cnt: torch.Tensor, out: Optional[torch.Tensor],
+                        lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                        softmax_scale: float = 0.0):
+    """Gate, top-k and sparse decode in two launches; out=None stops after the
+    first (the partial results stay in the workspace for sparse_decode_combine)."""
+    lib = load()
+    U = shape.batch * shape.num_kv_heads
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    if top_k is not None:
+        _need(top_k, torch.int32, shape.batch, "top_k")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    if out is None:
+        _check(lib.seer_gated_sparse_decode_partial(
+            ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
+            _ptr(top_k), keep_num, keep_den, k_max, softmax_scale, _ptr(scores), _ptr(sel_idx),
+            _ptr(sel_cnt), _ptr(workspace), workspace.numel(), _stream()))
+        return
+    _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
+    _check(lib.seer_gated_sparse_decode(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled), _ptr(top_k),
+        keep_num, keep_den, k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))

@@ -174,6 +174,38 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
                                        const void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/* seer_gated_sparse_decode -- one decode step from the pooled table: gate
+ * scores, top-k selection and sparse attention, as seer_gate_scores_topk
+ * followed by seer_sparse_decode on its selection, with bit-identical
+ * results (scores, sel_idx, sel_cnt, out, lse), in two launches instead of
+ * three: every workgroup of the attention kernel selects the blocks of the
+ * (sequence, KV head) pairs it streams itself, so the attention does not wait
+ * for a separate gate launch ("SeerAttention-R: Sparse Attention Adaptation
+ * for Long Reasoning", Abstract: gating on pooled keys with a sparse decoding
+ * kernel; "Sparse Attention Reasoning", Step 1 and Step 4).
+ *  Arguments: as seer_gate_scores_topk (q, pooled, lens, top_k / keep rule,
+ *  k_max, scores, sel_idx, sel_cnt, all outputs written) and
+ *  seer_sparse_decode (kv, softmax_scale, out, lse, workspace).
+ *  When one workgroup's selections would not fit in its LDS the call runs
+ *  the gate kernel first instead (same results).
+ * _partial: the first launch alone (gate + partial results in the workspace,
+ * selections written); seer_sparse_decode_combine finishes it. */
+seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
+                                     const int32_t* lens, const float* pooled,
+                                     const int32_t* top_k, int32_t keep_num, int32_t keep_den,
+                                     int32_t k_max, float softmax_scale, double* scores,
+                                     int32_t* sel_idx, int32_t* sel_cnt, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void* q,
+                                             const seer_kv* kv, const int32_t* lens,
+                                             const float* pooled, const int32_t* top_k,
+                                             int32_t keep_num, int32_t keep_den, int32_t k_max,
+                                             float softmax_scale, double* scores,
+                                             int32_t* sel_idx, int32_t* sel_cnt,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+
 /* Host helper: max(1, min(n, ceil(n * keep_num / keep_den))), or -1 for bad
  * arguments (n < 1, keep_num < 1, keep_den < keep_num). */
 int32_t seer_keep_blocks(int32_t n_blocks, int32_t keep_num, int32_t keep_den);

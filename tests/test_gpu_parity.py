@@ -154,6 +154,59 @@ def test_decode_with_oracle_selection():
         assert np.abs(out - ref["out"]).max() <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name", sorted(SMALL) + ["budget_32k", "long_131k"])
+def test_gated_equals_separate_calls_bitwise(name):
+    """The fused gate + attention call writes exactly what the gate call
+    followed by the attention call writes: scores, ids, counts, out, lse."""
+    wl = SMALL[name] if name in SMALL else WORKLOADS[name].with_(batch=2)
+    print(f"[case] gated vs separate {name}", flush=True)
+    case = make_case(wl, "cuda")
+    q = case.q[0] if wl.decode_steps else case.q
+    fused, sep = state_for(case), state_for(case)
+    for st in (fused, sep):
+        st.build_pool(case.lens)
+    fused.step(q, case.lens)
+    sep.step_unfused(q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
+
+
+def test_gated_with_a_wide_block_table():
+    """8192 blocks per sequence (the largest table): the gated call matches the
+    separate calls and the oracle (its key buffer alone is 64 KiB of LDS)."""
+    S, d, NB, L = 64, 64, 8192, 3000
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8192)
+    k = torch.zeros(1, 1, NB * S, d, device="cuda")
+    v = torch.zeros_like(k)
+    k[0, 0, :L] = torch.randn(L, d, generator=gen, device="cuda")
+    v[0, 0, :L] = torch.randn(L, d, generator=gen, device="cuda")
+    q = torch.randn(1, 4, d, generator=gen, device="cuda")
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    top_k = torch.tensor([7], dtype=torch.int32, device="cuda")
+    sts = [DecodeState(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=d, block_size=S,
+                       max_blocks=NB, dtype=torch.float32, k=k, v=v, k_max=16, top_k=top_k)
+           for _ in range(2)]
+    for st in sts:
+        st.build_pool(lens)
+    sts[0].step(q, lens)
+    sts[1].step_unfused(q, lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(sts[0], attr), getattr(sts[1], attr)), attr
+    kk, vv = f64(k[0, 0, :L]), f64(v[0, 0, :L])
+    p32, _, _ = O.pool_keys(kk, L, S)
+    qg = f64(q[0])
+    s = O.gate_scores(qg, p32, d)
+    sel = O.select_top_blocks(s, O.clamp_count(7, O.block_count(L, S)))
+    assert np.array_equal(sts[0].sel_idx[0, :7].cpu().numpy(), sel)
+    toks = O.selected_tokens(sel, L, S)
+    for h in range(4):
+        o, lse, _ = O.attend(qg[h], kk, vv, toks)
+        assert np.abs(sts[0].out[0, h].cpu().double().numpy() - o).max() <= TOL["f32"]
+
+
 def test_paged_equals_contiguous_bitwise():
     wl = SMALL["paged_small"]
     case = make_case(wl, "cuda")
