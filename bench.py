@@ -4,7 +4,8 @@ Workload (default ``sparse90_32k``): 16 sequences of 32768 tokens, 32 query /
 8 KV heads, head_dim 128, 128-token blocks, 90% sparsity (26 of 256 blocks kept
 per KV head), bf16 KV cache.  A step = gate scores + top-k selection + sparse
 decode (split-KV partials, then their log-sum-exp combine) for one attention
-layer; the pooled-key table is built once beforehand (after prefill).  For a
+layer, as two launches: the attention kernel with the gate fused in, then the
+combine; the pooled-key table is built once beforehand (after prefill).  For a
 workload with an incremental decode loop (``long_131k``) a step also appends
 the new token to the pooled table, and the timed loop runs every decode step
 of the loop, the context growing by one token per step.  The timed loop cycles
@@ -16,9 +17,11 @@ Timed regions are replays of HIP graphs captured from the library's launches
 
 Prints one JSON line per workload (``--workload all``: every workload).
 ``value`` is decode tokens/s for one attention layer (sequences x steps /
-time); ``roofline`` reports the partial-decode kernel's algorithmic bytes per
-launch over its mean launch time (HIP events on the launch stream) against the
-8 TB/s HBM peak; ``dense`` times the same step with every block kept;
+time); ``roofline`` reports the fused gate + partial-decode kernel's
+algorithmic bytes per launch (pooled table, kept K/V rows, query) over its mean
+launch time (HIP events on the launch stream) against the 8 TB/s HBM peak;
+``unfused`` times the same step as three launches (gate kernel, partial,
+combine); ``dense`` times the same step with every block kept;
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload.
 """
@@ -36,12 +39,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), 90% sparsity, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
-# Measured HBM bytes per launch of the partial kernel (rocprofv3 FETCH_SIZE and
+# Measured HBM bytes per launch of the fused kernel (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, calibrated on a plain copy), valid only for the kernel sources
 # whose digest the file records.
 KERNEL_SOURCES = ["block_sparse_attention_29_amd/csrc/sparse_decode.hip",
                   "block_sparse_attention_29_amd/csrc/seer_device.h",
                   "block_sparse_attention_29_amd/csrc/seer_kernels.h",
+                  "block_sparse_attention_29_amd/csrc/select_device.h",
                   "block_sparse_attention_29_amd/build.py"]
 
 
@@ -59,7 +63,7 @@ def kernel_source_digest() -> str:
 
 
 def measured_traffic(workload: str):
-    """Counter-measured bytes per partial launch, or None when the counters were
+    """Counter-measured bytes per fused launch, or None when the counters were
     taken on other kernel sources (or another workload)."""
     try:
         fields = {}
@@ -167,14 +171,21 @@ def run_workload(wl, args):
     def layer_of(i):
         return states[i % n_layers], cases[i % n_layers]
 
-    def step(i):
+    def step(i, fused=True):
         st, case = layer_of(i)
         if loop:
             s = i // n_layers                         # decode step of the loop
             st.append(lens_seq[s], lens_seq[s + 1])
-            st.step(case.q[s], lens_seq[s + 1])
+            q, lens = case.q[s], lens_seq[s + 1]
         else:
-            st.step(case.q, case.lens)
+            q, lens = case.q, case.lens
+        if fused:
+            st.step(q, lens)
+        else:
+            st.step_unfused(q, lens)
+
+    def step_unfused(i):
+        step(i, fused=False)
 
     def q_lens(i):
         st, case = layer_of(i)
@@ -184,10 +195,13 @@ def run_workload(wl, args):
         return case.q, case.lens
 
     def partial_only(i):
+        """The fused gate + partial-decode kernel alone (no combine)."""
         st, case = layer_of(i)
         q, lens = q_lens(i)
-        seer.sparse_decode_partial(st.shape, q, st.kv, lens, st.sel_idx, st.sel_cnt,
-                                   st.k_max, st.workspace)
+        num, den = st.keep if st.keep is not None else (1, 1)
+        seer.gated_sparse_decode(st.shape, q, st.kv, lens, st.pooled, st.top_k, num, den,
+                                 st.k_max, st.scores, st.sel_idx, st.sel_cnt, None, None,
+                                 st.workspace)
 
     def dense_step(i):
         st, case = layer_of(i)
@@ -238,19 +252,28 @@ def run_workload(wl, args):
     wall = time.perf_counter() - wall0
     ms_per_step = ms_total / n_steps
     tokens_per_s = wl.batch * n_steps / (ms_total / 1e3)
+    del g_steps
 
-    # ---- partial-kernel timing: back-to-back launches in one graph, events
-    # around it on the launch stream (selections computed beforehand) ----
-    for i in range(n_layers):
-        q, lens = q_lens(i)
-        states[i].select(q, lens)
+    # ---- the same steps as three launches (gate kernel, partial, combine) ----
+    if loop:
+        reset_pools()
+    g_unf = capture(step_unfused, n_steps)
+    if loop:
+        reset_pools()
+    unfused_ms = timed(g_unf) / n_steps
+    del g_unf
+    if loop:
+        reset_pools()
+
+    # ---- fused-kernel timing: back-to-back launches in one graph, events
+    # around it on the launch stream ----
     n_k = n_layers if loop else max(4 * n_layers, n_steps // 2)
     g_part = capture(partial_only, n_k)
     timed(g_part)
     k_ms = timed(g_part, 3) / (3 * n_k)
 
-    # algorithmic bytes of one partial launch (layer 0, the selection just
-    # made): valid K/V tokens of the kept blocks plus the query
+    # algorithmic bytes of one fused launch (layer 0, the selection it just
+    # made): the pooled table, valid K/V tokens of the kept blocks, the query
     st0 = states[0]
     q0, lens0 = q_lens(0)
     torch.cuda.synchronize()
@@ -265,14 +288,11 @@ def run_workload(wl, args):
             tokens += min(S, L - int(j) * S)
     kv_bytes = tokens * d * e * 2
     q_bytes = wl.batch * wl.num_q_heads * d * e
-    k_bytes = kv_bytes + q_bytes
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
-
-    # whole-step algorithmic bytes: + pooled-key table read by the gate
     blocks = int(sum(-(-int(L) // S) for L in lens))
     pooled_bytes = blocks * wl.num_kv_heads * d * 4
-    step_bytes = k_bytes + pooled_bytes
-    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    k_bytes = kv_bytes + q_bytes + pooled_bytes
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    step_gbps = k_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---- dense decode at the same shape (speedup denominator) ----
     dense = None
@@ -318,7 +338,10 @@ def run_workload(wl, args):
         "config": config,
         "step_hbm_gbps": step_gbps,
         "step_pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "kernel": f"decode_partial_kernel<{wl.dtype},{d},{G}>",
+        "unfused": {"ms_per_step": unfused_ms,
+                    "speedup_fused_vs_unfused": unfused_ms / ms_per_step},
+        "roofline": {"bound": "hbm",
+                     "kernel": f"decode_partial_kernel<{wl.dtype},{d},{G},gated>",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},

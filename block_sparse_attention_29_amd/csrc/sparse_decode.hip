@@ -261,17 +261,24 @@ void decode_partial_kernel(DecodeArgs a) {
   const int tsh = 31 - __builtin_clz(a.S / kTile);  // log2(tiles per block)
   const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
 
-  // Largest unit whose first tile is <= y (units without blocks share their
-  // first tile with the next unit and are skipped by the callers).
-  auto unit_at = [&](int y) {
-    int lo = 0, hi = U - 1;
-    const int x = y >> tsh;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= x) lo = mid; else hi = mid - 1;
+  // ---- units holding the first tile of each wave of this workgroup and the
+  // workgroup's last tile, looked up by all threads at once (one pass over
+  // the units instead of a serial binary search per wave) ----
+  __shared__ int s_unit[kWavesPerWG + 1];
+  const int wg0 = wg * kWavesPerWG;
+  {
+    int xq[kWavesPerWG + 1];  // block index of each query tile
+#pragma unroll
+    for (int v = 0; v < kWavesPerWG; ++v) xq[v] = (int)((int64_t)(wg0 + v) * Tot / a.W) >> tsh;
+    xq[kWavesPerWG] = ((int)((int64_t)(wg0 + kWavesPerWG) * Tot / a.W) - 1) >> tsh;
+    for (int uu = tid; uu < U; uu += kThreads) {
+      const int lo = s_prefix[uu], hi = s_prefix[uu + 1];
+#pragma unroll
+      for (int v = 0; v <= kWavesPerWG; ++v)
+        if (lo <= xq[v] && xq[v] < hi) s_unit[v] = uu;
     }
-    return lo;
-  };
+    __syncthreads();
+  }
 
   // ---- fused gate: the selections of every unit this workgroup streams, into
   // LDS (each workgroup selects on its own; a unit shared by workgroups is
@@ -285,11 +292,10 @@ void decode_partial_kernel(DecodeArgs a) {
     __shared__ int s_pick[3];
     __shared__ int s_sel_scan[kWavesPerWG + 1];
     uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
-    const int wg0 = wg * kWavesPerWG;
     const int Y0 = (int)((int64_t)wg0 * Tot / a.W);
     const int Y1 = (int)((int64_t)(wg0 + kWavesPerWG) * Tot / a.W);
     if (Y0 < Y1) {
-      const int u0 = unit_at(Y0), u1 = unit_at(Y1 - 1);
+      const int u0 = s_unit[0], u1 = s_unit[kWavesPerWG];
       ids_base = s_prefix[u0];
       for (int u = u0; u <= u1; ++u) {
         const int k = s_prefix[u + 1] - s_prefix[u];
@@ -324,7 +330,7 @@ void decode_partial_kernel(DecodeArgs a) {
   const float sl = a.scale_log2;
 
   // First unit of the range: largest u with s_prefix[u] <= block of y0.
-  int u = __builtin_amdgcn_readfirstlane(unit_at(y0));
+  int u = __builtin_amdgcn_readfirstlane(s_unit[wv]);
 
   int y = y0;
   while (y < y1) {
