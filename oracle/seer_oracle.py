@@ -162,6 +162,64 @@ def select_top_blocks(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[: int(k)])
 
 
+def gate_scores_unified(q_seq: np.ndarray, pooled_heads: Sequence[np.ndarray],
+                        head_dim: int) -> np.ndarray:
+    """One score per block for a whole sequence: the KV heads' gate scores
+    summed, s_j = sum_g sum_{h in group(g)} q_h . P_{g,j} / sqrt(d).
+
+    q_seq: (Hq, d) float64, all query heads of the sequence (head h belongs to
+    KV head h // G); pooled_heads[g]: (n, d), KV head g's stored pooled keys.
+    The cross-head selection of the LessIsMore abstract (author page "Shijie
+    Cao"): one ranking for every head of a layer instead of one per head.
+    """
+    Hkv = len(pooled_heads)
+    G = q_seq.shape[0] // Hkv
+    n = np.asarray(pooled_heads[0]).shape[0]
+    s = np.zeros(n, dtype=np.float64)
+    for g in range(Hkv):
+        p = np.asarray(pooled_heads[g], dtype=np.float64)
+        for h in range(g * G, (g + 1) * G):
+            s = s + p @ q_seq[h]
+    return s / np.sqrt(float(head_dim))
+
+
+def select_blocks(scores: np.ndarray, *, k: Optional[int] = None,
+                  threshold: Optional[float] = None, force_first: bool = False,
+                  force_last: bool = False, k_max: Optional[int] = None) -> np.ndarray:
+    """Kept block ids (ascending) of one selection under the general rule.
+
+    Forced blocks F: block 0 when ``force_first`` (an attention sink) and the
+    newest block n-1 when ``force_last`` (the recent context the LessIsMore
+    abstract keeps); they are kept whatever their score.
+    Top-k (``k`` given): the count is raised to |F| if smaller and capped at
+    min(n, k_max); the kept set is F plus the best other blocks by
+    (score desc, id asc) up to that count.
+    Threshold (``threshold`` = tau given): the hard gate of "Sparse Attention
+    Reasoning" (Step 1, the selection with a temperature keeps
+    sigmoid(s / T) > 0.5, i.e. s > 0 for any T > 0), generalised to s > tau:
+    the kept set is F plus every other block with s_j > tau; past k_max
+    blocks, F plus the best of them up to k_max; if empty, the single best
+    block.
+    """
+    s = np.asarray(scores, dtype=np.float64) + 0.0       # -0.0 + 0.0 is +0.0
+    n = s.shape[0]
+    cap = n if k_max is None else min(n, int(k_max))
+    forced = []
+    if force_first:
+        forced.append(0)
+    if force_last and (n - 1) not in forced:
+        forced.append(n - 1)
+    rest = np.array([j for j in range(n) if j not in forced], dtype=np.int64)
+    ranked = rest[np.lexsort((rest, -s[rest]))] if len(rest) else rest
+    if threshold is None:
+        count = max(int(k), len(forced))
+    else:
+        count = len(forced) + int(np.sum(s[rest] > float(threshold)))
+    count = max(1, min(count, cap))
+    kept = forced[:count] + list(ranked[: count - min(count, len(forced))])
+    return np.sort(np.array(kept, dtype=np.int64))
+
+
 # --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------

@@ -351,3 +351,90 @@ def test_pool_signed_zero_sum_of_valid_keys_only():
     p32, p64, _ = O.pool_keys(keys, 6, 4)
     assert np.signbit(p64[1]).all() and np.signbit(p32[1]).all()
     assert not np.signbit(p64[0]).any()
+
+
+# ------------------------------------------------------------------ selection rules
+
+def _rule_brute_force(s, k, forced, cap):
+    """Direct check of the top-k-with-forced-blocks definition."""
+    n = len(s)
+    count = max(1, min(max(k, len(forced)), cap))
+    chosen = list(forced[:count])
+    others = [j for j in range(n) if j not in forced]
+    while len(chosen) < count:
+        best = None
+        for j in others:
+            if j in chosen:
+                continue
+            if best is None or s[j] > s[best] or (s[j] == s[best] and j < best):
+                best = j
+        chosen.append(best)
+    return sorted(chosen)
+
+
+def test_select_blocks_reduces_to_plain_top_k():
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        s = np.round(rng.standard_normal(n), 1)          # many ties
+        k = int(rng.integers(1, n + 1))
+        assert np.array_equal(O.select_blocks(s, k=k), O.select_top_blocks(s, k))
+
+
+def test_select_blocks_forced_brute_force():
+    rng = np.random.default_rng(42)
+    for _ in range(300):
+        n = int(rng.integers(1, 30))
+        s = np.round(rng.standard_normal(n), 1)
+        k = int(rng.integers(1, n + 1))
+        ff, fl = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        cap = int(rng.integers(1, n + 1))
+        forced = ([0] if ff else []) + ([n - 1] if fl and not (ff and n == 1) else [])
+        got = O.select_blocks(s, k=k, force_first=ff, force_last=fl, k_max=cap)
+        assert list(got) == _rule_brute_force(s, k, forced, cap)
+        for f in forced[: len(got)]:
+            assert f in got
+
+
+def test_threshold_zero_is_the_sigmoid_gate():
+    """The pages' hard gate keeps sigmoid(s / T) > 0.5; with tau = 0 the rule
+    keeps exactly those blocks, whatever the temperature T > 0."""
+    rng = np.random.default_rng(43)
+    for T in (0.05, 1.0, 20.0):
+        for _ in range(50):
+            s = rng.standard_normal(64) * 3
+            gate = 1.0 / (1.0 + np.exp(-s / T)) > 0.5
+            if not gate.any():
+                continue
+            assert np.array_equal(O.select_blocks(s, threshold=0.0), np.nonzero(gate)[0])
+
+
+def test_threshold_edges():
+    s = np.array([-1.0, -0.5, -2.0, -0.5])
+    assert list(O.select_blocks(s, threshold=0.0)) == [1]        # none above: the best block
+    s = np.array([3.0, 1.0, 2.0, 5.0, 4.0])
+    assert list(O.select_blocks(s, threshold=0.0, k_max=2)) == [3, 4]   # capped: the best two
+    assert list(O.select_blocks(s, threshold=2.5)) == [0, 3, 4]
+    # forced blocks count towards the threshold set and survive the cap first
+    assert list(O.select_blocks(s, threshold=2.5, force_first=True, force_last=True,
+                                k_max=3)) == [0, 3, 4]
+    assert list(O.select_blocks(np.array([-0.0, 0.0, 1.0]), threshold=0.0)) == [2]
+
+
+def test_unified_scores_pins():
+    rng = np.random.default_rng(44)
+    d, n, Hkv, G = 16, 12, 3, 2
+    q = rng.standard_normal((Hkv * G, d))
+    P = [rng.standard_normal((n, d)).astype(np.float32).astype(np.float64) for _ in range(Hkv)]
+    # one KV head: the per-head gate score
+    assert np.array_equal(O.gate_scores_unified(q[:G], P[:1], d), O.gate_scores(q[:G], P[0], d))
+    # scaling the query by 2 doubles every score exactly
+    assert np.array_equal(O.gate_scores_unified(2 * q, P, d), 2 * O.gate_scores_unified(q, P, d))
+    # the sum of the per-head scores (equal up to the order of the additions)
+    per = sum(O.gate_scores(q[g * G:(g + 1) * G], P[g], d) for g in range(Hkv))
+    assert np.allclose(O.gate_scores_unified(q, P, d), per, rtol=1e-14, atol=1e-14)
+    # reordering the KV heads (with their query groups) changes nothing but rounding
+    perm = [2, 0, 1]
+    qp = np.concatenate([q[g * G:(g + 1) * G] for g in perm])
+    assert np.allclose(O.gate_scores_unified(qp, [P[g] for g in perm], d),
+                       O.gate_scores_unified(q, P, d), rtol=1e-14, atol=1e-14)
