@@ -198,10 +198,8 @@ def run_workload(wl, args):
         """The fused gate + partial-decode kernel alone (no combine)."""
         st, case = layer_of(i)
         q, lens = q_lens(i)
-        num, den = st.keep if st.keep is not None else (1, 1)
-        seer.gated_sparse_decode(st.shape, q, st.kv, lens, st.pooled, st.top_k, num, den,
-                                 st.k_max, st.scores, st.sel_idx, st.sel_cnt, None, None,
-                                 st.workspace)
+        seer.gated_sparse_decode(st.shape, q, st.kv, lens, st.pooled, st.rule, st.k_max,
+                                 st.scores, st.sel_idx, st.sel_cnt, None, None, st.workspace)
 
     def dense_step(i):
         st, case = layer_of(i)

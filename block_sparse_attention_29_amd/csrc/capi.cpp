@@ -140,21 +140,25 @@ seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv
 
 // Validates the gate's arguments.
 seer_status check_gate(const seer_shape* shape, const void* q, const float* pooled,
-                       const int32_t* lens, const int32_t* top_k, int32_t keep_num,
-                       int32_t keep_den, int32_t k_max, const double* scores,
-                       const int32_t* sel_idx, const int32_t* sel_cnt) {
+                       const int32_t* lens, const seer_select* rule, int32_t k_max,
+                       const double* scores, const int32_t* sel_idx, const int32_t* sel_cnt) {
   seer_status st = check_shape(shape);
   if (st) return st;
-  if (!q || !pooled || !lens || !scores || !sel_idx || !sel_cnt)
+  if (!q || !pooled || !lens || !rule || !scores || !sel_idx || !sel_cnt)
     return fail(SEER_ERR_INVALID_ARG, "a required pointer is NULL");
   if (k_max < 1 || k_max > shape->max_blocks)
     return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
                 shape->max_blocks);
-  if (!top_k) {
-    const int32_t kk = seer_keep_blocks(shape->max_blocks, keep_num, keep_den);
+  if (rule->mode != SEER_SELECT_TOPK && rule->mode != SEER_SELECT_THRESHOLD)
+    return fail(SEER_ERR_INVALID_ARG, "selection mode %d is not a seer_select_mode", rule->mode);
+  if (rule->mode == SEER_SELECT_THRESHOLD) {
+    if (!(rule->threshold == rule->threshold) || isinf(rule->threshold))
+      return fail(SEER_ERR_INVALID_ARG, "threshold is not finite");
+  } else if (!rule->top_k) {
+    const int32_t kk = seer_keep_blocks(shape->max_blocks, rule->keep_num, rule->keep_den);
     if (kk < 0)
       return fail(SEER_ERR_INVALID_ARG, "keep rule %d/%d invalid (need 1 <= num <= den)",
-                  keep_num, keep_den);
+                  rule->keep_num, rule->keep_den);
     if (kk > k_max)
       return fail(SEER_ERR_INVALID_ARG, "keep rule keeps %d of max_blocks=%d blocks > k_max=%d",
                   kk, shape->max_blocks, k_max);
@@ -222,20 +226,19 @@ seer_status seer_block_pool_keys(const seer_shape* shape, const seer_kv* kv,
   return ok();
 }
 
-seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const float* pooled,
-                                  const int32_t* lens, const int32_t* top_k, int32_t keep_num,
-                                  int32_t keep_den, int32_t k_max, double* scores,
-                                  int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
-  const seer_status st = check_gate(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max,
-                                    scores, sel_idx, sel_cnt);
+seer_status seer_gate_select(const seer_shape* shape, const void* q, const float* pooled,
+                             const int32_t* lens, const seer_select* rule, int32_t k_max,
+                             double* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                             hipStream_t stream) {
+  const seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (st) return st;
   seer::GateArgs a{};
   a.q = q;
   a.pooled = pooled;
   a.lens = lens;
-  a.top_k = top_k;
-  a.keep_num = keep_num;
-  a.keep_den = keep_den;
+  a.top_k = rule->top_k;
+  a.keep_num = rule->keep_num;
+  a.keep_den = rule->keep_den;
   a.k_max = k_max;
   a.B = shape->batch;
   a.Hq = shape->num_q_heads;
@@ -247,9 +250,28 @@ seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const 
   a.scores = scores;
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
+  a.threshold_mode = rule->mode == SEER_SELECT_THRESHOLD;
+  a.threshold = rule->threshold;
+  a.force_first = rule->force_first != 0;
+  a.force_last = rule->force_last != 0;
+  a.unified = rule->unified != 0;
+  if (seer::gate_smem_bytes(a.NB, k_max) > max_block_smem())
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
   const hipError_t e = seer::launch_gate_topk(a, stream);
   if (e != hipSuccess) return hip_fail(e, "gate_topk launch");
   return ok();
+}
+
+seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const float* pooled,
+                                  const int32_t* lens, const int32_t* top_k, int32_t keep_num,
+                                  int32_t keep_den, int32_t k_max, double* scores,
+                                  int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
+  seer_select rule{};
+  rule.mode = SEER_SELECT_TOPK;
+  rule.top_k = top_k;
+  rule.keep_num = keep_num;
+  rule.keep_den = keep_den;
+  return seer_gate_select(shape, q, pooled, lens, &rule, k_max, scores, sel_idx, sel_cnt, stream);
 }
 
 seer_status seer_sparse_decode_workspace_size(const seer_shape* shape, size_t* bytes) {
@@ -280,14 +302,12 @@ seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, c
 
 seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void* q,
                                              const seer_kv* kv, const int32_t* lens,
-                                             const float* pooled, const int32_t* top_k,
-                                             int32_t keep_num, int32_t keep_den, int32_t k_max,
-                                             float softmax_scale, double* scores,
+                                             const float* pooled, const seer_select* rule,
+                                             int32_t k_max, float softmax_scale, double* scores,
                                              int32_t* sel_idx, int32_t* sel_cnt,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream) {
-  seer_status st = check_gate(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max, scores,
-                              sel_idx, sel_cnt);
+  seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (st) return st;
   seer::DecodeArgs a;
   if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
@@ -296,13 +316,18 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
   const int U = shape->batch * shape->num_kv_heads;
   const int ids_cap = seer::gated_decode_ids_cap(U, k_max, a.W);
   const size_t smem = seer::gated_decode_smem_bytes(U, shape->max_blocks, ids_cap);
-  if (smem <= max_block_smem()) {
+  // The fused kernel selects by top-k per unit (forced blocks included); a
+  // threshold or a unified selection runs the gate kernel first.
+  const bool fusable = rule->mode == SEER_SELECT_TOPK && !rule->unified;
+  if (fusable && smem <= max_block_smem()) {
     a.sel_idx = nullptr;
     a.sel_cnt = nullptr;
     a.pooled = pooled;
-    a.top_k = top_k;
-    a.keep_num = keep_num;
-    a.keep_den = keep_den;
+    a.top_k = rule->top_k;
+    a.keep_num = rule->keep_num;
+    a.keep_den = rule->keep_den;
+    a.force_first = rule->force_first != 0;
+    a.force_last = rule->force_last != 0;
     a.scores = scores;
     a.sel_idx_out = sel_idx;
     a.sel_cnt_out = sel_cnt;
@@ -310,10 +335,10 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
     const hipError_t e = seer::launch_gated_decode_partial(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
   } else {
-    // The selections of one workgroup's units do not fit in its LDS: the gate
-    // kernel, then the partial kernel on its selection (same results).
-    if ((st = seer_gate_scores_topk(shape, q, pooled, lens, top_k, keep_num, keep_den, k_max,
-                                    scores, sel_idx, sel_cnt, stream)))
+    // The gate kernel, then the partial kernel on its selection (the same
+    // results as the fused kernel where both apply).
+    if ((st = seer_gate_select(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt,
+                               stream)))
       return st;
     const hipError_t e = seer::launch_decode_partial(a, stream);
     if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
@@ -323,15 +348,15 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
 
 seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                                      const int32_t* lens, const float* pooled,
-                                     const int32_t* top_k, int32_t keep_num, int32_t keep_den,
-                                     int32_t k_max, float softmax_scale, double* scores,
+                                     const seer_select* rule, int32_t k_max,
+                                     float softmax_scale, double* scores,
                                      int32_t* sel_idx, int32_t* sel_cnt, float* out, float* lse,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
   if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
   const seer_status st = seer_gated_sparse_decode_partial(
-      shape, q, kv, lens, pooled, top_k, keep_num, keep_den, k_max, softmax_scale, scores,
-      sel_idx, sel_cnt, workspace, workspace_bytes, stream);
+      shape, q, kv, lens, pooled, rule, k_max, softmax_scale, scores, sel_idx, sel_cnt,
+      workspace, workspace_bytes, stream);
   if (st) return st;
   return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
 }

@@ -45,6 +45,7 @@ struct DecodeArgs {
   int32_t* sel_idx_out;   // [B][Hkv][k_max] out
   int32_t* sel_cnt_out;   // [B][Hkv] out
   int32_t ids_cap;        // kept ids one workgroup holds in LDS
+  int32_t force_first, force_last;  // forced blocks of the fused gate's top-k
 };
 
 struct CombineArgs {
@@ -84,9 +85,16 @@ struct GateArgs {
   double* scores;
   int32_t* sel_idx;
   int32_t* sel_cnt;
+  int32_t threshold_mode;  // keep the blocks scoring above `threshold` (else top-k)
+  double threshold;
+  int32_t force_first;     // keep block 0 whatever its score
+  int32_t force_last;      // keep the newest block whatever its score
+  int32_t unified;         // one selection per sequence from the KV heads' summed scores
 };
 
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream);
+// Dynamic LDS of the gate kernel.
+size_t gate_smem_bytes(int NB, int k_max);
 
 // ---------------------------------------------------------------- pooling
 

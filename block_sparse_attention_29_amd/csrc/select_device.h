@@ -33,6 +33,26 @@ __device__ __forceinline__ int kept_count(int n, const int32_t* top_k, int b, in
   return k > k_max ? k_max : k;
 }
 
+// Blocks kept whatever their score: block 0 and/or the newest block n-1.
+__device__ __forceinline__ int forced_count(int n, int force_first, int force_last) {
+  if (n <= 0) return 0;
+  return (force_first ? 1 : 0) + ((force_last && !(force_first && n == 1)) ? 1 : 0);
+}
+
+// Top-k count of a unit with n blocks once nf forced blocks are counted in:
+// at least nf, at most min(n, k_max), at least 1 (0 when n == 0).
+__device__ __forceinline__ int kept_count_forced(int n, const int32_t* top_k, int b, int keep_num,
+                                                 int keep_den, int k_max, int nf) {
+  if (n <= 0) return 0;
+  int k = kept_count(n, top_k, b, keep_num, keep_den, k_max);
+  k = k < nf ? nf : k;
+  const int cap = n < k_max ? n : k_max;
+  return k > cap ? cap : k;
+}
+
+// Key that ranks a forced block above every score.
+constexpr uint64_t kForcedKey = ~0ull;
+
 // Writes the ids of the k largest keys of s_key[0..n) (ties to the lower id),
 // ascending, to out[0..k).  Requires 0 < k < n and NT >= 256; every thread of
 // the workgroup calls it (it contains __syncthreads()).  Scratch in LDS:

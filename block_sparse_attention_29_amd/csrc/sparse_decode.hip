@@ -77,8 +77,9 @@ __device__ __forceinline__ int tile_owner(int64_t y, int W, int64_t Tot) {
 template <bool GATED>
 __device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int u, int L) {
   if constexpr (GATED) {
-    return kept_count(seq_blocks(L, a.S, a.NB), a.top_k, u / a.Hkv, a.keep_num, a.keep_den,
-                      a.k_max);
+    const int n = seq_blocks(L, a.S, a.NB);
+    return kept_count_forced(n, a.top_k, u / a.Hkv, a.keep_num, a.keep_den, a.k_max,
+                             forced_count(n, a.force_first, a.force_last));
   }
   if (a.sel_idx) {
     const int c = a.sel_cnt[u];
@@ -183,10 +184,23 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   if (NB % 4 == 0) fused_scores<T, D, G, 4>(a, b, g, pu, n, s_q, s_part, s_key);
   else if (NB % 2 == 0) fused_scores<T, D, G, 2>(a, b, g, pu, n, s_q, s_part, s_key);
   else fused_scores<T, D, G, 1>(a, b, g, pu, n, s_q, s_part, s_key);
+  // forced blocks rank above every score while the selection runs
+  const uint64_t key_first = s_key[0], key_last = s_key[n - 1];
+  __syncthreads();
+  if (tid == 0) {
+    if (a.force_first) s_key[0] = kForcedKey;
+    if (a.force_last) s_key[n - 1] = kForcedKey;
+  }
+  __syncthreads();
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
   } else {
     block_topk_ids<kThreads>(s_key, n, k, s_hist, s_pick, s_scan, dst);
+  }
+  __syncthreads();
+  if (tid == 0) {  // the forced blocks' own scores go out
+    s_key[0] = key_first;
+    s_key[n - 1] = key_last;
   }
   __syncthreads();
   if (owner) {

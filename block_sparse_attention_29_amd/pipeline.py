@@ -28,16 +28,21 @@ class DecodeState:
                  block_size: int, max_blocks: int, dtype: torch.dtype, k: torch.Tensor,
                  v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
                  k_max: Optional[int] = None, keep: Optional[tuple] = None,
-                 top_k: Optional[torch.Tensor] = None):
+                 top_k: Optional[torch.Tensor] = None, threshold: Optional[float] = None,
+                 force_first: bool = False, force_last: bool = False, unified: bool = False):
         self.shape = seer.make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks, dtype)
         self.k, self.v, self.page_table = k, v, page_table
         self.kv = seer.make_kv(k, v, page_table)
         self.keep = keep
         self.top_k = top_k
+        self.rule = seer.make_select(top_k=top_k, keep=keep, threshold=threshold,
+                                     force_first=force_first, force_last=force_last,
+                                     unified=unified)
         if k_max is None:
-            if keep is not None:
+            if keep is not None and threshold is None:
                 k_max = seer.keep_blocks(max_blocks, keep[0], keep[1])
+                k_max = min(max_blocks, k_max + int(force_first) + int(force_last))
             else:
                 k_max = max_blocks
         self.k_max = int(k_max)
@@ -61,9 +66,8 @@ class DecodeState:
 
     # selection -------------------------------------------------------------
     def select(self, q: torch.Tensor, lens: torch.Tensor):
-        num, den = self.keep if self.keep is not None else (1, 1)
-        seer.gate_scores_topk(self.shape, q, self.pooled, lens, self.top_k, num, den, self.k_max,
-                              self.scores, self.sel_idx, self.sel_cnt)
+        seer.gate_select(self.shape, q, self.pooled, lens, self.rule, self.k_max, self.scores,
+                         self.sel_idx, self.sel_cnt)
 
     # attention -------------------------------------------------------------
     def attend(self, q: torch.Tensor, lens: torch.Tensor, dense: bool = False,
@@ -82,8 +86,7 @@ class DecodeState:
     def step(self, q: torch.Tensor, lens: torch.Tensor):
         """Gate, select and attend: one decode step over a built pooled table
         (the gate fused into the attention kernel)."""
-        num, den = self.keep if self.keep is not None else (1, 1)
-        seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.top_k, num, den,
+        seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,
                                  self.lse, self.workspace)
         return self.out, self.lse

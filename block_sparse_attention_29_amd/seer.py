@@ -30,6 +30,7 @@ SEER_BF16 = 1
 EXPORTS = (
     "seer_block_pool_keys",
     "seer_gate_scores_topk",
+    "seer_gate_select",
     "seer_sparse_decode_workspace_size",
     "seer_sparse_decode",
     "seer_sparse_decode_partial",
@@ -40,6 +41,32 @@ EXPORTS = (
     "seer_status_str",
     "seer_last_error",
 )
+
+
+SEER_SELECT_TOPK, SEER_SELECT_THRESHOLD = 0, 1
+
+
+class Select(ctypes.Structure):
+    """seer_select: the selection rule (include/seer.h)."""
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("top_k", ctypes.c_void_p),
+        ("keep_num", ctypes.c_int32),
+        ("keep_den", ctypes.c_int32),
+        ("threshold", ctypes.c_double),
+        ("force_first", ctypes.c_int32),
+        ("force_last", ctypes.c_int32),
+        ("unified", ctypes.c_int32),
+    ]
+
+
+def make_select(*, top_k: Optional[torch.Tensor] = None, keep=None, threshold=None,
+                force_first=False, force_last=False, unified=False) -> Select:
+    num, den = keep if keep is not None else (1, 1)
+    mode = SEER_SELECT_THRESHOLD if threshold is not None else SEER_SELECT_TOPK
+    return Select(mode, None if top_k is None else top_k.data_ptr(), num, den,
+                  0.0 if threshold is None else float(threshold), int(force_first),
+                  int(force_last), int(unified))
 
 
 class Shape(ctypes.Structure):
@@ -99,10 +126,11 @@ def load(path: str = LIB_PATH):
     lib.seer_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, _P, _I32, ctypes.c_float, _P,
                                                ctypes.c_size_t, _P]
     lib.seer_sparse_decode_combine.argtypes = [SP, _P, _P, _P, ctypes.c_size_t, _P]
-    lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, _P, _I32, _I32, _I32,
-                                             ctypes.c_float, _P, _P, _P, _P, _P, _P,
-                                             ctypes.c_size_t, _P]
-    lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, _P, _I32, _I32, _I32,
+    RP = ctypes.POINTER(Select)
+    lib.seer_gate_select.argtypes = [SP, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
+    lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, RP, _I32, ctypes.c_float, _P,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
                                                      ctypes.c_float, _P, _P, _P, _P,
                                                      ctypes.c_size_t, _P]
     lib.seer_keep_blocks.argtypes = [_I32, _I32, _I32]
@@ -111,7 +139,7 @@ def load(path: str = LIB_PATH):
     lib.seer_status_str.restype = ctypes.c_char_p
     lib.seer_last_error.argtypes = []
     lib.seer_last_error.restype = ctypes.c_char_p
-    for name in ("seer_block_pool_keys", "seer_gate_scores_topk",
+    for name in ("seer_block_pool_keys", "seer_gate_scores_topk", "seer_gate_select",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
                  "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial"):
@@ -186,6 +214,21 @@ def gate_scores_topk(shape: Shape, q: torch.Tensor, pooled: torch.Tensor, lens: 
                                      _ptr(sel_idx), _ptr(sel_cnt), _stream()))
 
 
+def gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor, lens: torch.Tensor,
+                rule: Select, k_max: int, scores: torch.Tensor, sel_idx: torch.Tensor,
+                sel_cnt: torch.Tensor):
+    lib = load()
+    U = shape.batch * shape.num_kv_heads
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    _check(lib.seer_gate_select(ctypes.byref(shape), _ptr(q), _ptr(pooled), _ptr(lens),
+                                ctypes.byref(rule), k_max, _ptr(scores), _ptr(sel_idx),
+                                _ptr(sel_cnt), _stream()))
+
+
 def sparse_decode_workspace_size(shape: Shape) -> int:
     lib = load()
     n = ctypes.c_size_t(0)
@@ -229,32 +272,30 @@ def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.T
 
 
 def gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
-                        pooled: torch.Tensor, top_k: Optional[torch.Tensor], keep_num: int,
-                        keep_den: int, k_max: int, scores: torch.Tensor, sel_idx: torch.Tensor,
-                        sel_cnt: torch.Tensor, out: Optional[torch.Tensor],
-                        lse: Optional[torch.Tensor], workspace: torch.Tensor,
-                        softmax_scale: float = 0.0):
-    """Gate, top-k and sparse decode in two launches; out=None stops after the
-    first (the partial results stay in the workspace for sparse_decode_combine)."""
+                        pooled: torch.Tensor, rule: Select, k_max: int, scores: torch.Tensor,
+                        sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                        out: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                        workspace: torch.Tensor, softmax_scale: float = 0.0):
+    """Gate, selection and sparse decode in two launches; out=None stops after
+    the first (the partial results stay in the workspace for
+    sparse_decode_combine)."""
     lib = load()
     U = shape.batch * shape.num_kv_heads
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
     _need(lens, torch.int32, shape.batch, "lens")
-    if top_k is not None:
-        _need(top_k, torch.int32, shape.batch, "top_k")
     _need(scores, torch.float64, U * shape.max_blocks, "scores")
     _need(sel_idx, torch.int32, U * k_max, "sel_idx")
     _need(sel_cnt, torch.int32, U, "sel_cnt")
     if out is None:
         _check(lib.seer_gated_sparse_decode_partial(
             ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
-            _ptr(top_k), keep_num, keep_den, k_max, softmax_scale, _ptr(scores), _ptr(sel_idx),
-            _ptr(sel_cnt), _ptr(workspace), workspace.numel(), _stream()))
+            ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+            _ptr(workspace), workspace.numel(), _stream()))
         return
     _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
     if lse is not None:
         _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
     _check(lib.seer_gated_sparse_decode(
-        ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled), _ptr(top_k),
-        keep_num, keep_den, k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+        ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
+        ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))

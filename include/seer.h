@@ -133,6 +133,44 @@ seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const 
                                   int32_t keep_den, int32_t k_max, double* scores,
                                   int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
 
+/* Selection rule of seer_gate_select and seer_gated_sparse_decode.
+ *  mode SEER_SELECT_TOPK: k_b as in seer_gate_scores_topk (top_k[b] when
+ *    top_k != NULL, else the keep fraction keep_num / keep_den).
+ *  mode SEER_SELECT_THRESHOLD: keep the blocks whose score is above
+ *    `threshold` -- the hard gate of "Sparse Attention Reasoning" (Step 1:
+ *    the selection with a temperature keeps sigmoid(s / T) > 0.5, which is
+ *    s > 0 for any T > 0) with a general threshold; at least 1 block (the
+ *    best), at most k_max (the best k_max).
+ *  force_first / force_last: block 0 (an attention sink) and the newest block
+ *    n_b - 1 are kept whatever their score; a top-k count below the number of
+ *    forced blocks is raised to it (still at most min(n_b, k_max)).
+ *  unified: one selection per sequence, from the scores summed over its KV
+ *    heads, s_j = sum_g sum_{h in group g} q_h . P_{g,j} / sqrt(d) (the KV
+ *    heads added in order), copied to every KV head of the sequence (the
+ *    cross-head selection of the LessIsMore abstract on the author page
+ *    "Shijie Cao"); scores[b][g] then holds the summed score for every g.
+ *  The order is score descending, ties to the lower block id, as everywhere. */
+typedef enum seer_select_mode { SEER_SELECT_TOPK = 0, SEER_SELECT_THRESHOLD = 1 } seer_select_mode;
+typedef struct seer_select {
+  int32_t mode;            /* seer_select_mode */
+  const int32_t* top_k;    /* TOPK: device [B] counts, or NULL for the keep fraction */
+  int32_t keep_num;        /* TOPK without top_k: kept fraction keep_num / keep_den */
+  int32_t keep_den;
+  double threshold;        /* THRESHOLD: keep blocks scoring above it (finite) */
+  int32_t force_first;     /* nonzero: keep block 0 */
+  int32_t force_last;      /* nonzero: keep block n_b - 1 */
+  int32_t unified;         /* nonzero: one selection per sequence over its KV heads */
+} seer_select;
+
+/* seer_gate_select -- seer_gate_scores_topk under a general rule (above);
+ * same arguments otherwise.  seer_gate_scores_topk(top_k, keep_num, keep_den)
+ * is this call with {SEER_SELECT_TOPK, top_k, keep_num, keep_den}.
+ * SEER_ERR_UNSUPPORTED when max_blocks needs more LDS than one workgroup has. */
+seer_status seer_gate_select(const seer_shape* shape, const void* q, const float* pooled,
+                             const int32_t* lens, const seer_select* rule, int32_t k_max,
+                             double* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                             hipStream_t stream);
+
 /* Bytes of workspace seer_sparse_decode needs for this shape on the current
  * device (it depends on the device's compute-unit count). */
 seer_status seer_sparse_decode_workspace_size(const seer_shape* shape, size_t* bytes);
@@ -183,25 +221,25 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
  * for a separate gate launch ("SeerAttention-R: Sparse Attention Adaptation
  * for Long Reasoning", Abstract: gating on pooled keys with a sparse decoding
  * kernel; "Sparse Attention Reasoning", Step 1 and Step 4).
- *  Arguments: as seer_gate_scores_topk (q, pooled, lens, top_k / keep rule,
- *  k_max, scores, sel_idx, sel_cnt, all outputs written) and
- *  seer_sparse_decode (kv, softmax_scale, out, lse, workspace).
- *  When one workgroup's selections would not fit in its LDS the call runs
- *  the gate kernel first instead (same results).
+ *  Arguments: as seer_gate_select (q, pooled, lens, rule, k_max, scores,
+ *  sel_idx, sel_cnt, all outputs written) and seer_sparse_decode (kv,
+ *  softmax_scale, out, lse, workspace).
+ *  The selection is fused for top-k rules (forced blocks included); for a
+ *  threshold or unified rule, or when one workgroup's selections would not
+ *  fit in its LDS, the call runs the gate kernel first instead (same
+ *  results).
  * _partial: the first launch alone (gate + partial results in the workspace,
  * selections written); seer_sparse_decode_combine finishes it. */
 seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                                      const int32_t* lens, const float* pooled,
-                                     const int32_t* top_k, int32_t keep_num, int32_t keep_den,
-                                     int32_t k_max, float softmax_scale, double* scores,
-                                     int32_t* sel_idx, int32_t* sel_cnt, float* out, float* lse,
-                                     void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream);
+                                     const seer_select* rule, int32_t k_max,
+                                     float softmax_scale, double* scores, int32_t* sel_idx,
+                                     int32_t* sel_cnt, float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
 seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void* q,
                                              const seer_kv* kv, const int32_t* lens,
-                                             const float* pooled, const int32_t* top_k,
-                                             int32_t keep_num, int32_t keep_den, int32_t k_max,
-                                             float softmax_scale, double* scores,
+                                             const float* pooled, const seer_select* rule,
+                                             int32_t k_max, float softmax_scale, double* scores,
                                              int32_t* sel_idx, int32_t* sel_cnt,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream);

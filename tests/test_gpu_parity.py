@@ -437,3 +437,82 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(ref, (st.sel_idx, st.sel_cnt, st.out, st.lse)):
             assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ selection rules
+
+RULES = [
+    ("force_first", dict(force_first=True)),
+    ("force_both", dict(force_first=True, force_last=True)),
+    ("threshold_0", dict(threshold=0.0)),
+    ("threshold_1", dict(threshold=1.0)),
+    ("threshold_forced", dict(threshold=1.5, force_last=True)),
+    ("unified", dict(unified=True)),
+    ("unified_forced", dict(unified=True, force_first=True, force_last=True)),
+    ("unified_threshold", dict(unified=True, threshold=0.0)),
+]
+
+
+@pytest.mark.parametrize("wname", ["planted_b2", "paged_small", "bf16_d64_g8"])
+@pytest.mark.parametrize("rname,rule", RULES, ids=[r[0] for r in RULES])
+def test_selection_rules(wname, rname, rule):
+    """Forced blocks, the threshold gate and the cross-head unified selection:
+    ids and counts bit-exact, scores and outputs against the oracle."""
+    wl = SMALL[wname]
+    print(f"[case] rule {rname} on {wname}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case, **rule)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    S, d, G, Hkv = wl.block_size, wl.head_dim, wl.group, wl.num_kv_heads
+    lens = case.lens.tolist()
+    for b in range(wl.batch):
+        L = lens[b]
+        n = O.block_count(L, S)
+        kv = [unit_kv(case, b, g, L) for g in range(Hkv)]
+        pooled = [O.pool_keys(k, L, S)[0] for k, _ in kv]
+        qb = f64(case.q[b])
+        if rule.get("unified"):
+            s_all = [O.gate_scores_unified(qb, pooled, d)] * Hkv
+        else:
+            s_all = [O.gate_scores(qb[g * G:(g + 1) * G], pooled[g], d) for g in range(Hkv)]
+        for g in range(Hkv):
+            u = b * Hkv + g
+            s = s_all[g]
+            if "threshold" in rule:
+                sel = O.select_blocks(s, threshold=rule["threshold"],
+                                      force_first=rule.get("force_first", False),
+                                      force_last=rule.get("force_last", False), k_max=st.k_max)
+            else:
+                k = (O.clamp_count(wl.top_k, n) if wl.top_k is not None
+                     else O.keep_count(n, *wl.keep))
+                sel = O.select_blocks(s, k=k, force_first=rule.get("force_first", False),
+                                      force_last=rule.get("force_last", False), k_max=st.k_max)
+            cnt = int(st.sel_cnt[u])
+            ids = st.sel_idx[u].cpu().numpy()
+            assert cnt == len(sel), f"{rname} count {b},{g}"
+            assert np.array_equal(ids[:cnt], sel), f"{rname} ids {b},{g}"
+            assert (ids[cnt:] == -1).all()
+            got_s = st.scores.view(-1, wl.max_blocks)[u, :n].cpu().numpy()
+            assert np.abs(got_s - s).max() <= 1e-12 * max(np.abs(s).max(), 1e-300)
+            toks = O.selected_tokens(sel, L, S)
+            out = st.out[b, g * G:(g + 1) * G].cpu().double().numpy()
+            for h in range(G):
+                o, lse, _ = O.attend(qb[g * G + h], kv[g][0], kv[g][1], toks)
+                assert np.abs(out[h] - o).max() <= TOL[wl.dtype], f"{rname} out {b},{g},{h}"
+
+
+@pytest.mark.parametrize("rule", [dict(force_first=True), dict(force_first=True, force_last=True)],
+                         ids=["first", "both"])
+def test_fused_forced_blocks_equal_separate_calls(rule):
+    wl = SMALL["paged_small"]
+    case = make_case(wl, "cuda")
+    fused, sep = state_for(case, **rule), state_for(case, **rule)
+    for st in (fused, sep):
+        st.build_pool(case.lens)
+    fused.step(case.q, case.lens)
+    sep.step_unfused(case.q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
