@@ -57,8 +57,7 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
   extern __shared__ uint64_t s_key[];  // [NB] keys (unified: fp64 sums first), then [k_max] ids
   __shared__ double s_q[D];
   __shared__ double s_part[4][256];
-  __shared__ int s_hist[2][256];
-  __shared__ int s_pick[3];
+  __shared__ int s_hist[3][256];
   __shared__ int s_scan[kTopkThreads / 64 + 1];
 
   const int tid = threadIdx.x;
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
   if (k >= n) {
     for (int j = tid; j < n; j += kTopkThreads) dst[j] = j;
   } else {
-    block_topk_ids<kTopkThreads>(s_key, n, k, &s_hist[0][0], s_pick, s_scan, dst);
+    block_topk_ids<kTopkThreads>(s_key, n, k, &s_hist[0][0], s_scan, dst);
   }
   if (nf > 0 || UNIFIED) __syncthreads();
   if (nf > 0) {

@@ -118,6 +118,30 @@ __device__ __forceinline__ int block_excl_scan(int x, int* scratch, int* total) 
   return base + inc - x;
 }
 
+// ---------------------------------------------------------------- division
+
+// floor(x / d) for 0 <= x < 2^52 and 0 < d < 2^31.  The fp64 quotient is off
+// by less than one there, so one integer step either way makes it exact; far
+// shorter than the generic 64-bit integer division.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d) {
+  int64_t q = (int64_t)((double)x / (double)d);
+  const int64_t r = x - q * d;
+  q += (r < 0) ? -1 : (r >= d ? 1 : 0);
+  return q;
+}
+
+// Equal split of `total` items over `parts` parts: part w starts at
+// floor(w * total / parts).  With total = q * parts + r that is
+// w * q + floor(w * r / parts), in 32-bit arithmetic for parts < 46341.
+struct EqualSplit {
+  int q, r, parts;
+  __device__ __forceinline__ EqualSplit(int total, int parts_)
+      : q(total / parts_), r(total - (total / parts_) * parts_), parts(parts_) {}
+  __device__ __forceinline__ int start(int w) const {
+    return w * q + (int)((uint32_t)(w * r) / (uint32_t)parts);
+  }
+};
+
 // ---------------------------------------------------------------- fp64 order key
 
 // Order-preserving map of a finite double to uint64 (larger value -> larger

@@ -19,6 +19,9 @@ constexpr int kDecodeWavesPerWG = 4;
 
 // Largest number of (sequence, KV head) units a call may have.
 constexpr int kMaxUnits = 8192;
+// Most waves one partial launch uses (the equal tile split does its
+// arithmetic in 32 bits up to 46340 waves).
+constexpr int kMaxWaves = 32768;
 
 struct DecodeArgs {
   const void* q;

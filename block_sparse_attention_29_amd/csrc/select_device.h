@@ -20,15 +20,17 @@ namespace seer {
 // Blocks a sequence of L tokens occupies, at most NB.
 __device__ __forceinline__ int seq_blocks(int L, int S, int NB) {
   if (L <= 0) return 0;
-  const int n = (int)(((int64_t)L + S - 1) / S);
+  const int n = (L - 1) / S + 1;
   return n > NB ? NB : n;
 }
 
 // Kept blocks of a unit with n blocks (0 when n == 0), at most k_max.
+// (n < 2^14 and keep_num <= keep_den < 2^31, so the product is below 2^52.)
 __device__ __forceinline__ int kept_count(int n, const int32_t* top_k, int b, int keep_num,
                                           int keep_den, int k_max) {
   if (n <= 0) return 0;
-  int k = top_k ? top_k[b] : (int)(((int64_t)n * keep_num + keep_den - 1) / keep_den);
+  int k = top_k ? top_k[b]
+                : (int)div_floor((int64_t)n * keep_num + keep_den - 1, keep_den);
   k = k < 1 ? 1 : (k > n ? n : k);
   return k > k_max ? k_max : k;
 }
@@ -56,66 +58,109 @@ constexpr uint64_t kForcedKey = ~0ull;
 // Writes the ids of the k largest keys of s_key[0..n) (ties to the lower id),
 // ascending, to out[0..k).  Requires 0 < k < n and NT >= 256; every thread of
 // the workgroup calls it (it contains __syncthreads()).  Scratch in LDS:
-// s_hist [2 * 256], s_pick [3], s_scan [NT / 64 + 1].
+// s_hist [3 * 256], s_scan [NT / 64 + 1].
 //
-// Exact radix select over the 64-bit keys, 8 bits per pass from the top.
-// Thread t owns the contiguous ids [t*m, t*m + m).  Each pass histograms the
-// next 8 bits of the candidates' keys (double-buffered histogram, the next one
-// cleared during the current pass); wave 0 scans the 256 bins from the top
-// with DPP and publishes the digit that holds the krem-th largest key.  After
-// a pass only the keys matching the chosen prefix remain candidates; once all
-// of them are needed (or all 64 bits are used) the kept set is every key with a
-// larger prefix plus the first krem keys equal to it in id order.  Random
-// scores usually settle after 3 passes.  One block scan of packed (above,
-// equal) counts then gives every thread the output slots of its ids.
+// Exact radix select over the 64-bit keys.  Thread t owns the contiguous ids
+// [t*m, t*m + m).  A block-wide AND and OR of the keys give the bits every key
+// shares; the first digit is the 8 bits from the highest bit where keys
+// differ, each later digit the next 8 bits down.  Each pass histograms the
+// digit of the keys still matching the chosen prefix, and every wave scans
+// the 256 bins from the top (DPP) to find the digit that holds the krem-th
+// largest key, so one barrier per pass suffices: the histograms rotate over
+// three buffers, the one cleared during a pass last read two passes before.
+// Once every remaining candidate is needed (or all bits are used) the kept set
+// is every key with a larger prefix plus the first krem keys equal to it in id
+// order.  One block scan of packed (above, equal) counts then gives every
+// thread the output slots of its ids.
 template <int NT>
-__device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int* s_pick,
-                               int* s_scan, int32_t* out) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int* s_scan,
+                               int32_t* out) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = (n + NT - 1) / NT;
   const int lo = min(n, tid * m), hi = min(n, lo + m);
-  uint64_t prefix = 0, mask = 0;
-  int krem = k;
+
+  // ---- bits shared by every key: block AND / OR (partials in buffer 2) ----
+  uint64_t kand = ~0ull, kor = 0;
+  for (int j = lo; j < hi; ++j) {
+    const uint64_t key = s_key[j];
+    kand &= key;
+    kor |= key;
+  }
+  uint32_t r4[4] = {(uint32_t)kand, (uint32_t)(kand >> 32), (uint32_t)kor, (uint32_t)(kor >> 32)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t x = r4[i];
+    const bool isand = i < 2;
+    uint32_t y;
+    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xF, 0xF, true);
+    x = isand ? (x & y) : (x | y);
+    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xF, 0xF, true);
+    x = isand ? (x & y) : (x | y);
+    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xF, 0xF, true);
+    x = isand ? (x & y) : (x | y);
+    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xF, 0xF, true);
+    x = isand ? (x & y) : (x | y);
+    const uint32_t a0 = (uint32_t)readlane_i((int)x, 0), a1 = (uint32_t)readlane_i((int)x, 16);
+    const uint32_t a2 = (uint32_t)readlane_i((int)x, 32), a3 = (uint32_t)readlane_i((int)x, 48);
+    r4[i] = isand ? (a0 & a1 & a2 & a3) : (a0 | a1 | a2 | a3);
+  }
+  int* s_red = s_hist + 2 * 256;
+  if (lane < 4)
+    s_red[wv * 4 + lane] = (int)(lane == 0 ? r4[0] : lane == 1 ? r4[1] : lane == 2 ? r4[2] : r4[3]);
   if (tid < 256) s_hist[tid] = 0;
   __syncthreads();
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    int* hist = s_hist + (pass & 1) * 256;
+  uint32_t t4[4] = {~0u, ~0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    t4[0] &= (uint32_t)s_red[i * 4 + 0];
+    t4[1] &= (uint32_t)s_red[i * 4 + 1];
+    t4[2] |= (uint32_t)s_red[i * 4 + 2];
+    t4[3] |= (uint32_t)s_red[i * 4 + 3];
+  }
+  kand = ((uint64_t)t4[1] << 32) | t4[0];
+  kor = ((uint64_t)t4[3] << 32) | t4[2];
+  const uint64_t diff = kand ^ kor;
+
+  int top = diff ? 63 - __builtin_clzll(diff) : -1;  // highest bit where keys differ
+  uint64_t mask = top >= 63 ? 0ull : (~0ull << (top + 1));
+  uint64_t prefix = kand & mask;
+  int krem = k;
+  int slot = 0, nxt = 1;
+  while (top >= 0) {
+    const int shift = top > 7 ? top - 7 : 0;
+    int* hist = s_hist + slot * 256;
     for (int j = lo; j < hi; ++j) {
       const uint64_t key = s_key[j];
       if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
     }
-    if (tid < 256) s_hist[((pass & 1) ^ 1) * 256 + tid] = 0;
+    if (tid < 256) s_hist[nxt * 256 + tid] = 0;
     __syncthreads();
-    if (tid < 64) {
-      // lane l holds digits 255-4l .. 252-4l (descending)
-      int c[4], sum = 0;
+    // every wave: lane l holds digits 255-4l .. 252-4l (descending)
+    int c[4], sum = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * lane - r]; sum += c[r]; }
-      int larger = wave_incl_scan(sum) - sum;  // keys with a larger digit than this lane's first
-      int pick = -1, nk = 0, pc = 0;
+    for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * lane - r]; sum += c[r]; }
+    int larger = wave_incl_scan(sum) - sum;  // keys with a larger digit than this lane's first
+    int pick = -1, nk = 0, pc = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (larger < krem && krem <= larger + c[r]) {
-          pick = 255 - 4 * lane - r;
-          nk = krem - larger;
-          pc = c[r];
-        }
-        larger += c[r];
+    for (int r = 0; r < 4; ++r) {
+      if (larger < krem && krem <= larger + c[r]) {
+        pick = 255 - 4 * lane - r;
+        nk = krem - larger;
+        pc = c[r];
       }
-      // exactly one lane picked: it publishes its digit, new krem and count
-      if (pick >= 0) {
-        s_pick[0] = pick;
-        s_pick[1] = nk;
-        s_pick[2] = pc;
-      }
+      larger += c[r];
     }
-    __syncthreads();
-    const int dv = s_pick[0], cnt = s_pick[2];
-    krem = s_pick[1];
+    // exactly one lane picked
+    const int src = __builtin_ctzll(__ballot(pick >= 0));
+    const int dv = readlane_i(pick, src), cnt = readlane_i(pc, src);
+    krem = readlane_i(nk, src);
     prefix |= (uint64_t)dv << shift;
     mask |= (uint64_t)255 << shift;
     if (cnt == krem) break;  // every remaining candidate is kept
+    top = shift - 1;
+    slot = nxt;
+    nxt = nxt == 2 ? 0 : nxt + 1;
   }
 
   int gt = 0, eq = 0;

@@ -66,9 +66,10 @@ __device__ __forceinline__ int64_t readlane64(int64_t x, int lane) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
-// Wave owning tile y when Tot tiles are split over W waves in equal ranges.
+// Wave owning tile y when Tot tiles are split over W waves in equal ranges:
+// the largest w with floor(w Tot / W) <= y.
 __device__ __forceinline__ int tile_owner(int64_t y, int W, int64_t Tot) {
-  return (int)(((y + 1) * W - 1) / Tot);
+  return (int)div_floor((y + 1) * W - 1, Tot);
 }
 
 // Blocks a unit contributes: its kept count (given, or from the keep rule when
@@ -175,7 +176,7 @@ template <typename T, int D, int G>
 __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
                                                 int32_t* dst,
                                                 bool owner, uint64_t* s_key, double* s_q,
-                                                double* s_part, int* s_hist, int* s_pick,
+                                                double* s_part, int* s_hist,
                                                 int* s_scan) {
   const int tid = threadIdx.x;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
@@ -185,24 +186,31 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   else if (NB % 2 == 0) fused_scores<T, D, G, 2>(a, b, g, pu, n, s_q, s_part, s_key);
   else fused_scores<T, D, G, 1>(a, b, g, pu, n, s_q, s_part, s_key);
   // forced blocks rank above every score while the selection runs
-  const uint64_t key_first = s_key[0], key_last = s_key[n - 1];
-  __syncthreads();
-  if (tid == 0) {
-    if (a.force_first) s_key[0] = kForcedKey;
-    if (a.force_last) s_key[n - 1] = kForcedKey;
+  const bool forced = a.force_first || a.force_last;  // uniform
+  uint64_t key_first = 0, key_last = 0;
+  if (forced) {
+    key_first = s_key[0];
+    key_last = s_key[n - 1];
+    __syncthreads();
+    if (tid == 0) {
+      if (a.force_first) s_key[0] = kForcedKey;
+      if (a.force_last) s_key[n - 1] = kForcedKey;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
   } else {
-    block_topk_ids<kThreads>(s_key, n, k, s_hist, s_pick, s_scan, dst);
+    block_topk_ids<kThreads>(s_key, n, k, s_hist, s_scan, dst);
   }
   __syncthreads();
-  if (tid == 0) {  // the forced blocks' own scores go out
-    s_key[0] = key_first;
-    s_key[n - 1] = key_last;
+  if (forced) {
+    if (tid == 0) {  // the forced blocks' own scores go out
+      s_key[0] = key_first;
+      s_key[n - 1] = key_last;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (owner) {
     int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
     for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
@@ -274,6 +282,7 @@ void decode_partial_kernel(DecodeArgs a) {
   // Tile coordinates fit in 32 bits: units * blocks * tiles per block < 2^31.
   const int tsh = 31 - __builtin_clz(a.S / kTile);  // log2(tiles per block)
   const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
+  const EqualSplit split(Tot, a.W);  // wave w's tiles: [split.start(w), split.start(w + 1))
 
   // ---- units holding the first tile of each wave of this workgroup and the
   // workgroup's last tile, looked up by all threads at once (one pass over
@@ -283,8 +292,8 @@ void decode_partial_kernel(DecodeArgs a) {
   {
     int xq[kWavesPerWG + 1];  // block index of each query tile
 #pragma unroll
-    for (int v = 0; v < kWavesPerWG; ++v) xq[v] = (int)((int64_t)(wg0 + v) * Tot / a.W) >> tsh;
-    xq[kWavesPerWG] = ((int)((int64_t)(wg0 + kWavesPerWG) * Tot / a.W) - 1) >> tsh;
+    for (int v = 0; v < kWavesPerWG; ++v) xq[v] = split.start(wg0 + v) >> tsh;
+    xq[kWavesPerWG] = (split.start(wg0 + kWavesPerWG) - 1) >> tsh;
     for (int uu = tid; uu < U; uu += kThreads) {
       const int lo = s_prefix[uu], hi = s_prefix[uu + 1];
 #pragma unroll
@@ -302,12 +311,11 @@ void decode_partial_kernel(DecodeArgs a) {
   if constexpr (GATED) {
     __shared__ double s_q[D];
     __shared__ double s_part[4 * 256];  // quarter sums of one pass (4 x 64*VEC)
-    __shared__ int s_hist[512];
-    __shared__ int s_pick[3];
+    __shared__ int s_hist[3 * 256];
     __shared__ int s_sel_scan[kWavesPerWG + 1];
     uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
-    const int Y0 = (int)((int64_t)wg0 * Tot / a.W);
-    const int Y1 = (int)((int64_t)(wg0 + kWavesPerWG) * Tot / a.W);
+    const int Y0 = split.start(wg0);
+    const int Y1 = split.start(wg0 + kWavesPerWG);
     if (Y0 < Y1) {
       const int u0 = s_unit[0], u1 = s_unit[kWavesPerWG];
       ids_base = s_prefix[u0];
@@ -319,7 +327,7 @@ void decode_partial_kernel(DecodeArgs a) {
         fused_gate_unit<T, D, G>(a, u, seq_blocks(s_len[u], a.S, a.NB), k,
                                  s_ids + (s_prefix[u] - ids_base),
                                  owner == wg, s_key, s_q, s_part, s_hist,
-                                 s_pick, s_sel_scan);
+                                 s_sel_scan);
       }
     }
     // Units without a kept block (a sequence of length 0) belong to nobody:
@@ -332,8 +340,8 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
   }
-  const int y0 = (int)((int64_t)w * Tot / a.W);
-  const int y1 = (int)((int64_t)(w + 1) * Tot / a.W);
+  const int y0 = split.start(w);
+  const int y1 = split.start(w + 1);
   if (y0 >= y1) return;
 
   const bool sparse = a.sel_idx != nullptr;
@@ -608,9 +616,9 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Whether wave w of W owns no tile when Tot tiles are split in equal ranges.
-__device__ __forceinline__ bool wave_empty(int64_t w, int W, int64_t Tot) {
-  return w * Tot / W == (w + 1) * Tot / W;
+// Whether wave w owns no tile under the equal split.
+__device__ __forceinline__ bool wave_empty(const EqualSplit& sp, int w) {
+  return sp.start(w) == sp.start(w + 1);
 }
 
 // Merges the partial records of one unit per workgroup, in wave order.
@@ -637,7 +645,7 @@ constexpr int kCombineFast = 32;    // units with at most this many records: one
 // in record order, so the only dependency chain is the fma chain.
 template <int D, int G, int NWB>
 __device__ __forceinline__ void combine_shot(const CombineArgs& a, const float* part, int nw,
-                                             int wlo, int W, int64_t Tot, int64_t head0) {
+                                             int wlo, int W, int Tot, int64_t head0) {
   constexpr int REC = G * D + 16;
   constexpr int EPT = G * D <= kCombineThreads ? 1 : G * D <= 2 * kCombineThreads ? 2 : 4;
   const int tid = threadIdx.x;
@@ -653,10 +661,11 @@ __device__ __forceinline__ void combine_shot(const CombineArgs& a, const float* 
     lv[t] = r[G * D + 8 + h];
   }
   // Waves are only ever empty when there are fewer tiles than waves; the
-  // 64-bit divisions that tell are kept out of the merge.
+  // divisions that tell are kept out of the merge.
   uint32_t skip = 0;
   if (Tot < W) {
-    for (int t = 0; t < nw; ++t) skip |= wave_empty(wlo + t, W, Tot) ? (1u << t) : 0u;
+    const EqualSplit sp(Tot, W);
+    for (int t = 0; t < nw; ++t) skip |= wave_empty(sp, wlo + t) ? (1u << t) : 0u;
   }
   float M = kNegInf;
 #pragma unroll
@@ -699,8 +708,8 @@ void decode_combine_kernel(CombineArgs a) {
   const int U = a.B * a.Hkv;
   const int tsh = 31 - __builtin_clz(a.S / kTile);
   const int W = a.hdr[0];
-  const int64_t Tot = (int64_t)a.prefix[U] << tsh;
-  const int64_t ylo = (int64_t)a.prefix[u] << tsh, yhi = (int64_t)a.prefix[u + 1] << tsh;
+  const int Tot = a.prefix[U] << tsh;
+  const int ylo = a.prefix[u] << tsh, yhi = a.prefix[u + 1] << tsh;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
   if (yhi <= ylo) {  // no tokens: out = 0, lse = -inf
@@ -708,11 +717,12 @@ void decode_combine_kernel(CombineArgs a) {
     if (a.lse && tid < G) a.lse[head0 + tid] = kNegInf;
     return;
   }
-  const int wlo = (int)(((ylo + 1) * W - 1) / Tot);
-  const int whi = (int)((yhi * W - 1) / Tot);
+  const int wlo = tile_owner(ylo, W, Tot);
+  const int whi = tile_owner(yhi - 1, W, Tot);
   const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
-  auto empty = [&](int t) { return wave_empty(wlo + t, W, Tot); };  // wrote no record
+  const EqualSplit sp(Tot, W);
+  auto empty = [&](int t) { return wave_empty(sp, wlo + t); };  // wrote no record
 
   if (nw <= 8) return combine_shot<D, G, 8>(a, part, nw, wlo, W, Tot, head0);
   if (nw <= 16) return combine_shot<D, G, 16>(a, part, nw, wlo, W, Tot, head0);
@@ -860,7 +870,7 @@ int decode_max_waves(int dtype, int D, int G) {
   const size_t smem = prefix_smem_bytes(kMaxUnits);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, smem) != hipSuccess) return 0;
   if (blocks < 1) return 0;
-  const int waves = cus * kWavesPerWG;
+  const int waves = cus * kWavesPerWG < kMaxWaves ? cus * kWavesPerWG : kMaxWaves;
   if (slot) slot->store(waves, std::memory_order_relaxed);
   return waves;
 }
