@@ -63,9 +63,14 @@ seer_status check_shape(const seer_shape* s) {
   return SEER_OK;
 }
 
+// The kernels move q, k, v, pooled rows and partial records in 16-byte loads.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 seer_status check_kv(const seer_kv* kv) {
   if (!kv) return fail(SEER_ERR_INVALID_ARG, "kv is NULL");
   if (!kv->k || !kv->v) return fail(SEER_ERR_INVALID_ARG, "kv.k or kv.v is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(SEER_ERR_INVALID_ARG, "kv.k and kv.v must be 16-byte aligned");
   if (kv->page_table && kv->num_pages < 1)
     return fail(SEER_ERR_INVALID_ARG, "paged cache with num_pages < 1");
   return SEER_OK;
@@ -84,6 +89,7 @@ seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv
   if (st) return st;
   if ((st = check_kv(kv))) return st;
   if (!q || !lens) return fail(SEER_ERR_INVALID_ARG, "q or lens is NULL");
+  if (!aligned16(q)) return fail(SEER_ERR_INVALID_ARG, "q must be 16-byte aligned");
   if (sel_idx) {
     if (!sel_cnt) return fail(SEER_ERR_INVALID_ARG, "sel_idx given without sel_cnt");
     if (k_max < 1 || k_max > shape->max_blocks)
@@ -93,6 +99,7 @@ seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(SEER_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(SEER_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   const int wmax = wave_cap(shape);
   if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
   const int U = shape->batch * shape->num_kv_heads;
@@ -146,6 +153,8 @@ seer_status check_gate(const seer_shape* shape, const void* q, const float* pool
   if (st) return st;
   if (!q || !pooled || !lens || !rule || !scores || !sel_idx || !sel_cnt)
     return fail(SEER_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(pooled))
+    return fail(SEER_ERR_INVALID_ARG, "q and pooled must be 16-byte aligned");
   if (k_max < 1 || k_max > shape->max_blocks)
     return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks=%d]", k_max,
                 shape->max_blocks);
@@ -207,6 +216,8 @@ seer_status seer_block_pool_keys(const seer_shape* shape, const seer_kv* kv,
   if ((st = check_kv(kv))) return st;
   if (!lens_new) return fail(SEER_ERR_INVALID_ARG, "lens_new is NULL");
   if (!pooled || !open_sum) return fail(SEER_ERR_INVALID_ARG, "pooled or open_sum is NULL");
+  if (!aligned16(pooled) || ((uintptr_t)open_sum & 7) != 0)
+    return fail(SEER_ERR_INVALID_ARG, "pooled must be 16-byte and open_sum 8-byte aligned");
   seer::PoolArgs a{};
   a.k = kv->k;
   a.page_table = kv->page_table;
@@ -368,6 +379,7 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
   if (st) return st;
   if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
   if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(SEER_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   const int wmax = wave_cap(shape);
   if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
   const int U = shape->batch * shape->num_kv_heads;

@@ -24,15 +24,20 @@ __device__ __forceinline__ int seq_blocks(int L, int S, int NB) {
   return n > NB ? NB : n;
 }
 
-// Kept blocks of a unit with n blocks (0 when n == 0), at most k_max.
+// Kept blocks of a unit with n blocks (0 when n == 0), at most k_max: the
+// explicit count kval when `explicit_k`, else the keep rule.
 // (n < 2^14 and keep_num <= keep_den < 2^31, so the product is below 2^52.)
-__device__ __forceinline__ int kept_count(int n, const int32_t* top_k, int b, int keep_num,
-                                          int keep_den, int k_max) {
+__device__ __forceinline__ int kept_count_of(int n, bool explicit_k, int kval, int keep_num,
+                                             int keep_den, int k_max) {
   if (n <= 0) return 0;
-  int k = top_k ? top_k[b]
-                : (int)div_floor((int64_t)n * keep_num + keep_den - 1, keep_den);
+  int k = explicit_k ? kval : (int)div_floor((int64_t)n * keep_num + keep_den - 1, keep_den);
   k = k < 1 ? 1 : (k > n ? n : k);
   return k > k_max ? k_max : k;
+}
+
+__device__ __forceinline__ int kept_count(int n, const int32_t* top_k, int b, int keep_num,
+                                          int keep_den, int k_max) {
+  return kept_count_of(n, top_k != nullptr, top_k ? top_k[b] : 0, keep_num, keep_den, k_max);
 }
 
 // Blocks kept whatever their score: block 0 and/or the newest block n-1.
@@ -43,13 +48,20 @@ __device__ __forceinline__ int forced_count(int n, int force_first, int force_la
 
 // Top-k count of a unit with n blocks once nf forced blocks are counted in:
 // at least nf, at most min(n, k_max), at least 1 (0 when n == 0).
-__device__ __forceinline__ int kept_count_forced(int n, const int32_t* top_k, int b, int keep_num,
-                                                 int keep_den, int k_max, int nf) {
+__device__ __forceinline__ int kept_count_forced_of(int n, bool explicit_k, int kval,
+                                                    int keep_num, int keep_den, int k_max,
+                                                    int nf) {
   if (n <= 0) return 0;
-  int k = kept_count(n, top_k, b, keep_num, keep_den, k_max);
+  int k = kept_count_of(n, explicit_k, kval, keep_num, keep_den, k_max);
   k = k < nf ? nf : k;
   const int cap = n < k_max ? n : k_max;
   return k > cap ? cap : k;
+}
+
+__device__ __forceinline__ int kept_count_forced(int n, const int32_t* top_k, int b, int keep_num,
+                                                 int keep_den, int k_max, int nf) {
+  return kept_count_forced_of(n, top_k != nullptr, top_k ? top_k[b] : 0, keep_num, keep_den,
+                              k_max, nf);
 }
 
 // Key that ranks a forced block above every score.

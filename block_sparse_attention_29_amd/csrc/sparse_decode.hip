@@ -72,21 +72,67 @@ __device__ __forceinline__ int tile_owner(int64_t y, int W, int64_t Tot) {
   return (int)div_floor((y + 1) * W - 1, Tot);
 }
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// The value a unit's block count needs besides its length: the explicit kept
+// count top_k[b] (fused gate) or the given selection's count sel_cnt[u].
+template <bool GATED>
+__device__ __forceinline__ int unit_aux(const DecodeArgs& a, int u) {
+  if constexpr (GATED) return a.top_k ? a.top_k[u / a.Hkv] : 0;
+  return a.sel_idx ? a.sel_cnt[u] : 0;
+}
+
 // Blocks a unit contributes: its kept count (given, or from the keep rule when
 // the gate is fused in), or all its blocks when dense.
-// L: the unit's sequence length.
+// L: the unit's sequence length; aux: unit_aux of the unit.
 template <bool GATED>
-__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int u, int L) {
+__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int L, int aux) {
   if constexpr (GATED) {
     const int n = seq_blocks(L, a.S, a.NB);
-    return kept_count_forced(n, a.top_k, u / a.Hkv, a.keep_num, a.keep_den, a.k_max,
-                             forced_count(n, a.force_first, a.force_last));
+    return kept_count_forced_of(n, a.top_k != nullptr, aux, a.keep_num, a.keep_den, a.k_max,
+                                forced_count(n, a.force_first, a.force_last));
   }
-  if (a.sel_idx) {
-    const int c = a.sel_cnt[u];
-    return c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
-  }
+  if (a.sel_idx) return aux < 0 ? 0 : (aux > a.k_max ? a.k_max : aux);
   return seq_blocks(L, a.S, a.NB);
+}
+
+// The first gate pass's pooled-table and query loads of one unit, issued at
+// kernel entry, before the plan says which unit the workgroup gates: u is the
+// unit it gates first when every unit keeps as many blocks as any other (the
+// plan then confirms it; otherwise the values go unused).  Lane (qd, jq) holds
+// dimensions qd*D/4 .. of blocks 4jq .. 4jq+3, as fused_scores loads them.
+template <typename T, int D, int G>
+struct GatePreload {
+  int u;
+  float pv[D / 4][4];
+  T qr[G];
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void issue_gate_preload(const DecodeArgs& a, int u,
+                                                   GatePreload<T, D, G>& pre) {
+  constexpr int DQ = D / 4;
+  const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
+  const int NB = a.NB;
+  pre.u = u;
+  // Aligned 16-byte loads need NB % 4 == 0; otherwise every lane re-reads the
+  // table's first 16 bytes (in bounds, unused) and the gate loads for itself.
+  const bool vec4 = NB % 4 == 0;
+  const float* row = vec4 ? a.pooled + ((int64_t)u * D + qd * DQ) * NB + min(4 * jq, NB - 4)
+                          : a.pooled;
+  const int64_t step = vec4 ? NB : 0;
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    const float4 v = *(const float4*)(row + i * step);
+    pre.pv[i][0] = v.x; pre.pv[i][1] = v.y; pre.pv[i][2] = v.z; pre.pv[i][3] = v.w;
+  }
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const T* qg = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D + min(tid, D - 1);
+#pragma unroll
+  for (int h = 0; h < G; ++h) pre.qr[h] = qg[h * D];
 }
 
 // VEC consecutive pooled values of one dimension row (one 4*VEC-byte load).
@@ -113,29 +159,47 @@ __device__ __forceinline__ void load_pooled_vec(const float* p, float (&x)[VEC])
 // arithmetic as the gate kernel.  The first pass's pooled loads go out before
 // the query's, so both round trips overlap.  VEC consecutive blocks are one
 // aligned load when NB is a multiple of VEC (no load crosses the table's end).
-template <typename T, int D, int G, int VEC>
+// With PRE and use_pre the first pass takes its pooled and query values from
+// `pre` (VEC = 4 only), loaded at kernel entry.
+template <typename T, int D, int G, int VEC, bool PRE>
 __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, const float* pu,
                                              int n, double* s_q, double* s_part,
-                                             uint64_t* s_key) {
+                                             uint64_t* s_key, const GatePreload<T, D, G>& pre,
+                                             bool use_pre) {
   constexpr int DQ = D / 4, PASS = 64 * VEC;
   const int NB = a.NB;
   const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
   const double inv = 1.0 / sqrt((double)D);
-  for (int j0 = 0; j0 < n; j0 += PASS) {
+  // One pass over blocks j0 .. j0 + PASS - 1; the first (FIRST) also sums the
+  // query and may take the entry loads (peeled, so that they are dead after).
+  auto pass = [&](int j0, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
     // block ids past n are clamped to a valid, aligned group (read, unused)
     const int jg = min(j0 + VEC * jq, ((n - 1) / VEC) * VEC);
     float pv[DQ][VEC];
     const float* row = pu + (int64_t)qd * DQ * NB + jg;
+    bool from_pre = false;
+    if constexpr (FIRST && PRE && VEC == 4) from_pre = use_pre;
+    if (from_pre) {
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) load_pooled_vec<VEC>(row + (int64_t)i * NB, pv[i]);
-    if (j0 == 0) {
+      for (int i = 0; i < DQ; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) pv[i][e] = pre.pv[i][e & 3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) load_pooled_vec<VEC>(row + (int64_t)i * NB, pv[i]);
+    }
+    if constexpr (FIRST) {
       if (tid < D) {
         const T* qg = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D + tid;
         double x[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          if constexpr (sizeof(T) == 2) x[h] = (double)__uint_as_float((uint32_t)qg[h * D] << 16);
-          else x[h] = (double)qg[h * D];
+          T qv;
+          if constexpr (PRE) qv = use_pre ? pre.qr[h] : qg[h * D];
+          else qv = qg[h * D];
+          if constexpr (sizeof(T) == 2) x[h] = (double)__uint_as_float((uint32_t)qv << 16);
+          else x[h] = (double)qv;
         }
         double sq = x[0];
 #pragma unroll
@@ -165,26 +229,29 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
       }
     }
     __syncthreads();
-  }
+  };
+  pass(0, BoolTag<true>{});  // n >= 1
+  for (int j0 = PASS; j0 < n; j0 += PASS) pass(j0, BoolTag<false>{});
 }
 
 // Gate of unit u inside a decode workgroup (the fused mode): the fp64 scores
 // of its n blocks (fused_scores), then its k kept ids, ascending, into dst
 // (LDS).  The owner workgroup of the unit also writes the scores, ids and
 // count out.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool PRE>
 __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
                                                 int32_t* dst,
                                                 bool owner, uint64_t* s_key, double* s_q,
                                                 double* s_part, int* s_hist,
-                                                int* s_scan) {
+                                                int* s_scan, const GatePreload<T, D, G>& pre) {
   const int tid = threadIdx.x;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int NB = a.NB;
   const float* pu = a.pooled + (int64_t)u * D * NB;
-  if (NB % 4 == 0) fused_scores<T, D, G, 4>(a, b, g, pu, n, s_q, s_part, s_key);
-  else if (NB % 2 == 0) fused_scores<T, D, G, 2>(a, b, g, pu, n, s_q, s_part, s_key);
-  else fused_scores<T, D, G, 1>(a, b, g, pu, n, s_q, s_part, s_key);
+  const bool use_pre = u == pre.u;  // the entry loads are this unit's (uniform)
+  if (NB % 4 == 0) fused_scores<T, D, G, 4, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
+  else if (NB % 2 == 0) fused_scores<T, D, G, 2, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
+  else fused_scores<T, D, G, 1, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
   // forced blocks rank above every score while the selection runs
   const bool forced = a.force_first || a.force_last;  // uniform
   uint64_t key_first = 0, key_last = 0;
@@ -238,14 +305,38 @@ void decode_partial_kernel(DecodeArgs a) {
   int* s_scan = s_dyn + U + 1;                // [kWavesPerWG + 1]
   int* s_len = s_dyn + U + 1 + kWavesPerWG + 1;  // [U] sequence length of each unit
 
+  const int lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane >> 4, n16 = lane & 15;
+  // Workgroups are dealt to the XCDs round-robin (workgroup i runs on XCD
+  // i % 8), each XCD with its own L2.  Consecutive tile ranges go to the
+  // workgroups of one XCD, so the workgroups that share a unit mostly share an
+  // L2 (its pooled table, read by each of them in the fused gate, comes from
+  // HBM once).  Any other placement is still correct.
+  const int nwg = (int)gridDim.x;
+  const int wg = (nwg % kXcds == 0)
+      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
+      : (int)blockIdx.x;
+  const int wg0 = wg * kWavesPerWG;
+
+  GatePreload<T, D, G> pre;  // the fused gate's entry loads
+  pre.u = -1;
+
   // ---- plan: block prefix over units (every workgroup computes the same) ----
   {
     const int per = (U + kThreads - 1) / kThreads;
     const int u_lo = min(U, tid * per), u_hi = min(U, u_lo + per);
+    // The loads of the thread's first unit go out first, the gate's entry
+    // loads after them, so the plan waits for its own loads only.
+    const int u_f = min(u_lo, U - 1);
+    const int L_f = a.lens[u_f / a.Hkv];
+    const int aux_f = unit_aux<GATED>(a, u_f);
+    // (wg0 * U < 2^31: fewer than 2^15 waves, at most 2^13 units)
+    if constexpr (GATED)
+      issue_gate_preload<T, D, G>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
     int local = 0;
     for (int u = u_lo; u < u_hi; ++u) {
-      const int L = a.lens[u / a.Hkv];
-      const int c = unit_blocks<GATED>(a, u, L);
+      const int L = u == u_lo ? L_f : a.lens[u / a.Hkv];
+      const int c = unit_blocks<GATED>(a, L, u == u_lo ? aux_f : unit_aux<GATED>(a, u));
       s_len[u] = L;
       s_prefix[u] = c;
       local += c;
@@ -265,17 +356,6 @@ void decode_partial_kernel(DecodeArgs a) {
     }
   }
 
-  const int lane = tid & 63, wv = tid >> 6;
-  const int r16 = lane >> 4, n16 = lane & 15;
-  // Workgroups are dealt to the XCDs round-robin (workgroup i runs on XCD
-  // i % 8), each XCD with its own L2.  Consecutive tile ranges go to the
-  // workgroups of one XCD, so the workgroups that share a unit mostly share an
-  // L2 (its pooled table, read by each of them in the fused gate, comes from
-  // HBM once).  Any other placement is still correct.
-  const int nwg = (int)gridDim.x;
-  const int wg = (nwg % kXcds == 0)
-      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
-      : (int)blockIdx.x;
   // The wave index is uniform per wave; say so, so that everything derived
   // from it (the tile range, the loop counters) lives in scalar registers.
   const int w = __builtin_amdgcn_readfirstlane(wg * kWavesPerWG + wv);
@@ -288,7 +368,6 @@ void decode_partial_kernel(DecodeArgs a) {
   // workgroup's last tile, looked up by all threads at once (one pass over
   // the units instead of a serial binary search per wave) ----
   __shared__ int s_unit[kWavesPerWG + 1];
-  const int wg0 = wg * kWavesPerWG;
   {
     int xq[kWavesPerWG + 1];  // block index of each query tile
 #pragma unroll
@@ -319,16 +398,19 @@ void decode_partial_kernel(DecodeArgs a) {
     if (Y0 < Y1) {
       const int u0 = s_unit[0], u1 = s_unit[kWavesPerWG];
       ids_base = s_prefix[u0];
-      for (int u = u0; u <= u1; ++u) {
+      auto gate = [&](int u, auto pre_tag) {
         const int k = s_prefix[u + 1] - s_prefix[u];
-        if (k == 0) continue;
+        if (k == 0) return;
         // the owner holds the unit's first tile
         const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
-        fused_gate_unit<T, D, G>(a, u, seq_blocks(s_len[u], a.S, a.NB), k,
-                                 s_ids + (s_prefix[u] - ids_base),
-                                 owner == wg, s_key, s_q, s_part, s_hist,
-                                 s_sel_scan);
-      }
+        fused_gate_unit<T, D, G, decltype(pre_tag)::value>(
+            a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
+            owner == wg, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
+      };
+      // The first unit may use the entry loads; peeled off, so that they are
+      // dead in the loop.
+      gate(u0, BoolTag<true>{});
+      for (int u = u0 + 1; u <= u1; ++u) gate(u, BoolTag<false>{});
     }
     // Units without a kept block (a sequence of length 0) belong to nobody:
     // workgroup 0 writes their (empty) selection.

@@ -33,6 +33,9 @@
  *    per call; kernels skip out-of-range ids instead of reading out of bounds.
  *  - Calls that share output or scratch buffers on one stream are ordered by
  *    the stream; concurrent calls on different streams must not share them.
+ *  - q, k, v, the pooled table and the workspace must be 16-byte aligned
+ *    (open_sum 8-byte); a misaligned one returns SEER_ERR_INVALID_ARG
+ *    (SEER_ERR_WORKSPACE for the workspace).
  *
  * Supported: head_dim d in {64, 128}; block_size S in {64, 128}; G = Hq/Hkv in
  * 1..8; dtype fp32 or bf16 for q, k, v (one dtype for all three); at most

@@ -124,3 +124,31 @@ def test_pointer_and_rule_validation(lib):
     assert st == seer.SEER_ERR_INVALID_ARG
     st = lib.seer_sparse_decode_combine(ctypes.byref(sh), None, None, FAKE, 1 << 20, None)
     assert st == seer.SEER_ERR_INVALID_ARG
+
+
+def test_alignment_validation(lib):
+    """16-byte loads need 16-byte aligned q, k, v, pooled and workspace."""
+    sh = _shape()
+    kv = seer.KV(0x1000, 0x1000, None, 0)
+    odd = ctypes.c_void_p(0x1004)
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), odd, FAKE, FAKE, None, 1, 10, 4, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"aligned" in lib.seer_last_error()
+    st = lib.seer_gate_scores_topk(ctypes.byref(sh), FAKE, odd, FAKE, None, 1, 10, 4, FAKE,
+                                   FAKE, FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"aligned" in lib.seer_last_error()
+    bad_kv = seer.KV(0x1000, 0x1008, None, 0)
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), ctypes.byref(bad_kv), None, FAKE, FAKE,
+                                  FAKE, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"aligned" in lib.seer_last_error()
+    st = lib.seer_block_pool_keys(ctypes.byref(sh), ctypes.byref(kv), None, FAKE, odd, FAKE,
+                                  None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"aligned" in lib.seer_last_error()
+    st = lib.seer_sparse_decode(ctypes.byref(sh), odd, ctypes.byref(kv), FAKE, None, None, 0,
+                                ctypes.c_float(0.0), FAKE, None, FAKE, 1 << 20, None)
+    assert st == seer.SEER_ERR_INVALID_ARG and b"aligned" in lib.seer_last_error()
+    st = lib.seer_sparse_decode(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, 0,
+                                ctypes.c_float(0.0), FAKE, None, odd, 1 << 20, None)
+    assert st == seer.SEER_ERR_WORKSPACE and b"aligned" in lib.seer_last_error()
+    st = lib.seer_sparse_decode_combine(ctypes.byref(sh), FAKE, None, odd, 1 << 20, None)
+    assert st == seer.SEER_ERR_WORKSPACE and b"aligned" in lib.seer_last_error()
