@@ -32,7 +32,13 @@ gate but give no weights or internals):
   (a token budget B gives B // S), clamped to [1, n];
 * order: score descending, ties to the lower block index, -0 equal to +0;
   the kept block ids are reported in ascending order;
-* the new token's key and value are in the cache (its length includes it).
+* the new token's key and value are in the cache (its length includes it);
+* a second, learned gate (``learned_gate_scores``) has the shape of the pages'
+  gate network (Linear(d, 256), ReLU, then a 256-wide second layer whose
+  weights are a projection of the query, so the query stays unpooled); its
+  weights are given (seeded, untrained), stored int8 with per-row scales, and
+  its input is a per-block int8 image of the pooled keys, so that the first
+  layer is an exact integer product.
 
 Every function works on one (sequence, KV head) unless its name says otherwise.
 Inputs are float64 arrays holding the exact values of the stored tensors.
@@ -218,6 +224,56 @@ def select_blocks(scores: np.ndarray, *, k: Optional[int] = None,
     count = max(1, min(count, cap))
     kept = forced[:count] + list(ranked[: count - min(count, len(forced))])
     return np.sort(np.array(kept, dtype=np.int64))
+
+
+# --------------------------------------------------------------------------
+# Learned gate (the gate network's shape, with given weights)
+# --------------------------------------------------------------------------
+
+GATE_HIDDEN = 256  # hidden width of the gate network ("Sparse Attention Reasoning", Step 1)
+
+
+def quantize_blocks(pooled32: np.ndarray):
+    """Per-block int8 image of the stored pooled keys, the learned gate's input.
+
+    pooled32: (n, d) float32.  Returns (q8 (n, d) int8, alpha (n,) float32):
+    alpha_j = max_i |P_ji| / 127 and q8_ji = P_ji / alpha_j rounded to the
+    nearest integer, ties to even, both quotients taken in fp32 (correctly
+    rounded); an all-zero block has alpha_j = 1.
+    """
+    p = np.asarray(pooled32, dtype=np.float32)
+    amax = np.max(np.abs(p), axis=1)
+    alpha = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.rint(p / alpha[:, None]).astype(np.int8)
+    return q, alpha
+
+
+def learned_gate_scores(q_group: np.ndarray, pooled32: np.ndarray, w1: np.ndarray,
+                        w1_scale: np.ndarray, b1: np.ndarray, wq: np.ndarray) -> np.ndarray:
+    """Gate scores of one KV head from a two-layer gate network.
+
+    The network has the shape of the gate of "Sparse Attention Reasoning"
+    (Step 1: Linear(hidden, 256), ReLU, Linear(256, 1)) applied to each block's
+    pooled key; the second layer's weights are a projection of the group's
+    query, u = Wq qbar, so that the score depends on the unpooled decode query
+    ("SeerAttention-R", Abstract: a learned gate, query pooling removed):
+
+        h_j = relu(z_j),  z_jm = alpha_j * beta_m * (W1_m . q8_j) + b1_m,
+        s_j = u . h_j / sqrt(H),  u_m = Wq_m . qbar,  qbar = sum_h q_h,
+
+    with (q8, alpha) = quantize_blocks(pooled32), W1 (H, d) int8 with row
+    scales beta = w1_scale (H,) float32, b1 (H,) float32, Wq (H, d) float32,
+    q_group (G, d) float64.  The int8 dot products are exact integers; the
+    rest is fp64 on the exact values.
+    """
+    q8, alpha = quantize_blocks(pooled32)
+    dots = q8.astype(np.int64) @ np.asarray(w1, dtype=np.int64).T          # (n, H), exact
+    scale = alpha.astype(np.float64)[:, None] * np.asarray(w1_scale, dtype=np.float64)[None, :]
+    z = scale * dots.astype(np.float64) + np.asarray(b1, dtype=np.float64)[None, :]
+    h = np.maximum(z, 0.0)
+    qbar = np.asarray(q_group, dtype=np.float64).sum(axis=0)
+    u = np.asarray(wq, dtype=np.float64) @ qbar
+    return (h @ u) / np.sqrt(float(np.asarray(w1).shape[0]))
 
 
 # --------------------------------------------------------------------------

@@ -438,3 +438,97 @@ def test_unified_scores_pins():
     qp = np.concatenate([q[g * G:(g + 1) * G] for g in perm])
     assert np.allclose(O.gate_scores_unified(qp, [P[g] for g in perm], d),
                        O.gate_scores_unified(q, P, d), rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- learned gate
+
+def _gate_weights(rng, H, d):
+    w1 = rng.integers(-127, 128, size=(H, d)).astype(np.int8)
+    beta = (rng.uniform(0.5, 1.5, size=H) / (127.0 * math.sqrt(d))).astype(np.float32)
+    b1 = rng.normal(0.0, 0.05, size=H).astype(np.float32)
+    wq = (rng.normal(0.0, 1.0, size=(H, d)) / math.sqrt(d)).astype(np.float32)
+    return w1, beta, b1, wq
+
+
+def test_quantize_blocks_hand_cases():
+    c = GOLD["learned_gate_quantize"]
+    q8, alpha = O.quantize_blocks(np.array(c["rows"], dtype=np.float32))
+    assert q8.dtype == np.int8
+    assert q8.tolist() == c["expected_q8"]
+    assert alpha[3] == np.float32(1.0)
+
+
+def test_quantize_round_trip_bound():
+    rng = np.random.default_rng(11)
+    p = (rng.standard_t(3, size=(300, 128)) * 10.0 ** rng.uniform(-6, 6, size=(300, 1))).astype(np.float32)
+    q8, alpha = O.quantize_blocks(p)
+    a = alpha.astype(np.float64)[:, None]
+    err = np.abs(q8.astype(np.float64) * a - p.astype(np.float64))
+    # the fp32 quotient is off by at most 127 * 2^-24 before rounding to an integer
+    assert np.all(err <= a * (0.5 + 127 * 2.0 ** -24))
+    assert np.abs(q8.astype(np.int64)).max() <= 127
+    assert np.all(np.abs(q8.astype(np.int64)).max(axis=1) == 127)   # the largest entry maps to +-127
+
+
+def test_learned_gate_hidden_permutation_invariance():
+    rng = np.random.default_rng(12)
+    H, d, n = 256, 64, 40
+    w1, beta, b1, wq = _gate_weights(rng, H, d)
+    p = rng.normal(size=(n, d)).astype(np.float32)
+    qg = rng.normal(size=(4, d))
+    s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
+    perm = rng.permutation(H)
+    s2 = O.learned_gate_scores(qg, p, w1[perm], beta[perm], b1[perm], wq[perm])
+    assert np.allclose(s, s2, rtol=1e-12, atol=1e-12 * np.abs(s).max())
+
+
+def test_learned_gate_homogeneity():
+    rng = np.random.default_rng(13)
+    H, d, n = 256, 128, 33
+    w1, beta, b1, wq = _gate_weights(rng, H, d)
+    p = rng.normal(size=(n, d)).astype(np.float32)
+    qg = rng.normal(size=(4, d))
+    s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
+    # the query enters linearly (through u only): 2q gives exactly 2s
+    assert np.array_equal(O.learned_gate_scores(2.0 * qg, p, w1, beta, b1, wq), 2.0 * s)
+    # keys scaled by a power of two: alpha scales with them, the int8 image does not
+    q8, alpha = O.quantize_blocks(p)
+    q8b, alphab = O.quantize_blocks(p * np.float32(4.0))
+    assert np.array_equal(q8, q8b) and np.array_equal(alphab, alpha * np.float32(4.0))
+    zb = np.zeros_like(b1)
+    s0 = O.learned_gate_scores(qg, p, w1, beta, zb, wq)
+    assert np.array_equal(O.learned_gate_scores(qg, p * np.float32(4.0), w1, beta, zb, wq), 4.0 * s0)
+
+
+def test_learned_gate_bias_saturation():
+    rng = np.random.default_rng(14)
+    H, d, n = 256, 64, 50
+    w1, beta, _, wq = _gate_weights(rng, H, d)
+    p = rng.normal(size=(n, d)).astype(np.float32)
+    qg = rng.normal(size=(2, d))
+    s = O.learned_gate_scores(qg, p, w1, beta, np.full(H, -1e30, dtype=np.float32), wq)
+    assert np.all(s == 0.0)
+    assert O.select_top_blocks(s, 7).tolist() == list(range(7))
+
+
+def test_learned_gate_reduces_to_the_linear_gate():
+    """With every hidden unit active the network is linear: s_j equals the
+    parameter-free gate on the dequantised keys with the effective query
+    w = sum_m u_m beta_m W1_m, plus a constant."""
+    rng = np.random.default_rng(15)
+    H, d, n = 256, 128, 64
+    w1, beta, _, wq = _gate_weights(rng, H, d)
+    p = rng.normal(size=(n, d)).astype(np.float32)
+    qg = rng.normal(size=(4, d))
+    q8, alpha = O.quantize_blocks(p)
+    zmax = (alpha[:, None].astype(np.float64) * beta[None, :].astype(np.float64)
+            * np.abs(q8.astype(np.float64) @ w1.astype(np.float64).T)).max()
+    b1 = np.full(H, np.float32(2.0 * zmax + 1.0), dtype=np.float32)     # every z_jm > 0
+    s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
+    u = wq.astype(np.float64) @ qg.sum(axis=0)
+    w = (u * beta.astype(np.float64)) @ w1.astype(np.float64)
+    c = float(u @ b1.astype(np.float64)) / math.sqrt(H)
+    deq = q8.astype(np.float64) * alpha.astype(np.float64)[:, None]
+    lin = O.gate_scores(w[None, :], deq, d) * math.sqrt(d) / math.sqrt(H)
+    assert np.allclose(s - c, lin, rtol=0, atol=1e-9 * (abs(c) + np.abs(lin).max()))
+    assert not np.allclose(lin, 0.0)

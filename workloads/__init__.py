@@ -7,6 +7,7 @@ attention).
 """
 
 from .configs import WORKLOADS, Workload, get_workload
-from .gen import Case, make_case
+from .gen import Case, GateWeights, make_case, make_gate_weights
 
-__all__ = ["WORKLOADS", "Workload", "get_workload", "Case", "make_case"]
+__all__ = ["WORKLOADS", "Workload", "get_workload", "Case", "make_case", "GateWeights",
+           "make_gate_weights"]

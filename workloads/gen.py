@@ -152,3 +152,36 @@ def make_case(wl: Workload, device="cpu", poison: bool = False) -> Case:
         kp[ids_l] = k[b, :, : nb * S].reshape(Hkv, nb, S, d).transpose(0, 1)
         vp[ids_l] = v[b, :, : nb * S].reshape(Hkv, nb, S, d).transpose(0, 1)
     return Case(wl, q, kp, vp, lens.to(torch.int32), table, top_k, planted, num_pages)
+
+
+@dataclasses.dataclass
+class GateWeights:
+    """Weights of the learned gate network, one set per KV head (CPU tensors).
+
+    w1 int8 [Hkv][H][d], w1_scale float32 [Hkv][H], b1 float32 [Hkv][H],
+    wq float32 [Hkv][H][d]; H is the hidden width.
+    """
+    w1: torch.Tensor
+    w1_scale: torch.Tensor
+    b1: torch.Tensor
+    wq: torch.Tensor
+
+    def to(self, device) -> "GateWeights":
+        return GateWeights(*(t.to(device) for t in (self.w1, self.w1_scale, self.b1, self.wq)))
+
+
+def make_gate_weights(num_kv_heads: int, head_dim: int, hidden: int = 256,
+                      seed: int = 0) -> GateWeights:
+    """Seeded random gate weights, drawn on the CPU in a fixed order: w1 as
+    ``randint(-127, 128)``, w1_scale as ``(0.5 + rand) / (127 sqrt(d))``, b1 as
+    ``0.05 * randn``, wq as ``randn / sqrt(d)``.  Untrained: they give the gate
+    its shape and a realistic spread of scores, nothing more."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    H, d = hidden, head_dim
+    w1 = torch.randint(-127, 128, (num_kv_heads, H, d), generator=g, dtype=torch.int64).to(torch.int8)
+    w1_scale = (0.5 + torch.rand((num_kv_heads, H), generator=g)) / (127.0 * d ** 0.5)
+    b1 = 0.05 * torch.randn((num_kv_heads, H), generator=g)
+    wq = torch.randn((num_kv_heads, H, d), generator=g) / d ** 0.5
+    return GateWeights(w1.contiguous(), w1_scale.float().contiguous(), b1.float().contiguous(),
+                       wq.float().contiguous())
