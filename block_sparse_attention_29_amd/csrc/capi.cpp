@@ -185,6 +185,37 @@ size_t max_block_smem() {
 }
 
 
+// The gate kernels' arguments from a validated call.
+seer::GateArgs gate_args(const seer_shape* shape, const void* q, const float* pooled,
+                         const int32_t* lens, const seer_select* rule, int32_t k_max,
+                         double* scores, int32_t* sel_idx, int32_t* sel_cnt) {
+  seer::GateArgs a{};
+  a.q = q;
+  a.pooled = pooled;
+  a.lens = lens;
+  a.top_k = rule->top_k;
+  a.keep_num = rule->keep_num;
+  a.keep_den = rule->keep_den;
+  a.k_max = k_max;
+  a.B = shape->batch;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.D = shape->head_dim;
+  a.NB = shape->max_blocks;
+  a.S = shape->block_size;
+  a.dtype = shape->dtype;
+  a.scores = scores;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.threshold_mode = rule->mode == SEER_SELECT_THRESHOLD;
+  a.threshold = rule->threshold;
+  a.force_first = rule->force_first != 0;
+  a.force_last = rule->force_last != 0;
+  a.unified = rule->unified != 0;
+  return a;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -237,39 +268,48 @@ seer_status seer_block_pool_keys(const seer_shape* shape, const seer_kv* kv,
   return ok();
 }
 
+
 seer_status seer_gate_select(const seer_shape* shape, const void* q, const float* pooled,
                              const int32_t* lens, const seer_select* rule, int32_t k_max,
                              double* scores, int32_t* sel_idx, int32_t* sel_cnt,
                              hipStream_t stream) {
   const seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (st) return st;
-  seer::GateArgs a{};
-  a.q = q;
-  a.pooled = pooled;
-  a.lens = lens;
-  a.top_k = rule->top_k;
-  a.keep_num = rule->keep_num;
-  a.keep_den = rule->keep_den;
-  a.k_max = k_max;
-  a.B = shape->batch;
-  a.Hq = shape->num_q_heads;
-  a.Hkv = shape->num_kv_heads;
-  a.D = shape->head_dim;
-  a.NB = shape->max_blocks;
-  a.S = shape->block_size;
-  a.dtype = shape->dtype;
-  a.scores = scores;
-  a.sel_idx = sel_idx;
-  a.sel_cnt = sel_cnt;
-  a.threshold_mode = rule->mode == SEER_SELECT_THRESHOLD;
-  a.threshold = rule->threshold;
-  a.force_first = rule->force_first != 0;
-  a.force_last = rule->force_last != 0;
-  a.unified = rule->unified != 0;
+  const seer::GateArgs a =
+      gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (seer::gate_smem_bytes(a.NB, k_max) > max_block_smem())
     return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
   const hipError_t e = seer::launch_gate_topk(a, stream);
   if (e != hipSuccess) return hip_fail(e, "gate_topk launch");
+  return ok();
+}
+
+seer_status seer_learned_gate_select(const seer_shape* shape, const void* q, const float* pooled,
+                                     const int32_t* lens, const seer_gate_weights* weights,
+                                     const seer_select* rule, int32_t k_max, double* scores,
+                                     int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
+  const seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (st) return st;
+  if (!weights || !weights->w1 || !weights->w1_scale || !weights->b1 || !weights->wq)
+    return fail(SEER_ERR_INVALID_ARG, "gate weights missing");
+  if (!aligned16(weights->w1) || ((uintptr_t)weights->w1_scale & 3) ||
+      ((uintptr_t)weights->b1 & 3) || ((uintptr_t)weights->wq & 3))
+    return fail(SEER_ERR_INVALID_ARG,
+                "gate weights misaligned (w1 16-byte aligned, the float arrays 4-byte)");
+  if (weights->hidden != seer::kGateHidden)
+    return fail(SEER_ERR_UNSUPPORTED, "gate hidden width %d != %d", weights->hidden,
+                seer::kGateHidden);
+  if (rule->unified)
+    return fail(SEER_ERR_UNSUPPORTED, "a unified selection is not supported by the learned gate");
+  seer::GateArgs a = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  a.w1 = weights->w1;
+  a.w1_scale = weights->w1_scale;
+  a.b1 = weights->b1;
+  a.wq = weights->wq;
+  if (seer::learned_gate_smem_total(a.D, a.NB) > max_block_smem())
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
+  const hipError_t e = seer::launch_learned_gate(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "learned_gate launch");
   return ok();
 }
 

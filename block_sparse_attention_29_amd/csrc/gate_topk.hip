@@ -35,6 +35,79 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
   return (double)p[i];
 }
 
+// The selection rule and the outputs of one selection, once s_key[0..n) holds
+// the scores' order keys: forced blocks get a key above every score; the count
+// is the top-k count (raised to the forced blocks), or the number of keys
+// above the threshold's key; then block_topk_ids (an exact radix select by the
+// whole workgroup); the ids go to the rows of KV heads g_lo .. g_hi - 1 (from
+// LDS when UNIFIED), the scores written out are the blocks' own.
+template <int NT, bool UNIFIED>
+__device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, int g_hi, int n,
+                                            uint64_t* s_key, int32_t* s_ids, int* s_hist,
+                                            int* s_scan) {
+  const int tid = threadIdx.x;
+  // ---- forced blocks and the kept count ----
+  const int nf = forced_count(n, a.force_first, a.force_last);
+  uint64_t key_first = 0, key_last = 0;
+  if (nf > 0) {
+    key_first = s_key[0];
+    key_last = s_key[n - 1];
+    __syncthreads();
+    if (tid == 0) {
+      if (a.force_first) s_key[0] = kForcedKey;
+      if (a.force_last) s_key[n - 1] = kForcedKey;
+    }
+    __syncthreads();
+  }
+  int k;
+  if (a.threshold_mode) {
+    const uint64_t kt = order_key(a.threshold);
+    int c = 0;
+    for (int j = tid; j < n; j += NT) c += s_key[j] > kt;
+    int total;
+    block_excl_scan<NT>(c, s_scan, &total);
+    const int cap = n < a.k_max ? n : a.k_max;
+    k = n > 0 ? max(1, min(total, cap)) : 0;
+  } else {
+    k = kept_count_forced(n, a.top_k, b, a.keep_num, a.keep_den, a.k_max, nf);
+  }
+
+  // ---- selection: into the unit's row, or into LDS and then every row of
+  // the sequence when unified ----
+  int32_t* row0 = a.sel_idx + (int64_t)(b * a.Hkv + g_lo) * a.k_max;
+  int32_t* dst = UNIFIED ? s_ids : row0;
+  if (k >= n) {
+    for (int j = tid; j < n; j += NT) dst[j] = j;
+  } else {
+    block_topk_ids<NT>(s_key, n, k, s_hist, s_scan, dst);
+  }
+  if (nf > 0 || UNIFIED) __syncthreads();
+  if (nf > 0) {
+    if (tid == 0) {  // the forced blocks' own scores go out
+      s_key[0] = key_first;
+      s_key[n - 1] = key_last;
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs (the scores last: a pending store holds its data registers,
+  // so nothing waits behind it) ----
+  for (int g = g_lo; g < g_hi; ++g) {
+    const int u = b * a.Hkv + g;
+    int32_t* out = a.sel_idx + (int64_t)u * a.k_max;
+    if constexpr (UNIFIED) {
+      for (int j = tid; j < a.k_max; j += NT) out[j] = j < k ? s_ids[j] : -1;
+    } else {
+      for (int j = k + tid; j < a.k_max; j += NT) out[j] = -1;
+    }
+    if (tid == 0) a.sel_cnt[u] = k;
+  }
+  for (int g = g_lo; g < g_hi; ++g) {
+    double* sc = a.scores + (int64_t)(b * a.Hkv + g) * a.NB;
+    for (int j = tid; j < n; j += NT) sc[j] = key_score(s_key[j]);
+  }
+}
+
 // One workgroup per selection -- a unit (sequence b, KV head g), or a whole
 // sequence when the selection is unified over its KV heads: scores for all
 // blocks, then the selection.
@@ -127,66 +200,183 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
     __syncthreads();
   }
 
-  // ---- forced blocks and the kept count ----
-  const int nf = forced_count(n, a.force_first, a.force_last);
-  uint64_t key_first = 0, key_last = 0;
-  if (nf > 0) {
-    key_first = s_key[0];
-    key_last = s_key[n - 1];
-    __syncthreads();
-    if (tid == 0) {
-      if (a.force_first) s_key[0] = kForcedKey;
-      if (a.force_last) s_key[n - 1] = kForcedKey;
-    }
-    __syncthreads();
-  }
-  int k;
-  if (a.threshold_mode) {
-    const uint64_t kt = order_key(a.threshold);
-    int c = 0;
-    for (int j = tid; j < n; j += kTopkThreads) c += s_key[j] > kt;
-    int total;
-    block_excl_scan<kTopkThreads>(c, s_scan, &total);
-    const int cap = n < a.k_max ? n : a.k_max;
-    k = n > 0 ? max(1, min(total, cap)) : 0;
-  } else {
-    k = kept_count_forced(n, a.top_k, b, a.keep_num, a.keep_den, a.k_max, nf);
-  }
+  gate_finish<kTopkThreads, UNIFIED>(a, b, g_lo, g_hi, n, s_key, s_ids, &s_hist[0][0], s_scan);
+}
 
-  // ---- selection: into the unit's row, or into LDS and then every row of
-  // the sequence when unified ----
-  int32_t* row0 = a.sel_idx + (int64_t)(b * a.Hkv + g_lo) * a.k_max;
-  int32_t* dst = UNIFIED ? s_ids : row0;
-  if (k >= n) {
-    for (int j = tid; j < n; j += kTopkThreads) dst[j] = j;
-  } else {
-    block_topk_ids<kTopkThreads>(s_key, n, k, &s_hist[0][0], s_scan, dst);
+// ---------------------------------------------------------------- learned gate
+//
+// The gate network of "Sparse Attention Reasoning" (Step 1: Linear(hidden, 256),
+// ReLU, Linear(256, 1)) on each block's pooled key, with the second layer's
+// weights a projection of the group's query so that the decode query stays
+// unpooled ("SeerAttention-R", Abstract):
+//   z_jm = alpha_j * beta_m * (W1_m . q8_j) + b1_m,  s_j = sum_m u_m relu(z_jm) / 16,
+//   u_m = Wq_m . qbar (fp64),
+// where q8_j = round-half-even(P_j / alpha_j) (fp32 quotient) and
+// alpha_j = max_i |P_ji| / 127 (fp32; 1 for an all-zero block) is the block's
+// int8 image and W1 is int8 with fp32 row scales beta.  The first layer is
+// an exact int32 product on int8 MFMA (v_mfma_i32_16x16x64_i8: A = W1 rows,
+// B = int8 blocks, both operands with the same lane -> k assignment, so the
+// dot products are exact whatever the hardware's k order); the rest is fp64
+// (alpha * beta is exact in fp64).  One 1024-thread workgroup per unit:
+// wave w owns hidden units 16w .. 16w + 15 and every block tile of a chunk
+// of 128 blocks; a score is summed over the wave's units, then over the 16
+// waves in order.  The selection rule and outputs are the gate kernel's.
+
+constexpr int kLgThreads = 1024;  // 16 waves x 16 hidden units = 256
+constexpr int kLgChunk = 128;     // blocks quantised and scored per pass
+constexpr int kLgPad = 16;        // bytes added to every LDS row of int8 data (bank spread)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int D>
+__global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
+  constexpr int H = kGateHidden, JC = kLgChunk, NW = kLgThreads / 64;
+  constexpr int KS = D / 64;                 // MFMA k-steps
+  constexpr int PD = D + kLgPad;             // LDS row pitch of int8 rows
+  constexpr int TPB = kLgThreads / JC;       // quantisation threads per block
+  constexpr int DQ = D / TPB;                // dimensions per quantisation thread
+  static_assert(H == 16 * NW, "one wave per 16 hidden units");
+  static_assert(DQ == 8 || DQ == 16, "8 or 16 int8 per quantisation thread");
+  extern __shared__ uint64_t s_key[];               // [NB] order keys of the scores
+  __shared__ __align__(16) int8_t s_w1[H * PD];     // W1 of the KV head: row m, k contiguous
+  __shared__ __align__(16) int8_t s_pq[JC * PD];    // int8 image of the chunk's blocks: row j
+  __shared__ double s_red[NW][JC];                  // per-wave sums of the chunk's scores
+  __shared__ double s_u[H];
+  __shared__ double s_q[D];
+  __shared__ float s_beta[H], s_b1[H], s_alpha[JC];
+  __shared__ float s_amx[TPB][JC];
+  __shared__ int s_hist[3 * 256];
+  __shared__ int s_scan[NW + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane >> 4, n16 = lane & 15;
+  const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  const int G = a.Hq / a.Hkv;
+  const int NB = a.NB;
+
+  // ---- the KV head's weights into LDS; the group-summed query (fp64, head order) ----
+  const int8_t* w1g = a.w1 + (int64_t)g * H * D;
+  for (int o = tid * 16; o < H * D; o += kLgThreads * 16)
+    *(int4*)(s_w1 + (o / D) * PD + o % D) = *(const int4*)(w1g + o);
+  if (tid < H) {
+    s_beta[tid] = a.w1_scale[(int64_t)g * H + tid];
+    s_b1[tid] = a.b1[(int64_t)g * H + tid];
   }
-  if (nf > 0 || UNIFIED) __syncthreads();
-  if (nf > 0) {
-    if (tid == 0) {  // the forced blocks' own scores go out
-      s_key[0] = key_first;
-      s_key[n - 1] = key_last;
+  if (tid < D) {
+    const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+    double sq = load_as_double<T>(q, tid);
+    for (int h = 1; h < G; ++h) sq = sq + load_as_double<T>(q, (int64_t)h * D + tid);
+    s_q[tid] = sq;
+  }
+  __syncthreads();
+
+  // ---- u = Wq qbar: four threads per hidden unit, D/4 dimensions each ----
+  {
+    const int m = tid >> 2, qp = tid & 3;
+    const float* wr = a.wq + ((int64_t)g * H + m) * D + qp * (D / 4);
+    double c = 0.0;
+#pragma unroll 8
+    for (int i = 0; i < D / 4; ++i) c = fma((double)wr[i], s_q[qp * (D / 4) + i], c);
+    c = quad_sum_f64(c);
+    if (qp == 0) s_u[m] = c;
+  }
+  __syncthreads();
+
+  // This lane's hidden units in the MFMA result: m = 16 wv + 4 r16 + i.
+  double um[4], bm[4], betam[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wv * 16 + 4 * r16 + i;
+    um[i] = s_u[m];
+    bm[i] = (double)s_b1[m];
+    betam[i] = (double)s_beta[m];
+  }
+  // A operand: W1 row 16 wv + n16, bytes 64 s + 16 r16 .. + 15 of k-step s.
+  i32x4 wa[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    wa[st] = *(const i32x4*)(s_w1 + (wv * 16 + n16) * PD + st * 64 + r16 * 16);
+
+  for (int j0 = 0; j0 < n; j0 += JC) {
+    // ---- int8 image of blocks j0 .. j0 + JC - 1 (thread: block jl, dims part*DQ ..) ----
+    {
+      const int jl = tid % JC, part = tid / JC, j = j0 + jl;
+      const bool live = j < n;
+      const float* col = a.pooled + ((int64_t)u * D + part * DQ) * NB + min(j, n - 1);
+      float x[DQ];
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        const float v = col[(int64_t)i * NB];  // clamped column: in bounds
+        x[i] = live ? v : 0.f;
+        mx = fmaxf(mx, fabsf(x[i]));
+      }
+      s_amx[part][jl] = mx;
+      __syncthreads();
+      float amax = 0.f;
+#pragma unroll
+      for (int p = 0; p < TPB; ++p) amax = fmaxf(amax, s_amx[p][jl]);
+      const float alpha = amax > 0.f ? amax / 127.f : 1.f;  // IEEE division
+      uint32_t w[DQ / 4];
+#pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qv = (int)rintf(x[4 * i + e] / alpha);  // |qv| <= 127
+          word |= (uint32_t)(qv & 0xFF) << (8 * e);
+        }
+        w[i] = word;
+      }
+      int8_t* dst = s_pq + jl * PD + part * DQ;
+      if constexpr (DQ == 16) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+      else *(uint2*)dst = make_uint2(w[0], w[1]);
+      if (part == 0) s_alpha[jl] = alpha;
     }
     __syncthreads();
-  }
 
-  // ---- outputs (the scores last: a pending store holds its data registers,
-  // so nothing waits behind it) ----
-  for (int g = g_lo; g < g_hi; ++g) {
-    const int u = b * a.Hkv + g;
-    int32_t* out = a.sel_idx + (int64_t)u * a.k_max;
-    if constexpr (UNIFIED) {
-      for (int j = tid; j < a.k_max; j += kTopkThreads) out[j] = j < k ? s_ids[j] : -1;
-    } else {
-      for (int j = k + tid; j < a.k_max; j += kTopkThreads) out[j] = -1;
+    // ---- first layer on MFMA, the rest in fp64 ----
+#pragma unroll 2
+    for (int jt = 0; jt < JC / 16; ++jt) {
+      i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const i32x4 pb = *(const i32x4*)(s_pq + (jt * 16 + n16) * PD + st * 64 + r16 * 16);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[st], pb, acc, 0, 0, 0);
+      }
+      // lane (r16, n16) holds z's integer part for units 16 wv + 4 r16 + i, block jt*16 + n16
+      const double al = (double)s_alpha[jt * 16 + n16];
+      double sc = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double z = fma(al * betam[i], (double)acc[i], bm[i]);
+        sc = fma(um[i], fmax(z, 0.0), sc);
+      }
+      sc = sc + __shfl_xor(sc, 16, 64);  // row groups 0+1 and 2+3
+      sc = sc + __shfl_xor(sc, 32, 64);  // then the two pairs
+      if (r16 == 0) s_red[wv][jt * 16 + n16] = sc;
     }
-    if (tid == 0) a.sel_cnt[u] = k;
+    __syncthreads();
+
+    // ---- scores: the 16 waves' sums in order, 1/sqrt(256) = 1/16 exactly ----
+    if (tid < JC && j0 + tid < n) {
+      double sj = s_red[0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sj = sj + s_red[w][tid];
+      s_key[j0 + tid] = order_key(sj * (1.0 / 16.0));
+    }
+    // (the next chunk rewrites s_red only after its barriers)
   }
-  for (int g = g_lo; g < g_hi; ++g) {
-    double* sc = a.scores + (int64_t)(b * a.Hkv + g) * a.NB;
-    for (int j = tid; j < n; j += kTopkThreads) sc[j] = key_score(s_key[j]);
-  }
+  __syncthreads();
+  gate_finish<kLgThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+}
+
+template <typename T, int D>
+const void* learned_fn() { return (const void*)&learned_gate_kernel<T, D>; }
+
+const void* learned_kernel(int dtype, int D) {
+  if (dtype == 1) return D == 64 ? learned_fn<uint16_t, 64>() : learned_fn<uint16_t, 128>();
+  return D == 64 ? learned_fn<float, 64>() : learned_fn<float, 128>();
 }
 
 }  // namespace
@@ -214,6 +404,25 @@ hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
   const int grid = a.unified ? a.B : U;
   return hipLaunchKernel(fn, dim3(grid), dim3(kTopkThreads), params,
                          gate_smem_bytes(a.NB, a.k_max), stream);
+}
+
+}  // namespace seer
+
+namespace seer {
+
+size_t learned_gate_smem_dynamic(int NB) { return (size_t)NB * sizeof(uint64_t); }
+
+size_t learned_gate_smem_total(int D, int NB) {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, learned_kernel(1, D)) != hipSuccess) return (size_t)-1;
+  return attr.sharedSizeBytes + learned_gate_smem_dynamic(NB);
+}
+
+hipError_t launch_learned_gate(const GateArgs& a, hipStream_t stream) {
+  GateArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(learned_kernel(a.dtype, a.D), dim3(a.B * a.Hkv), dim3(kLgThreads), params,
+                         learned_gate_smem_dynamic(a.NB), stream);
 }
 
 }  // namespace seer

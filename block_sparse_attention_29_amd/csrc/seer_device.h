@@ -69,6 +69,22 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// fp64 through two 32-bit DPP moves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)((uint64_t)b >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// ((x0 + x1) + (x2 + x3)) over the four lanes of a quad, in every lane of it
+// (IEEE addition commutes, so all four compute the same bits).
+__device__ __forceinline__ double quad_sum_f64(double x) {
+  x = x + dpp_f64<kDppQuadXor1>(x);
+  return x + dpp_f64<kDppQuadXor2>(x);
+}
+
 __device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));

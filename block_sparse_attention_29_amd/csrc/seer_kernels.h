@@ -93,11 +93,23 @@ struct GateArgs {
   int32_t force_first;     // keep block 0 whatever its score
   int32_t force_last;      // keep the newest block whatever its score
   int32_t unified;         // one selection per sequence from the KV heads' summed scores
+  // Learned gate (launch_learned_gate only): per KV head, w1 int8 [Hkv][256][D]
+  // with row scales w1_scale [Hkv][256], b1 [Hkv][256], wq [Hkv][256][D].
+  const int8_t* w1;
+  const float* w1_scale;
+  const float* b1;
+  const float* wq;
 };
 
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream);
 // Dynamic LDS of the gate kernel.
 size_t gate_smem_bytes(int NB, int k_max);
+// The learned gate network's scores, then the same selection rule (not unified).
+constexpr int kGateHidden = 256;
+hipError_t launch_learned_gate(const GateArgs& a, hipStream_t stream);
+// All LDS (static and dynamic) the learned gate kernel needs, and its dynamic part.
+size_t learned_gate_smem_total(int D, int NB);
+size_t learned_gate_smem_dynamic(int NB);
 
 // ---------------------------------------------------------------- pooling
 

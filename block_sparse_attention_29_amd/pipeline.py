@@ -5,10 +5,11 @@ table, open-block sums, scores, selection, outputs, workspace) and enqueues:
 
     build_pool(lens)             bulk key pooling after prefill
     append(lens_old, lens_new)   incremental pooling of newly cached tokens
-    select(q, lens)              gate scores + top-k block selection
+    select(q, lens)              gate scores + top-k block selection (the learned
+                                 gate network when gate weights are given)
     attend(q, lens)              sparse (or dense) decode attention
     step(q, lens)                select + attend, the gate fused into the attention
-                                 kernel (two launches)
+                                 kernel (two launches; with a learned gate, three)
     step_unfused(q, lens)        select, then attend (three launches)
 
 all on torch's current stream, with no host synchronisation.
@@ -29,13 +30,16 @@ class DecodeState:
                  v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
                  k_max: Optional[int] = None, keep: Optional[tuple] = None,
                  top_k: Optional[torch.Tensor] = None, threshold: Optional[float] = None,
-                 force_first: bool = False, force_last: bool = False, unified: bool = False):
+                 force_first: bool = False, force_last: bool = False, unified: bool = False,
+                 gate_weights=None):
         self.shape = seer.make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks, dtype)
         self.k, self.v, self.page_table = k, v, page_table
         self.kv = seer.make_kv(k, v, page_table)
         self.keep = keep
         self.top_k = top_k
+        # learned gate: device tensors w1, w1_scale, b1, wq (or None: parameter-free gate)
+        self.gate_weights = gate_weights
         self.rule = seer.make_select(top_k=top_k, keep=keep, threshold=threshold,
                                      force_first=force_first, force_last=force_last,
                                      unified=unified)
@@ -66,8 +70,13 @@ class DecodeState:
 
     # selection -------------------------------------------------------------
     def select(self, q: torch.Tensor, lens: torch.Tensor):
-        seer.gate_select(self.shape, q, self.pooled, lens, self.rule, self.k_max, self.scores,
-                         self.sel_idx, self.sel_cnt)
+        if self.gate_weights is not None:
+            seer.learned_gate_select(self.shape, q, self.pooled, lens, self.gate_weights,
+                                     self.rule, self.k_max, self.scores, self.sel_idx,
+                                     self.sel_cnt)
+        else:
+            seer.gate_select(self.shape, q, self.pooled, lens, self.rule, self.k_max,
+                             self.scores, self.sel_idx, self.sel_cnt)
 
     # attention -------------------------------------------------------------
     def attend(self, q: torch.Tensor, lens: torch.Tensor, dense: bool = False,
@@ -85,7 +94,9 @@ class DecodeState:
 
     def step(self, q: torch.Tensor, lens: torch.Tensor):
         """Gate, select and attend: one decode step over a built pooled table
-        (the gate fused into the attention kernel)."""
+        (the parameter-free gate fused into the attention kernel)."""
+        if self.gate_weights is not None:
+            return self.step_unfused(q, lens)
         seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,
                                  self.lse, self.workspace)

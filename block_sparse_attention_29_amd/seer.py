@@ -31,6 +31,7 @@ EXPORTS = (
     "seer_block_pool_keys",
     "seer_gate_scores_topk",
     "seer_gate_select",
+    "seer_learned_gate_select",
     "seer_sparse_decode_workspace_size",
     "seer_sparse_decode",
     "seer_sparse_decode_partial",
@@ -67,6 +68,17 @@ def make_select(*, top_k: Optional[torch.Tensor] = None, keep=None, threshold=No
     return Select(mode, None if top_k is None else top_k.data_ptr(), num, den,
                   0.0 if threshold is None else float(threshold), int(force_first),
                   int(force_last), int(unified))
+
+
+class GateWeightsC(ctypes.Structure):
+    """seer_gate_weights: the learned gate's weights (include/seer.h)."""
+    _fields_ = [
+        ("w1", ctypes.c_void_p),
+        ("w1_scale", ctypes.c_void_p),
+        ("b1", ctypes.c_void_p),
+        ("wq", ctypes.c_void_p),
+        ("hidden", ctypes.c_int32),
+    ]
 
 
 class Shape(ctypes.Structure):
@@ -128,6 +140,8 @@ def load(path: str = LIB_PATH):
     lib.seer_sparse_decode_combine.argtypes = [SP, _P, _P, _P, ctypes.c_size_t, _P]
     RP = ctypes.POINTER(Select)
     lib.seer_gate_select.argtypes = [SP, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
+    lib.seer_learned_gate_select.argtypes = [SP, _P, _P, _P, ctypes.POINTER(GateWeightsC), RP,
+                                             _I32, _P, _P, _P, _P]
     lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, RP, _I32, ctypes.c_float, _P,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
@@ -140,6 +154,7 @@ def load(path: str = LIB_PATH):
     lib.seer_last_error.argtypes = []
     lib.seer_last_error.restype = ctypes.c_char_p
     for name in ("seer_block_pool_keys", "seer_gate_scores_topk", "seer_gate_select",
+                 "seer_learned_gate_select",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
                  "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial"):
@@ -227,6 +242,30 @@ def gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor, lens: torch
     _check(lib.seer_gate_select(ctypes.byref(shape), _ptr(q), _ptr(pooled), _ptr(lens),
                                 ctypes.byref(rule), k_max, _ptr(scores), _ptr(sel_idx),
                                 _ptr(sel_cnt), _stream()))
+
+
+def learned_gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor,
+                        lens: torch.Tensor, weights, rule: Select, k_max: int,
+                        scores: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor):
+    """seer_learned_gate_select; ``weights`` has device tensors w1 (int8), w1_scale,
+    b1, wq (float32) in the layouts of include/seer.h."""
+    lib = load()
+    U = shape.batch * shape.num_kv_heads
+    H = int(weights.w1.shape[-2])
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    _need(weights.w1, torch.int8, shape.num_kv_heads * H * shape.head_dim, "w1")
+    _need(weights.w1_scale, torch.float32, shape.num_kv_heads * H, "w1_scale")
+    _need(weights.b1, torch.float32, shape.num_kv_heads * H, "b1")
+    _need(weights.wq, torch.float32, shape.num_kv_heads * H * shape.head_dim, "wq")
+    w = GateWeightsC(_ptr(weights.w1), _ptr(weights.w1_scale), _ptr(weights.b1),
+                     _ptr(weights.wq), H)
+    _check(lib.seer_learned_gate_select(ctypes.byref(shape), _ptr(q), _ptr(pooled), _ptr(lens),
+                                        ctypes.byref(w), ctypes.byref(rule), k_max,
+                                        _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _stream()))
 
 
 def sparse_decode_workspace_size(shape: Shape) -> int:

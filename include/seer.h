@@ -174,6 +174,44 @@ seer_status seer_gate_select(const seer_shape* shape, const void* q, const float
                              double* scores, int32_t* sel_idx, int32_t* sel_cnt,
                              hipStream_t stream);
 
+/* Weights of the learned gate network, one set per KV head (device memory).
+ * hidden must be 256.
+ *   w1       int8  [Hkv][256][d]   first layer, row m = hidden unit m
+ *   w1_scale float [Hkv][256]      row scales: the weight is w1_scale[m] * w1[m][i]
+ *   b1       float [Hkv][256]      first-layer bias
+ *   wq       float [Hkv][256][d]   query projection (the second layer's weights)
+ * w1 must be 16-byte aligned, the float arrays 4-byte aligned. */
+typedef struct seer_gate_weights {
+  const int8_t* w1;
+  const float* w1_scale;
+  const float* b1;
+  const float* wq;
+  int32_t hidden;
+} seer_gate_weights;
+
+/* seer_learned_gate_select -- gate scores from a learned gate network, then
+ * the selection rule of seer_gate_select.
+ *
+ *  The network has the shape of the gate of "Sparse Attention Reasoning"
+ *  (Step 1: Linear(d, 256), ReLU, then a 256-wide second layer) applied to
+ *  every block's pooled key; its second layer's weights are a projection of
+ *  the group's query, so that the decode query is used unpooled
+ *  ("SeerAttention-R", Abstract).  For KV head g of sequence b, block j:
+ *    alpha_j = max_i |P_ji| / 127 (fp32; 1 for an all-zero block),
+ *    q8_ji   = P_ji / alpha_j rounded to the nearest integer, ties to even,
+ *    z_jm    = alpha_j * w1_scale[m] * (w1[m] . q8_j) + b1[m],
+ *    s_j     = sum_m u_m * max(z_jm, 0) / 16,  u_m = wq[m] . qbar,
+ *  qbar the sum of the group's query heads.  The int8 products are exact;
+ *  everything else is fp64.  scores (fp64), sel_idx, sel_cnt, lens, k_max and
+ *  the rule are as in seer_gate_select; a unified rule is
+ *  SEER_ERR_UNSUPPORTED, so are hidden != 256 and tables that need more LDS
+ *  than one workgroup has.  Missing or misaligned weights:
+ *  SEER_ERR_INVALID_ARG. */
+seer_status seer_learned_gate_select(const seer_shape* shape, const void* q, const float* pooled,
+                                     const int32_t* lens, const seer_gate_weights* weights,
+                                     const seer_select* rule, int32_t k_max, double* scores,
+                                     int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
+
 /* Bytes of workspace seer_sparse_decode needs for this shape on the current
  * device (it depends on the device's compute-unit count). */
 seer_status seer_sparse_decode_workspace_size(const seer_shape* shape, size_t* bytes);

@@ -152,3 +152,20 @@ def test_alignment_validation(lib):
     assert st == seer.SEER_ERR_WORKSPACE and b"aligned" in lib.seer_last_error()
     st = lib.seer_sparse_decode_combine(ctypes.byref(sh), FAKE, None, odd, 1 << 20, None)
     assert st == seer.SEER_ERR_WORKSPACE and b"aligned" in lib.seer_last_error()
+
+
+def test_learned_gate_validation(lib):
+    sh = _shape()
+    sel = seer.make_select(keep=(1, 10))
+    w = seer.GateWeightsC(FAKE, FAKE, FAKE, FAKE, 256)
+    args = lambda wp, r: (ctypes.byref(sh), FAKE, FAKE, FAKE, wp, ctypes.byref(r), 10, FAKE,
+                          FAKE, FAKE, None)
+    assert lib.seer_learned_gate_select(*args(None, sel)) == seer.SEER_ERR_INVALID_ARG
+    missing = seer.GateWeightsC(FAKE, None, FAKE, FAKE, 256)
+    assert lib.seer_learned_gate_select(*args(ctypes.byref(missing), sel)) == seer.SEER_ERR_INVALID_ARG
+    odd = seer.GateWeightsC(ctypes.c_void_p(0x1004), FAKE, FAKE, FAKE, 256)
+    assert lib.seer_learned_gate_select(*args(ctypes.byref(odd), sel)) == seer.SEER_ERR_INVALID_ARG
+    wide = seer.GateWeightsC(FAKE, FAKE, FAKE, FAKE, 128)
+    assert lib.seer_learned_gate_select(*args(ctypes.byref(wide), sel)) == seer.SEER_ERR_UNSUPPORTED
+    uni = seer.make_select(keep=(1, 10), unified=True)
+    assert lib.seer_learned_gate_select(*args(ctypes.byref(w), uni)) == seer.SEER_ERR_UNSUPPORTED
