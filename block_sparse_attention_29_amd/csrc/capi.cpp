@@ -292,10 +292,10 @@ seer_status seer_learned_gate_select(const seer_shape* shape, const void* q, con
   if (st) return st;
   if (!weights || !weights->w1 || !weights->w1_scale || !weights->b1 || !weights->wq)
     return fail(SEER_ERR_INVALID_ARG, "gate weights missing");
-  if (!aligned16(weights->w1) || ((uintptr_t)weights->w1_scale & 3) ||
-      ((uintptr_t)weights->b1 & 3) || ((uintptr_t)weights->wq & 3))
+  if (!aligned16(weights->w1) || !aligned16(weights->wq) || ((uintptr_t)weights->w1_scale & 3) ||
+      ((uintptr_t)weights->b1 & 3))
     return fail(SEER_ERR_INVALID_ARG,
-                "gate weights misaligned (w1 16-byte aligned, the float arrays 4-byte)");
+                "gate weights misaligned (w1 and wq 16-byte aligned, w1_scale and b1 4-byte)");
   if (weights->hidden != seer::kGateHidden)
     return fail(SEER_ERR_UNSUPPORTED, "gate hidden width %d != %d", weights->hidden,
                 seer::kGateHidden);

@@ -209,18 +209,21 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
 // ReLU, Linear(256, 1)) on each block's pooled key, with the second layer's
 // weights a projection of the group's query so that the decode query stays
 // unpooled ("SeerAttention-R", Abstract):
-//   z_jm = alpha_j * beta_m * (W1_m . q8_j) + b1_m,  s_j = sum_m u_m relu(z_jm) / 16,
+//   z_jm = 2^e_j * beta_m * (W1_m . q8_j) + b1_m,  s_j = sum_m u_m relu(z_jm) / 16,
 //   u_m = Wq_m . qbar (fp64),
-// where q8_j = round-half-even(P_j / alpha_j) (fp32 quotient) and
-// alpha_j = max_i |P_ji| / 127 (fp32; 1 for an all-zero block) is the block's
-// int8 image and W1 is int8 with fp32 row scales beta.  The first layer is
-// an exact int32 product on int8 MFMA (v_mfma_i32_16x16x64_i8: A = W1 rows,
-// B = int8 blocks, both operands with the same lane -> k assignment, so the
-// dot products are exact whatever the hardware's k order); the rest is fp64
-// (alpha * beta is exact in fp64).  One 1024-thread workgroup per unit:
-// wave w owns hidden units 16w .. 16w + 15 and every block tile of a chunk
-// of 128 blocks; a score is summed over the wave's units, then over the 16
-// waves in order.  The selection rule and outputs are the gate kernel's.
+// where q8_j = round-half-even(P_j / 2^e_j) is the block's int8 image, e_j the
+// smallest exponent with 127 * 2^e_j >= max_i |P_ji| (a shared power-of-two
+// block scale: the scaling is exact), and W1 is int8 with fp32 row scales
+// beta.  The first layer is an exact int32 product on int8 MFMA
+// (v_mfma_i32_16x16x64_i8: A = W1 rows, B = int8 blocks, both operands with
+// the same lane -> k assignment, so the dot products are exact whatever the
+// hardware's k order); the rest is fp64 (2^e * beta is exact).  One
+// 1024-thread workgroup per unit: wave w owns hidden units 16w .. 16w + 15
+// and every block tile of a chunk of 128 blocks; a score is summed over the
+// wave's units, then over the 16 waves in order.  Every global load that does
+// not wait on another is issued at entry, and a chunk's pooled loads go out
+// while the previous chunk is being scored.  The selection rule and outputs
+// are the gate kernel's.
 
 constexpr int kLgThreads = 1024;  // 16 waves x 16 hidden units = 256
 constexpr int kLgChunk = 128;     // blocks quantised and scored per pass
@@ -234,6 +237,8 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
   constexpr int PD = D + kLgPad;             // LDS row pitch of int8 rows
   constexpr int TPB = kLgThreads / JC;       // quantisation threads per block
   constexpr int DQ = D / TPB;                // dimensions per quantisation thread
+  constexpr int WPL = D / 16;                // Wq floats per lane (16 lanes, one DPP row, per row)
+  constexpr int RPP = 4;                     // Wq rows per pass of a wave
   static_assert(H == 16 * NW, "one wave per 16 hidden units");
   static_assert(DQ == 8 || DQ == 16, "8 or 16 int8 per quantisation thread");
   extern __shared__ uint64_t s_key[];               // [NB] order keys of the scores
@@ -242,19 +247,36 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
   __shared__ double s_red[NW][JC];                  // per-wave sums of the chunk's scores
   __shared__ double s_u[H];
   __shared__ double s_q[D];
-  __shared__ float s_beta[H], s_b1[H], s_alpha[JC];
-  __shared__ float s_amx[TPB][JC];
+  __shared__ float s_beta[H], s_b1[H], s_amx[TPB][JC];
+  __shared__ int s_exp[JC];
   __shared__ int s_hist[3 * 256];
   __shared__ int s_scan[NW + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane >> 4, n16 = lane & 15;
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
-  const int n = seq_blocks(a.lens[b], a.S, a.NB);
   const int G = a.Hq / a.Hkv;
   const int NB = a.NB;
+  const int jl = tid % JC, part = tid / JC;  // quantisation: block jl of a chunk, dims part*DQ ..
 
-  // ---- the KV head's weights into LDS; the group-summed query (fp64, head order) ----
+  // ---- loads that wait on nothing: the first chunk's pooled columns (clamped
+  // to the table, masked once the length is known), Wq rows, W1, scales, query ----
+  const float* pcol = a.pooled + ((int64_t)u * D + part * DQ) * NB;
+  float x[DQ];
+  auto load_chunk = [&](int j0) {
+    const float* c = pcol + min(j0 + jl, NB - 1);
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) x[i] = c[(int64_t)i * NB];
+  };
+  load_chunk(0);
+  float4 wq4[16 / RPP][WPL / 4];
+  const int lr = lane & 15, rp = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 16 / RPP; ++r)
+#pragma unroll
+    for (int c = 0; c < WPL / 4; ++c)
+      wq4[r][c] = *(const float4*)(a.wq + ((int64_t)g * H + wv * 16 + r * RPP + rp) * D +
+                                   WPL * lr + 4 * c);
   const int8_t* w1g = a.w1 + (int64_t)g * H * D;
   for (int o = tid * 16; o < H * D; o += kLgThreads * 16)
     *(int4*)(s_w1 + (o / D) * PD + o % D) = *(const int4*)(w1g + o);
@@ -262,7 +284,8 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     s_beta[tid] = a.w1_scale[(int64_t)g * H + tid];
     s_b1[tid] = a.b1[(int64_t)g * H + tid];
   }
-  if (tid < D) {
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  if (tid < D) {  // the group-summed query, fp64, head order
     const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
     double sq = load_as_double<T>(q, tid);
     for (int h = 1; h < G; ++h) sq = sq + load_as_double<T>(q, (int64_t)h * D + tid);
@@ -270,15 +293,22 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
   }
   __syncthreads();
 
-  // ---- u = Wq qbar: four threads per hidden unit, D/4 dimensions each ----
-  {
-    const int m = tid >> 2, qp = tid & 3;
-    const float* wr = a.wq + ((int64_t)g * H + m) * D + qp * (D / 4);
+  // ---- u = Wq qbar: one 16-lane row per Wq row, D/16 dimensions per lane
+  // (an fp64 chain), then a DPP sum over the row ----
+#pragma unroll
+  for (int r = 0; r < 16 / RPP; ++r) {
     double c = 0.0;
-#pragma unroll 8
-    for (int i = 0; i < D / 4; ++i) c = fma((double)wr[i], s_q[qp * (D / 4) + i], c);
-    c = quad_sum_f64(c);
-    if (qp == 0) s_u[m] = c;
+#pragma unroll
+    for (int cc = 0; cc < WPL / 4; ++cc) {
+      const float4 w4 = wq4[r][cc];
+      const double* qv = s_q + WPL * lr + 4 * cc;
+      c = fma((double)w4.x, qv[0], c);
+      c = fma((double)w4.y, qv[1], c);
+      c = fma((double)w4.z, qv[2], c);
+      c = fma((double)w4.w, qv[3], c);
+    }
+    c = row_sum16_f64(c);
+    if (lr == 0) s_u[wv * 16 + r * RPP + rp] = c;
   }
   __syncthreads();
 
@@ -298,17 +328,13 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     wa[st] = *(const i32x4*)(s_w1 + (wv * 16 + n16) * PD + st * 64 + r16 * 16);
 
   for (int j0 = 0; j0 < n; j0 += JC) {
-    // ---- int8 image of blocks j0 .. j0 + JC - 1 (thread: block jl, dims part*DQ ..) ----
+    // ---- int8 image of blocks j0 .. j0 + JC - 1 ----
     {
-      const int jl = tid % JC, part = tid / JC, j = j0 + jl;
-      const bool live = j < n;
-      const float* col = a.pooled + ((int64_t)u * D + part * DQ) * NB + min(j, n - 1);
-      float x[DQ];
+      const bool live = j0 + jl < n;
       float mx = 0.f;
 #pragma unroll
       for (int i = 0; i < DQ; ++i) {
-        const float v = col[(int64_t)i * NB];  // clamped column: in bounds
-        x[i] = live ? v : 0.f;
+        x[i] = live ? x[i] : 0.f;
         mx = fmaxf(mx, fabsf(x[i]));
       }
       s_amx[part][jl] = mx;
@@ -316,23 +342,26 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
       float amax = 0.f;
 #pragma unroll
       for (int p = 0; p < TPB; ++p) amax = fmaxf(amax, s_amx[p][jl]);
-      const float alpha = amax > 0.f ? amax / 127.f : 1.f;  // IEEE division
+      int k2;
+      const float f = frexpf(amax, &k2);  // amax = f * 2^k2, 0.5 <= f < 1
+      const int e = amax > 0.f ? (f <= 127.f / 128.f ? k2 - 7 : k2 - 6) : 0;
       uint32_t w[DQ / 4];
 #pragma unroll
       for (int i = 0; i < DQ / 4; ++i) {
         uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qv = (int)rintf(x[4 * i + e] / alpha);  // |qv| <= 127
-          word |= (uint32_t)(qv & 0xFF) << (8 * e);
+        for (int c = 0; c < 4; ++c) {
+          const int qv = (int)rintf(ldexpf(x[4 * i + c], -e));  // exact scaling, |qv| <= 127
+          word |= (uint32_t)(qv & 0xFF) << (8 * c);
         }
         w[i] = word;
       }
       int8_t* dst = s_pq + jl * PD + part * DQ;
       if constexpr (DQ == 16) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
       else *(uint2*)dst = make_uint2(w[0], w[1]);
-      if (part == 0) s_alpha[jl] = alpha;
+      if (part == 0) s_exp[jl] = e;
     }
+    if (j0 + JC < n) load_chunk(j0 + JC);  // the next chunk's loads fly while this one is scored
     __syncthreads();
 
     // ---- first layer on MFMA, the rest in fp64 ----
@@ -344,16 +373,15 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
         const i32x4 pb = *(const i32x4*)(s_pq + (jt * 16 + n16) * PD + st * 64 + r16 * 16);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[st], pb, acc, 0, 0, 0);
       }
-      // lane (r16, n16) holds z's integer part for units 16 wv + 4 r16 + i, block jt*16 + n16
-      const double al = (double)s_alpha[jt * 16 + n16];
+      // lane (r16, n16) holds the products of units 16 wv + 4 r16 + i with block jt*16 + n16
+      const int e = s_exp[jt * 16 + n16];
       double sc = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double z = fma(al * betam[i], (double)acc[i], bm[i]);
+        const double z = fma(ldexp(betam[i], e), (double)acc[i], bm[i]);
         sc = fma(um[i], fmax(z, 0.0), sc);
       }
-      sc = sc + __shfl_xor(sc, 16, 64);  // row groups 0+1 and 2+3
-      sc = sc + __shfl_xor(sc, 32, 64);  // then the two pairs
+      sc = cross_row_sum_f64(sc);  // the four row groups: units 16 wv .. 16 wv + 15
       if (r16 == 0) s_red[wv][jt * 16 + n16] = sc;
     }
     __syncthreads();

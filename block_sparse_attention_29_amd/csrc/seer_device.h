@@ -72,17 +72,38 @@ __device__ __forceinline__ float row_sum16(float x) {
 // fp64 through two 32-bit DPP moves.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
-  const long long b = __double_as_longlong(x);
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
   const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)((uint64_t)b >> 32), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
-// ((x0 + x1) + (x2 + x3)) over the four lanes of a quad, in every lane of it
-// (IEEE addition commutes, so all four compute the same bits).
-__device__ __forceinline__ double quad_sum_f64(double x) {
+// Sum over the 16 lanes of a row, pairs first (lanes i, i^1), then quads,
+// eights and the row; IEEE addition commutes, so every lane gets the same bits.
+__device__ __forceinline__ double row_sum16_f64(double x) {
   x = x + dpp_f64<kDppQuadXor1>(x);
-  return x + dpp_f64<kDppQuadXor2>(x);
+  x = x + dpp_f64<kDppQuadXor2>(x);
+  x = x + dpp_f64<kDppRowHalfMirror>(x);
+  return x + dpp_f64<kDppRowMirror>(x);
+}
+
+// Sum over the four rows of the wave, (r0 + r1) + (r2 + r3), in every lane:
+// v_permlane16_swap with both operands x leaves rows (0,0,2,2) in the first
+// result and (1,1,3,3) in the second; v_permlane32_swap then pairs the halves.
+__device__ __forceinline__ double cross_row_sum_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  auto mk = [](uint32_t l, uint32_t h) {
+    return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+  };
+  const double y = mk(l16[0], h16[0]) + mk(l16[1], h16[1]);
+  const uint64_t c = (uint64_t)__double_as_longlong(y);
+  const uint32_t clo = (uint32_t)c, chi = (uint32_t)(c >> 32);
+  const auto l32 = __builtin_amdgcn_permlane32_swap(clo, clo, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(chi, chi, false, false);
+  return mk(l32[0], h32[0]) + mk(l32[1], h32[1]);
 }
 
 __device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }

@@ -180,7 +180,7 @@ seer_status seer_gate_select(const seer_shape* shape, const void* q, const float
  *   w1_scale float [Hkv][256]      row scales: the weight is w1_scale[m] * w1[m][i]
  *   b1       float [Hkv][256]      first-layer bias
  *   wq       float [Hkv][256][d]   query projection (the second layer's weights)
- * w1 must be 16-byte aligned, the float arrays 4-byte aligned. */
+ * w1 and wq must be 16-byte aligned, w1_scale and b1 4-byte aligned. */
 typedef struct seer_gate_weights {
   const int8_t* w1;
   const float* w1_scale;
@@ -197,7 +197,8 @@ typedef struct seer_gate_weights {
  *  every block's pooled key; its second layer's weights are a projection of
  *  the group's query, so that the decode query is used unpooled
  *  ("SeerAttention-R", Abstract).  For KV head g of sequence b, block j:
- *    alpha_j = max_i |P_ji| / 127 (fp32; 1 for an all-zero block),
+ *    alpha_j = 2^e_j, e_j the smallest integer with 127 * 2^e_j >= max_i |P_ji|
+ *              (e_j = 0 for an all-zero block): a power-of-two block scale,
  *    q8_ji   = P_ji / alpha_j rounded to the nearest integer, ties to even,
  *    z_jm    = alpha_j * w1_scale[m] * (w1[m] . q8_j) + b1[m],
  *    s_j     = sum_m u_m * max(z_jm, 0) / 16,  u_m = wq[m] . qbar,

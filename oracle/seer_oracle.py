@@ -236,16 +236,19 @@ GATE_HIDDEN = 256  # hidden width of the gate network ("Sparse Attention Reasoni
 def quantize_blocks(pooled32: np.ndarray):
     """Per-block int8 image of the stored pooled keys, the learned gate's input.
 
-    pooled32: (n, d) float32.  Returns (q8 (n, d) int8, alpha (n,) float32):
-    alpha_j = max_i |P_ji| / 127 and q8_ji = P_ji / alpha_j rounded to the
-    nearest integer, ties to even, both quotients taken in fp32 (correctly
-    rounded); an all-zero block has alpha_j = 1.
+    pooled32: (n, d) float32.  Returns (q8 (n, d) int8, alpha (n,) float64):
+    alpha_j = 2^e_j with e_j the smallest integer such that
+    127 * 2^e_j >= max_i |P_ji| (e_j = 0 for an all-zero block), and
+    q8_ji = P_ji / alpha_j rounded to the nearest integer, ties to even.  A
+    power-of-two block scale (a shared exponent) makes the scaling exact.
     """
     p = np.asarray(pooled32, dtype=np.float32)
     amax = np.max(np.abs(p), axis=1)
-    alpha = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
-    q = np.rint(p / alpha[:, None]).astype(np.int8)
-    return q, alpha
+    f, k = np.frexp(amax)                        # amax = f * 2^k, 0.5 <= f < 1
+    e = np.where(f <= np.float32(127.0 / 128.0), k - 7, k - 6)
+    e = np.where(amax > 0, e, 0).astype(np.int64)
+    q = np.rint(p.astype(np.float64) * np.ldexp(1.0, -e)[:, None]).astype(np.int8)
+    return q, np.ldexp(1.0, e)
 
 
 def learned_gate_scores(q_group: np.ndarray, pooled32: np.ndarray, w1: np.ndarray,
@@ -263,12 +266,13 @@ def learned_gate_scores(q_group: np.ndarray, pooled32: np.ndarray, w1: np.ndarra
 
     with (q8, alpha) = quantize_blocks(pooled32), W1 (H, d) int8 with row
     scales beta = w1_scale (H,) float32, b1 (H,) float32, Wq (H, d) float32,
-    q_group (G, d) float64.  The int8 dot products are exact integers; the
-    rest is fp64 on the exact values.
+    q_group (G, d) float64.  The int8 dot products are exact integers and
+    alpha * beta is exact (a power of two times an fp32 value); the rest is
+    fp64 on the exact values.
     """
     q8, alpha = quantize_blocks(pooled32)
     dots = q8.astype(np.int64) @ np.asarray(w1, dtype=np.int64).T          # (n, H), exact
-    scale = alpha.astype(np.float64)[:, None] * np.asarray(w1_scale, dtype=np.float64)[None, :]
+    scale = alpha[:, None] * np.asarray(w1_scale, dtype=np.float64)[None, :]
     z = scale * dots.astype(np.float64) + np.asarray(b1, dtype=np.float64)[None, :]
     h = np.maximum(z, 0.0)
     qbar = np.asarray(q_group, dtype=np.float64).sum(axis=0)
