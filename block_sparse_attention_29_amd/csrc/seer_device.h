@@ -106,6 +106,25 @@ __device__ __forceinline__ double cross_row_sum_f64(double x) {
   return mk(l32[0], h32[0]) + mk(l32[1], h32[1]);
 }
 
+// The same over fp32: (r0 + r1) + (r2 + r3) of the four rows, in every lane.
+__device__ __forceinline__ float cross_row_sum_f32(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float y = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t c = __float_as_uint(y);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+// x + x of the lane 32 apart (lower half + upper half), in every lane.
+__device__ __forceinline__ float cross_half_sum_f32(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8, lane i of a row reads lane i ^ 8
+
 __device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));

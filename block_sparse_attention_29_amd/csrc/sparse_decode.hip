@@ -671,9 +671,12 @@ void decode_partial_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
+        // the lanes holding the same V columns: i, i ^ 8 (8 lanes per row),
+        // then the other rows (VALU swaps, no LDS round trip)
         float x = acc[h][e];
-#pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+        if constexpr (LPR == 8) x = x + dpp_f32<kDppRowRor8>(x);
+        if constexpr (LPR <= 16) x = cross_row_sum_f32(x);
+        else x = cross_half_sum_f32(x);
         acc[h][e] = x;
       }
     float* rec = a.part + (int64_t)(u + w) * REC;
