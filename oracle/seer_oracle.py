@@ -327,6 +327,53 @@ def attend_masked(q_head: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# Several new query tokens per sequence (speculative or chunked decode)
+# --------------------------------------------------------------------------
+
+def gate_scores_tokens(q_tokens: np.ndarray, pooled: np.ndarray, head_dim: int) -> np.ndarray:
+    """Gate scores shared by the T new query tokens of one KV head: the query
+    summed over the tokens and the group's heads (token-major),
+    s_j = sum_t sum_h q_{t,h} . P_j / sqrt(d).
+
+    q_tokens: (T, G, d) float64; pooled: (n, d).  The query tokens are pooled
+    for the gate only, as SeerAttention pools queries before "-R" removes the
+    pooling for single-token decoding ("SeerAttention-R", Abstract).
+    """
+    p = np.asarray(pooled, dtype=np.float64)
+    s = np.zeros(p.shape[0], dtype=np.float64)
+    for t in range(q_tokens.shape[0]):
+        for h in range(q_tokens.shape[1]):
+            s = s + p @ q_tokens[t, h]
+    return s / np.sqrt(float(head_dim))
+
+
+def attend_tokens(q_tokens: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                  sel: Sequence[int], length: int, block_size: int,
+                  scale: Optional[float] = None):
+    """Causal attention of T new tokens over the kept blocks of one KV head.
+
+    The new tokens sit at positions length-T .. length-1 (their keys and
+    values are in the cache); token t sees the kept positions p <= length-T+t
+    ("Sparse Attention Reasoning", Step 4, with query_len = T and the causal
+    mask of autoregressive decoding).  q_tokens: (T, G, d).  Returns out
+    (T, G, d) and lse (T, G); a token that sees no key gets 0 and -inf.
+    """
+    T, G, d = q_tokens.shape
+    toks = selected_tokens(sel, length, block_size)
+    out = np.zeros((T, G, d))
+    lse = np.full((T, G), -np.inf)
+    for t in range(T):
+        vis = toks[toks <= length - T + t]
+        if len(vis) == 0:
+            continue
+        for h in range(G):
+            o, l, _ = attend(q_tokens[t, h], keys, values, vis, scale)
+            out[t, h] = o
+            lse[t, h] = l
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # Paged caches
 # --------------------------------------------------------------------------
 

@@ -534,3 +534,70 @@ def test_learned_gate_reduces_to_the_linear_gate():
     lin = O.gate_scores(w[None, :], deq, d) * math.sqrt(d) / math.sqrt(H)
     assert np.allclose(s - c, lin, rtol=0, atol=1e-9 * (abs(c) + np.abs(lin).max()))
     assert not np.allclose(lin, 0.0)
+
+
+# ---------------------------------------------------------------- several query tokens
+
+def test_gate_scores_tokens_reduce_to_the_head_sum():
+    rng = np.random.default_rng(21)
+    q = rng.normal(size=(3, 4, 64))
+    p = rng.normal(size=(30, 64)).astype(np.float32)
+    s = O.gate_scores_tokens(q, p, 64)
+    # the T x G query rows act as T*G heads of one group (same order of addition)
+    assert np.array_equal(s, O.gate_scores(q.reshape(12, 64), p, 64))
+    assert np.array_equal(O.gate_scores_tokens(q[:1], p, 64), O.gate_scores(q[0], p, 64))
+    assert np.array_equal(O.gate_scores_tokens(2.0 * q, p, 64), 2.0 * s)
+
+
+def test_attend_tokens_single_token_and_causal_truncation():
+    rng = np.random.default_rng(22)
+    S, d, L, T, G = 16, 32, 150, 5, 3
+    k = rng.normal(size=(L, d))
+    v = rng.normal(size=(L, d))
+    q = rng.normal(size=(T, G, d))
+    sel = [0, 3, 7, 8, 9]
+    out, lse = O.attend_tokens(q, k, v, sel, L, S)
+    # T = 1 is the single-token decode
+    o1, l1 = O.attend_tokens(q[-1:], k, v, sel, L, S)
+    toks = O.selected_tokens(sel, L, S)
+    for h in range(G):
+        o, l, _ = O.attend(q[-1, h], k, v, toks)
+        assert np.allclose(o1[0, h], o) and np.isclose(l1[0, h], l)
+    # token t is the single-token decode of the sequence cut after its own position
+    for t in range(T):
+        cut = O.selected_tokens(sel, L - T + 1 + t, S)
+        for h in range(G):
+            o, l, _ = O.attend(q[t, h], k, v, cut)
+            assert np.allclose(out[t, h], o, rtol=0, atol=1e-12) and np.isclose(lse[t, h], l)
+
+
+def test_attend_tokens_equals_the_causal_masked_form():
+    """The gather form against softmax over every key with a -inf mask that is
+    block-selected AND causal (the mask form of the pages' Step 4)."""
+    rng = np.random.default_rng(23)
+    S, d, L, T, G = 8, 16, 61, 4, 2
+    k = rng.normal(size=(L, d))
+    v = rng.normal(size=(L, d))
+    q = rng.normal(size=(T, G, d))
+    sel = [1, 5, 7]                            # block 7 holds the last tokens 56..60
+    out, lse = O.attend_tokens(q, k, v, sel, L, S)
+    pos = np.arange(L)
+    for t in range(T):
+        mask = np.isin(pos // S, sel) & (pos <= L - T + t)
+        for h in range(G):
+            o, l = O.attend_masked(q[t, h], k, v, mask)
+            assert np.allclose(out[t, h], o, rtol=0, atol=1e-12) and np.isclose(lse[t, h], l)
+
+
+def test_attend_tokens_nothing_visible():
+    """A token whose kept blocks all lie after it sees nothing: 0 and -inf."""
+    rng = np.random.default_rng(24)
+    S, d, L, T = 8, 8, 20, 3                   # tokens at 17, 18, 19; block 2 = 16..19
+    k = rng.normal(size=(L, d))
+    v = rng.normal(size=(L, d))
+    q = rng.normal(size=(T, 1, d))
+    out, lse = O.attend_tokens(q, k, v, [2], L, S)
+    assert np.all(np.isfinite(lse))            # block 2 starts at 16 <= 17
+    out, lse = O.attend_tokens(q, k, v, [2], 17, S)   # tokens at 14, 15, 16
+    assert lse[0, 0] == -np.inf and lse[1, 0] == -np.inf and np.isfinite(lse[2, 0])
+    assert np.all(out[0] == 0.0) and np.all(out[1] == 0.0)

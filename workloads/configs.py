@@ -38,6 +38,7 @@ class Workload:
     planted_fraction: Optional[Tuple[int, int]] = None    # share of blocks planted
     heavy_tailed_keys: bool = False                       # Student-t(3) keys
     decode_steps: int = 0                                 # >0: an incremental decode loop
+    query_tokens: int = 1                                 # new query tokens per sequence
     seed: int = 0
 
     @property
@@ -92,6 +93,11 @@ WORKLOADS = {
     "long_131k": Workload("long_131k", batch=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
                           block_size=128, dtype="bf16", context=131072, keep=(1, 20),
                           heavy_tailed_keys=True, decode_steps=256, seed=29005),
+    # sparse90_32k with 4 new query tokens per sequence (speculative or chunked
+    # decode): 16 query rows per KV head, one selection for the 4 tokens.
+    "spec4_32k": Workload("spec4_32k", batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          block_size=128, dtype="bf16", context=32768, keep=(1, 10),
+                          query_tokens=4, seed=29006),
 }
 
 

@@ -4,7 +4,9 @@ Everything is drawn with one ``torch.Generator`` seeded with the workload's
 seed, on the device the tensors are made on, in a fixed order:
 
 1. lengths (variable-context workloads only): ``randint(lo, hi + 1, (B,))``;
-2. the query ``q``: ``randn(B, Hq, d)`` (for a decode loop: ``randn(steps, B, Hq, d)``);
+2. the query ``q``: ``randn(B, Hq, d)`` (for a decode loop: ``randn(steps, B, Hq, d)``;
+   for T > 1 new query tokens per sequence: ``randn(B, T, Hq, d)``, token t at
+   position length - T + t);
 3. the keys, one (sequence, KV head) slice at a time in (b, g) order: the
    filled rows ``randn(rows, d)``, or Student-t(3) as
    ``z0 / sqrt((z1^2 + z2^2 + z3^2) / 3)`` from four normal slices drawn in the
@@ -44,7 +46,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 @dataclasses.dataclass
 class Case:
     wl: Workload
-    q: torch.Tensor                    # [B][Hq][d]  or [steps][B][Hq][d]
+    q: torch.Tensor                    # [B][Hq][d], [steps][B][Hq][d] or [B][T][Hq][d]
     k: torch.Tensor                    # contiguous [B][Hkv][T][d] or pool [P][Hkv][S][d]
     v: torch.Tensor
     lens: torch.Tensor                 # int32 [B]: tokens in the cache incl. the new one
@@ -93,13 +95,15 @@ def make_case(wl: Workload, device="cpu", poison: bool = False) -> Case:
     fill = lens + wl.decode_steps
 
     # 2. query
-    qshape = (wl.decode_steps, B, Hq, d) if wl.decode_steps else (B, Hq, d)
+    Tq = wl.query_tokens
+    qshape = ((wl.decode_steps, B, Hq, d) if wl.decode_steps
+              else (B, Tq, Hq, d) if Tq > 1 else (B, Hq, d))
     q = _normal(g, qshape, device).to(dt)
 
     # Direction used to plant blocks: the group's summed query, normalised.
     plant_dir = None
     if wl.planted_fraction is not None:
-        qs = q.float().view(B, Hkv, G, d).sum(dim=2)
+        qs = q.float().reshape(B, Tq, Hkv, G, d).sum(dim=(1, 3))
         plant_dir = qs / qs.norm(dim=-1, keepdim=True)
 
     nblk = [-(-int(x) // S) for x in lens.tolist()]
