@@ -37,8 +37,12 @@ gate but give no weights or internals):
   gate network (Linear(d, 256), ReLU, then a 256-wide second layer whose
   weights are a projection of the query, so the query stays unpooled); its
   weights are given (seeded, untrained), stored int8 with per-row scales, and
-  its input is a per-block int8 image of the pooled keys, so that the first
-  layer is an exact integer product.
+  its input is a per-block int8 image of the pooled keys with a power-of-two
+  block scale, so that the first layer is an exact integer product;
+* several new query tokens per sequence (T, speculative or chunked decode):
+  token t sits at position length-T+t and sees the kept positions up to its
+  own (causal), and one selection per KV head serves all T tokens, scored
+  with the query summed over the tokens and the group's heads.
 
 Every function works on one (sequence, KV head) unless its name says otherwise.
 Inputs are float64 arrays holding the exact values of the stored tensors.
