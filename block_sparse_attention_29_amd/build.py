@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libseer.so")
 
-SOURCES = ["capi.cpp", "pool_keys.hip", "gate_topk.hip", "sparse_decode.hip"]
+SOURCES = ["capi.cpp", "pool_keys.hip", "gate_topk.hip", "sparse_decode.hip", "multi_decode.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -212,9 +212,20 @@ seer::GateArgs gate_args(const seer_shape* shape, const void* q, const float* po
   a.force_first = rule->force_first != 0;
   a.force_last = rule->force_last != 0;
   a.unified = rule->unified != 0;
+  a.tokens = 1;
   return a;
 }
 
+
+// Token count of a multi-token call.
+seer_status check_tokens(const seer_shape* shape, int32_t tokens) {
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (tokens < 1) return fail(SEER_ERR_INVALID_ARG, "tokens %d < 1", tokens);
+  if ((int64_t)G * tokens > seer::kMultiRows)
+    return fail(SEER_ERR_UNSUPPORTED, "G * tokens = %lld > %d query rows per KV head",
+                (long long)G * tokens, seer::kMultiRows);
+  return SEER_OK;
+}
 
 }  // namespace
 
@@ -442,6 +453,73 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
   c.lse = lse;
   const hipError_t e = seer::launch_decode_combine(c, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
+  return ok();
+}
+
+seer_status seer_multi_gate_select(const seer_shape* shape, int32_t tokens, const void* q,
+                                   const float* pooled, const int32_t* lens,
+                                   const seer_select* rule, int32_t k_max, double* scores,
+                                   int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
+  seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
+  seer::GateArgs a = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  a.tokens = tokens;
+  if (seer::gate_smem_bytes(a.NB, k_max) > max_block_smem())
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
+  const hipError_t e = seer::launch_gate_topk(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "gate_topk launch");
+  return ok();
+}
+
+seer_status seer_multi_sparse_decode_workspace_size(const seer_shape* shape, int32_t tokens,
+                                                    size_t* bytes) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
+  if (!bytes) return fail(SEER_ERR_INVALID_ARG, "bytes is NULL");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  *bytes = seer::decode_multi_workspace_bytes(shape->batch, shape->num_kv_heads, shape->head_dim,
+                                              wmax);
+  return ok();
+}
+
+seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, const void* q,
+                                     const seer_kv* kv, const int32_t* lens,
+                                     const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     int32_t k_max, float softmax_scale, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
+  seer::DecodeArgs a;
+  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale, workspace,
+                           workspace_bytes, &a)))
+    return st;
+  const size_t need = seer::decode_multi_workspace_bytes(shape->batch, shape->num_kv_heads,
+                                                         shape->head_dim, wave_cap(shape));
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  a.tokens = tokens;
+  hipError_t e = seer::launch_decode_multi(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "multi decode launch");
+  seer::CombineArgs c{};
+  c.B = a.B;
+  c.Hq = a.Hq;
+  c.Hkv = a.Hkv;
+  c.D = a.D;
+  c.S = a.S;
+  c.tokens = tokens;
+  c.hdr = a.hdr;
+  c.prefix = a.prefix;
+  c.part = a.part;
+  c.out = out;
+  c.lse = lse;
+  e = seer::launch_decode_multi_combine(c, stream);
+  if (e != hipSuccess) return hip_fail(e, "multi combine launch");
   return ok();
 }
 

@@ -158,17 +158,22 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
     };
     load_pooled(jl);  // unconditional (in bounds even when n == 0)
 
-    // ---- group-summed query, fp64, head order ----
-    const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+    // ---- group-summed query, fp64, token-major then head order ----
+    const int TQ = a.tokens;
+    const T* q0 = (const T*)a.q + ((int64_t)b * TQ * a.Hq + (int64_t)g * G) * D;
     for (int i = tid; i < D; i += kTopkThreads) {
-      // All 8 possible heads are loaded (clamped to the group) before summing the
-      // first G in head order, so the loads are in flight together.
-      double x[8];
+      double sq = 0.0;
+      for (int t = 0; t < TQ; ++t) {
+        const T* q = q0 + (int64_t)t * a.Hq * D;
+        // All 8 possible heads are loaded (clamped to the group) before summing
+        // the first G in head order, so the loads are in flight together.
+        double x[8];
 #pragma unroll
-      for (int h = 0; h < 8; ++h) x[h] = load_as_double<T>(q, (int64_t)min(h, G - 1) * D + i);
-      double sq = x[0];
+        for (int h = 0; h < 8; ++h) x[h] = load_as_double<T>(q, (int64_t)min(h, G - 1) * D + i);
+        sq = t == 0 ? x[0] : sq + x[0];
 #pragma unroll
-      for (int h = 1; h < 8; ++h) sq = h < G ? sq + x[h] : sq;
+        for (int h = 1; h < 8; ++h) sq = h < G ? sq + x[h] : sq;
+      }
       s_q[i] = sq;
     }
     __syncthreads();

@@ -1,0 +1,454 @@
+// Split-KV block-sparse decode of several new query tokens per sequence
+// (speculative or chunked decode) for gfx950.
+//
+// Sequence b has T new tokens at positions L_b - T .. L_b - 1, their keys and
+// values already in the cache.  For KV head g, the G query heads of each of
+// the T tokens are one unit's R = G * T <= 16 query rows, row r = t * G + h.
+// Token t attends to the tokens of the kept blocks at positions
+// p <= L_b - T + t: "Sparse Attention Reasoning", Step 4, with query_len = T
+// and the causal mask of autoregressive decoding; one selection per
+// (sequence, KV head) serves all T tokens, so the kept K/V bytes are read
+// once for T tokens.
+//
+// The work split is the single-token kernel's (equal ranges of 32-token tiles
+// over all waves, one partial record per (unit, wave) segment, merged in wave
+// order).  Per tile a wave:
+//  * computes the 16 x 32 logits with v_mfma_f32_16x16x32_bf16 (fp32 data:
+//    v_mfma_f32_16x16x4_f32), the R query rows being the A operand;
+//  * masks each row to its token's causal limit, updates the online softmax
+//    and writes the probabilities (fp32) to a 2 KiB LDS buffer;
+//  * multiplies them with V on v_mfma_f32_16x16x4_f32 in fp32: V is loaded
+//    16 lanes per token row, so lane (r, n) holds token 4k + r, dimensions
+//    n*D/16 .. of load k, which is exactly the B operand of k-step k for
+//    column n -- output column n of dimension step e is dimension n*D/16 + e,
+//    and each lane's rows of the result are its rows of the softmax state.
+#include "decode_common.h"
+#include "select_device.h"
+
+namespace seer {
+namespace {
+
+constexpr int kRows = kMultiRows;  // MFMA rows: G * T <= 16
+
+template <typename T, int D>
+struct MGeo {
+  static constexpr int EB = sizeof(T);
+  static constexpr int ROWB = D * EB;     // bytes per token row
+  static constexpr int NKL = ROWB / 64;   // K chunks per lane per 16-token column
+  static constexpr int VB = ROWB / 16;    // V bytes per lane per token row (16 lanes a row)
+  static constexpr int DPL = D / 16;      // V dimensions per lane
+  static constexpr int NVQ = (VB + 15) / 16;  // 16-byte pieces per lane per token row
+  static constexpr int REC = kRows * D + 2 * kRows;  // record: acc[16][D], m[16], l[16]
+};
+
+// V element e (0 .. DPL-1) of a lane's token row piece, as fp32.
+template <typename T, int NVQ>
+__device__ __forceinline__ float v_elem(const uint4 (&v)[NVQ], int e);
+
+template <>
+__device__ __forceinline__ float v_elem<uint16_t, 1>(const uint4 (&v)[1], int e) {
+  return chunk_elem<uint16_t>(v[0], e);
+}
+template <>
+__device__ __forceinline__ float v_elem<float, 1>(const uint4 (&v)[1], int e) {
+  return chunk_elem<float>(v[0], e);
+}
+template <>
+__device__ __forceinline__ float v_elem<float, 2>(const uint4 (&v)[2], int e) {
+  return chunk_elem<float>(v[e >> 2], e & 3);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_multi_kernel(DecodeArgs a) {
+  using GE = MGeo<T, D>;
+  constexpr int EB = GE::EB, ROWB = GE::ROWB, NKL = GE::NKL, VB = GE::VB, DPL = GE::DPL;
+  constexpr int NVQ = GE::NVQ, REC = GE::REC;
+
+  __shared__ __align__(16) float s_p[kWavesPerWG][kTile * kRows];
+  extern __shared__ int s_dyn[];
+
+  const int U = a.B * a.Hkv;
+  const int tid = threadIdx.x;
+  const int TQ = a.tokens, G = a.Hq / a.Hkv, R = G * TQ;
+  int* s_prefix = s_dyn;                         // [U + 1]
+  int* s_scan = s_dyn + U + 1;                   // [kWavesPerWG + 1]
+  int* s_len = s_dyn + U + 1 + kWavesPerWG + 1;  // [U]
+
+  // ---- plan: block prefix over units (every workgroup computes the same) ----
+  {
+    const int per = (U + kThreads - 1) / kThreads;
+    const int u_lo = min(U, tid * per), u_hi = min(U, u_lo + per);
+    int local = 0;
+    for (int u = u_lo; u < u_hi; ++u) {
+      const int L = a.lens[u / a.Hkv];
+      int c;
+      if (a.sel_idx) {
+        c = a.sel_cnt[u];
+        c = c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
+      } else {
+        c = seq_blocks(L, a.S, a.NB);
+      }
+      s_len[u] = L;
+      s_prefix[u] = c;
+      local += c;
+    }
+    int total;
+    int base = block_excl_scan<kThreads>(local, s_scan, &total);
+    for (int u = u_lo; u < u_hi; ++u) {
+      const int c = s_prefix[u];
+      s_prefix[u] = base;
+      base += c;
+    }
+    if (tid == 0) s_prefix[U] = total;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int u = tid; u <= U; u += kThreads) a.prefix[u] = s_prefix[u];
+      if (tid == 0) a.hdr[0] = a.W;
+    }
+  }
+
+  const int lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane >> 4, n16 = lane & 15;
+  const int nwg = (int)gridDim.x;
+  const int wg = (nwg % kXcds == 0)
+      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
+      : (int)blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(wg * kWavesPerWG + wv);
+  const int tsh = 31 - __builtin_clz(a.S / kTile);
+  const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
+  const EqualSplit split(Tot, a.W);
+  const int y0 = split.start(w), y1 = split.start(w + 1);
+  if (y0 >= y1) return;
+
+  const bool sparse = a.sel_idx != nullptr;
+  const int Hkv = a.Hkv, S = a.S, NB = a.NB;
+  const char* kbase = (const char*)a.k;
+  const char* vbase = (const char*)a.v;
+  float* pw = s_p[wv];
+  const float sl = a.scale_log2;
+
+  // First unit of the range: the largest u with s_prefix[u] <= block of y0.
+  int u = 0;
+  {
+    int lo = 0, hi = U;  // s_prefix[lo] << tsh <= y0 < s_prefix[hi] << tsh
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((s_prefix[mid] << tsh) <= y0) lo = mid; else hi = mid;
+    }
+    u = __builtin_amdgcn_readfirstlane(lo);
+  }
+
+  int y = y0;
+  while (y < y1) {
+    while ((__builtin_amdgcn_readfirstlane(s_prefix[u + 1]) << tsh) <= y) ++u;
+    const int Yu = __builtin_amdgcn_readfirstlane(s_prefix[u]) << tsh;
+    const int ye = min(y1, __builtin_amdgcn_readfirstlane(s_prefix[u + 1]) << tsh);
+    const int b = u / Hkv, g = u - b * Hkv;
+    const int L = __builtin_amdgcn_readfirstlane(s_len[u]);
+
+    // Per-lane descriptors of 64 consecutive kept blocks (slots) of unit u.
+    int cs = -(1 << 30), ci_nv = 0, ci_j = 0;
+    int64_t ci_off = 0;
+    auto load_chunk = [&](int slot0) {
+      cs = slot0;
+      const int slot = slot0 + lane;
+      int nv = 0, jj = 0;
+      int64_t off = 0;
+      if (slot < s_prefix[u + 1] - s_prefix[u]) {
+        const int j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
+        if (j >= 0 && j < NB && (int64_t)j * S < L) {
+          nv = min(S, L - j * S);
+          jj = j;
+          if (a.page_table) {
+            const int pg = a.page_table[(int64_t)b * NB + j];
+            if (pg >= 0 && pg < a.num_pages) off = ((int64_t)pg * Hkv + g) * S * D;
+            else nv = 0;
+          } else {
+            off = (((int64_t)b * Hkv + g) * NB + j) * (int64_t)S * D;
+          }
+        }
+      }
+      ci_nv = nv;
+      ci_j = jj;
+      ci_off = off;
+    };
+    // Tile yt: valid tokens (by length), element offset of its rows, and the
+    // position of its first token.  Empty tiles re-read their block's last
+    // valid tile (in bounds, masked).
+    auto describe = [&](int yt, int& tv, int64_t& row0, int& tp0) {
+      const int rel = yt - Yu;
+      const int slot = rel >> tsh;
+      const int tib = rel - (slot << tsh);
+      const int li = slot - cs;
+      const int nv = readlane_i(ci_nv, li);
+      const int j = readlane_i(ci_j, li);
+      const int64_t off = readlane64(ci_off, li);
+      tv = min(kTile, max(0, nv - tib * kTile));
+      const int tl = nv > 0 ? min(tib, (nv - 1) / kTile) : 0;
+      row0 = off + (int64_t)tl * kTile * D;
+      tp0 = j * S + tib * kTile;
+    };
+
+    // Query rows as the MFMA A operand: row n16 = token n16 / G, head n16 % G;
+    // rows n16 >= R are zero (their loads are clamped and in bounds).
+    uint4 qa[NKL];
+    {
+      const int rq = min(n16, R - 1), tq = rq / G, hq = rq - tq * G;
+      const char* qr = (const char*)a.q +
+                       (((int64_t)b * TQ + tq) * a.Hq + (int64_t)g * G + hq) * ROWB + r16 * 16;
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+        const uint4 z = *(const uint4*)(qr + c * 64);
+        qa[c] = n16 < R ? z : make_uint4(0, 0, 0, 0);
+      }
+    }
+    // This lane's softmax rows 4 r16 + i: the causal limit of their token
+    // (keys at positions < lim are visible); rows past R see nothing.
+    int lim[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * r16 + i;
+      lim[i] = row < R ? L - TQ + 1 + row / G : 0;
+    }
+    float m_run[4], l_run[4];
+    f32x4 acc[DPL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = kNegInf; l_run[i] = 0.f; }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 kr[kCols][NKL];
+    uint4 vr[8][NVQ];  // token 4k + r16 of the tile, bytes n16 * VB ..
+    auto issue_k = [&](int64_t row0) {
+      const char* kb = kbase + row0 * EB;
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct)
+#pragma unroll
+        for (int c = 0; c < NKL; ++c)
+          kr[ct][c] = *(const uint4*)(kb + (ct * 16 + n16) * ROWB + c * 64 + r16 * 16);
+    };
+    auto issue_v = [&](int64_t row0) {
+      const char* vb = vbase + row0 * EB;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const char* src = vb + (4 * k + r16) * ROWB + n16 * VB;
+        if constexpr (VB == 8) {
+          const uint2 h = *(const uint2*)src;
+          vr[k][0] = make_uint4(h.x, h.y, 0u, 0u);
+        } else {
+#pragma unroll
+          for (int c = 0; c < NVQ; ++c) vr[k][c] = *(const uint4*)(src + 16 * c);
+        }
+      }
+    };
+
+    auto qk = [&](f32x4 (&sc)[kCols]) {
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct) sc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          if constexpr (EB == 2) {
+            sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                             __builtin_bit_cast(bf16x8, kr[ct][c]),
+                                                             sc[ct], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(chunk_elem<float>(qa[c], e),
+                                                            chunk_elem<float>(kr[ct][c], e),
+                                                            sc[ct], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    // Online softmax of the lane's rows 4 r16 + i over the tile's tokens
+    // ct*16 + n16; p (fp32) to LDS as [token][row]; acc rows rescaled.
+    auto softmax = [&](const f32x4 (&sc)[kCols], int tv, int tp0) {
+      float x[kCols][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tvr = min(tv, max(0, lim[i] - tp0));
+        float mx = kNegInf;
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          x[ct][i] = (ct * 16 + n16 < tvr) ? sc[ct][i] * sl : kNegInf;
+          mx = fmaxf(mx, x[ct][i]);
+        }
+        mx = row_max16(mx);
+        const float mn = fmaxf(m_run[i], mx);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        // Arguments are <= 0 (or -inf): the hardware exp2 is accurate there.
+        const float alpha = __builtin_amdgcn_exp2f(m_run[i] - mu);
+        float ps = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct) {
+          x[ct][i] = __builtin_amdgcn_exp2f(x[ct][i] - mu);
+          ps += x[ct][i];
+        }
+        l_run[i] = l_run[i] * alpha + ps;
+        m_run[i] = mn;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e][i] *= alpha;
+      }
+#pragma unroll
+      for (int ct = 0; ct < kCols; ++ct)
+        *(float4*)(pw + (ct * 16 + n16) * kRows + r16 * 4) =
+            make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // O += P V on fp32 MFMA: k-step k takes tokens 4k .. 4k + 3 (lane row
+    // group r16 = token 4k + r16); V rows past the length are zeroed (they may
+    // hold anything, even NaN).
+    auto pv = [&](int tv) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float ap = pw[(4 * k + r16) * kRows + n16];
+        const bool live = 4 * k + r16 < tv;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          const float bv = live ? v_elem<T, NVQ>(vr[k], e) : 0.f;
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, bv, acc[e], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    while (y < ye) {
+      const int slot0 = (y - Yu) >> tsh;
+      load_chunk(slot0);
+      const int yc = min(ye, Yu + ((slot0 + kWave) << tsh));
+      int tv, tp0;
+      int64_t row0;
+      describe(y, tv, row0, tp0);
+      issue_k(row0);
+      issue_v(row0);
+      for (; y < yc; ++y) {
+        int tv_n, tp_n;
+        int64_t row_n;
+        describe(min(y + 1, yc - 1), tv_n, row_n, tp_n);
+        f32x4 sc[kCols];
+        qk(sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(row_n);
+        softmax(sc, tv, tp0);
+        pv(tv);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(row_n);
+        tv = tv_n;
+        tp0 = tp_n;
+      }
+      y = yc;
+    }
+
+    // ---- segment result: partial record (u, w) at slot u + w, all 16 rows ----
+    float lt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lt[i] = row_sum16(l_run[i]);
+    float* rec = a.part + (int64_t)(u + w) * REC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* dst = rec + (4 * r16 + i) * D + n16 * DPL;
+#pragma unroll
+      for (int e = 0; e < DPL; e += 4)
+        *(float4*)(dst + e) = make_float4(acc[e][i], acc[e + 1][i], acc[e + 2][i], acc[e + 3][i]);
+    }
+    if (n16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rec[kRows * D + 4 * r16 + i] = m_run[i];
+        rec[kRows * D + kRows + 4 * r16 + i] = lt[i];
+      }
+    }
+  }
+}
+
+// Merges a unit's records row by row in wave order (a running maximum):
+//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l;
+// then out = o / l and lse = (M + log2 l) ln 2, for token t = row / G, head
+// g*G + row % G.  Empty waves and records without a valid token are skipped.
+constexpr int kMCombineThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMCombineThreads) void decode_multi_combine_kernel(CombineArgs a) {
+  constexpr int REC = MGeo<float, D>::REC;
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int U = a.B * a.Hkv, TQ = a.tokens, G = a.Hq / a.Hkv, R = G * TQ;
+  const int tsh = 31 - __builtin_clz(a.S / kTile);
+  const int W = a.hdr[0];
+  const int Tot = a.prefix[U] << tsh;
+  const int ylo = a.prefix[u] << tsh, yhi = a.prefix[u + 1] << tsh;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  auto out_index = [&](int row) {
+    const int t = row / G, h = row - t * G;
+    return ((int64_t)b * TQ + t) * a.Hq + (int64_t)g * G + h;
+  };
+  if (yhi <= ylo) {  // no tokens: out = 0, lse = -inf
+    for (int idx = tid; idx < R * D; idx += kMCombineThreads)
+      a.out[out_index(idx / D) * D + idx % D] = 0.f;
+    if (a.lse && tid < R) a.lse[out_index(tid)] = kNegInf;
+    return;
+  }
+  const int wlo = tile_owner(ylo, W, Tot), whi = tile_owner(yhi - 1, W, Tot);
+  const EqualSplit sp(Tot, W);
+  const float* part = a.part + (int64_t)(u + wlo) * REC;
+  for (int idx = tid; idx < R * D; idx += kMCombineThreads) {
+    const int row = idx / D, dim = idx - row * D;
+    float M = kNegInf, l = 0.f, o = 0.f;
+    for (int t = 0; t <= whi - wlo; ++t) {
+      if (Tot < W && wave_empty(sp, wlo + t)) continue;  // wrote no record
+      const float* r = part + (int64_t)t * REC;
+      const float mw = r[kRows * D + row];
+      if (mw == kNegInf) continue;                        // no valid token in it
+      const float mn = fmaxf(M, mw);
+      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(mw - mn);
+      o = o * sa + r[row * D + dim] * sb;
+      l = l * sa + r[kRows * D + kRows + row] * sb;
+      M = mn;
+    }
+    a.out[out_index(row) * D + dim] = l > 0.f ? o / l : 0.f;
+    if (a.lse && dim == 0)
+      a.lse[out_index(row)] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+  }
+}
+
+template <typename T, int D>
+const void* multi_fn() { return (const void*)&decode_multi_kernel<T, D>; }
+
+const void* multi_kernel(int dtype, int D) {
+  if (dtype == 1) return D == 64 ? multi_fn<uint16_t, 64>() : multi_fn<uint16_t, 128>();
+  return D == 64 ? multi_fn<float, 64>() : multi_fn<float, 128>();
+}
+
+}  // namespace
+
+size_t decode_multi_workspace_bytes(int B, int Hkv, int D, int wmax) {
+  const int U = B * Hkv;
+  return decode_part_offset(U) + (size_t)(U + wmax) * (kRows * D + 2 * kRows) * sizeof(float);
+}
+
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
+  const int U = a.B * a.Hkv;
+  DecodeArgs args = a;
+  void* params[] = {&args};
+  const size_t smem = (size_t)(2 * U + 1 + kWavesPerWG + 1) * sizeof(int);
+  return hipLaunchKernel(multi_kernel(a.dtype, a.D), dim3(a.W / kWavesPerWG), dim3(kThreads),
+                         params, smem, stream);
+}
+
+hipError_t launch_decode_multi_combine(const CombineArgs& a, hipStream_t stream) {
+  CombineArgs args = a;
+  void* params[] = {&args};
+  const void* fn = a.D == 64 ? (const void*)&decode_multi_combine_kernel<64>
+                             : (const void*)&decode_multi_combine_kernel<128>;
+  return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(kMCombineThreads), params, 0, stream);
+}
+
+}  // namespace seer

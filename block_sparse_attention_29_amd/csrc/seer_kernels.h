@@ -49,10 +49,12 @@ struct DecodeArgs {
   int32_t* sel_cnt_out;   // [B][Hkv] out
   int32_t ids_cap;        // kept ids one workgroup holds in LDS
   int32_t force_first, force_last;  // forced blocks of the fused gate's top-k
+  int32_t tokens;         // new query tokens per sequence (multi-token kernel; q [B][tokens][Hq][D])
 };
 
 struct CombineArgs {
   int32_t B, Hq, Hkv, D, S;
+  int32_t tokens;  // multi-token combine: query tokens per sequence
   const int32_t* hdr;
   const int32_t* prefix;
   const float* part;
@@ -76,6 +78,13 @@ size_t gated_decode_smem_bytes(int U, int NB, int ids_cap);
 int gated_decode_ids_cap(int U, int k_max, int W);
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 
+// Several new query tokens per sequence: G * tokens <= 16 query rows per unit,
+// partial records of 16 rows.  Selection given (or dense).
+constexpr int kMultiRows = 16;
+size_t decode_multi_workspace_bytes(int B, int Hkv, int D, int wmax);
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_multi_combine(const CombineArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- gate
 
 struct GateArgs {
@@ -93,6 +102,7 @@ struct GateArgs {
   int32_t force_first;     // keep block 0 whatever its score
   int32_t force_last;      // keep the newest block whatever its score
   int32_t unified;         // one selection per sequence from the KV heads' summed scores
+  int32_t tokens;          // query tokens per sequence, summed into the gate's query (q [B][tokens][Hq][D])
   // Learned gate (launch_learned_gate only): per KV head, w1 int8 [Hkv][256][D]
   // with row scales w1_scale [Hkv][256], b1 [Hkv][256], wq [Hkv][256][D].
   const int8_t* w1;

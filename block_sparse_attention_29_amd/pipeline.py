@@ -31,7 +31,7 @@ class DecodeState:
                  k_max: Optional[int] = None, keep: Optional[tuple] = None,
                  top_k: Optional[torch.Tensor] = None, threshold: Optional[float] = None,
                  force_first: bool = False, force_last: bool = False, unified: bool = False,
-                 gate_weights=None):
+                 gate_weights=None, query_tokens: int = 1):
         self.shape = seer.make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks, dtype)
         self.k, self.v, self.page_table = k, v, page_table
@@ -40,6 +40,10 @@ class DecodeState:
         self.top_k = top_k
         # learned gate: device tensors w1, w1_scale, b1, wq (or None: parameter-free gate)
         self.gate_weights = gate_weights
+        # new query tokens per sequence (q [B][T][Hq][d] when T > 1)
+        self.T = int(query_tokens)
+        if self.T > 1 and gate_weights is not None:
+            raise ValueError("the learned gate takes one query token per sequence")
         self.rule = seer.make_select(top_k=top_k, keep=keep, threshold=threshold,
                                      force_first=force_first, force_last=force_last,
                                      unified=unified)
@@ -57,9 +61,15 @@ class DecodeState:
         self.scores = torch.zeros(U * max_blocks, dtype=torch.float64, device=dev)
         self.sel_idx = torch.full((U, self.k_max), -1, dtype=torch.int32, device=dev)
         self.sel_cnt = torch.zeros(U, dtype=torch.int32, device=dev)
-        self.out = torch.zeros((batch, num_q_heads, head_dim), dtype=torch.float32, device=dev)
-        self.lse = torch.zeros((batch, num_q_heads), dtype=torch.float32, device=dev)
-        self.workspace = seer.alloc_workspace(self.shape, dev)
+        tok = (self.T,) if self.T > 1 else ()
+        self.out = torch.zeros((batch, *tok, num_q_heads, head_dim), dtype=torch.float32,
+                               device=dev)
+        self.lse = torch.zeros((batch, *tok, num_q_heads), dtype=torch.float32, device=dev)
+        if self.T > 1:
+            self.workspace = torch.empty(seer.multi_decode_workspace_size(self.shape, self.T),
+                                         dtype=torch.uint8, device=dev)
+        else:
+            self.workspace = seer.alloc_workspace(self.shape, dev)
 
     # pooling ---------------------------------------------------------------
     def build_pool(self, lens: torch.Tensor):
@@ -70,7 +80,10 @@ class DecodeState:
 
     # selection -------------------------------------------------------------
     def select(self, q: torch.Tensor, lens: torch.Tensor):
-        if self.gate_weights is not None:
+        if self.T > 1:
+            seer.multi_gate_select(self.shape, self.T, q, self.pooled, lens, self.rule,
+                                   self.k_max, self.scores, self.sel_idx, self.sel_cnt)
+        elif self.gate_weights is not None:
             seer.learned_gate_select(self.shape, q, self.pooled, lens, self.gate_weights,
                                      self.rule, self.k_max, self.scores, self.sel_idx,
                                      self.sel_cnt)
@@ -88,14 +101,18 @@ class DecodeState:
             si, sc, km = sel_idx, sel_cnt, int(k_max if k_max is not None else sel_idx.shape[-1])
         else:
             si, sc, km = self.sel_idx, self.sel_cnt, self.k_max
-        seer.sparse_decode(self.shape, q, self.kv, lens, si, sc, km, self.out, self.lse,
-                           self.workspace)
+        if self.T > 1:
+            seer.multi_sparse_decode(self.shape, self.T, q, self.kv, lens, si, sc, km, self.out,
+                                     self.lse, self.workspace)
+        else:
+            seer.sparse_decode(self.shape, q, self.kv, lens, si, sc, km, self.out, self.lse,
+                               self.workspace)
         return self.out, self.lse
 
     def step(self, q: torch.Tensor, lens: torch.Tensor):
         """Gate, select and attend: one decode step over a built pooled table
         (the parameter-free gate fused into the attention kernel)."""
-        if self.gate_weights is not None:
+        if self.gate_weights is not None or self.T > 1:
             return self.step_unfused(q, lens)
         seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,

@@ -38,6 +38,9 @@ EXPORTS = (
     "seer_sparse_decode_combine",
     "seer_gated_sparse_decode",
     "seer_gated_sparse_decode_partial",
+    "seer_multi_gate_select",
+    "seer_multi_sparse_decode_workspace_size",
+    "seer_multi_sparse_decode",
     "seer_keep_blocks",
     "seer_status_str",
     "seer_last_error",
@@ -142,6 +145,11 @@ def load(path: str = LIB_PATH):
     lib.seer_gate_select.argtypes = [SP, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
     lib.seer_learned_gate_select.argtypes = [SP, _P, _P, _P, ctypes.POINTER(GateWeightsC), RP,
                                              _I32, _P, _P, _P, _P]
+    lib.seer_multi_gate_select.argtypes = [SP, _I32, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
+    lib.seer_multi_sparse_decode_workspace_size.argtypes = [SP, _I32,
+                                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.seer_multi_sparse_decode.argtypes = [SP, _I32, _P, KP, _P, _P, _P, _I32, ctypes.c_float,
+                                             _P, _P, _P, ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, RP, _I32, ctypes.c_float, _P,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
@@ -154,7 +162,8 @@ def load(path: str = LIB_PATH):
     lib.seer_last_error.argtypes = []
     lib.seer_last_error.restype = ctypes.c_char_p
     for name in ("seer_block_pool_keys", "seer_gate_scores_topk", "seer_gate_select",
-                 "seer_learned_gate_select",
+                 "seer_learned_gate_select", "seer_multi_gate_select",
+                 "seer_multi_sparse_decode_workspace_size", "seer_multi_sparse_decode",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
                  "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial"):
@@ -290,6 +299,46 @@ def sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
     _check(lib.seer_sparse_decode(ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens),
                                   _ptr(sel_idx), _ptr(sel_cnt), k_max, softmax_scale, _ptr(out),
                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def multi_gate_select(shape: Shape, tokens: int, q: torch.Tensor, pooled: torch.Tensor,
+                      lens: torch.Tensor, rule: Select, k_max: int, scores: torch.Tensor,
+                      sel_idx: torch.Tensor, sel_cnt: torch.Tensor):
+    """seer_multi_gate_select: q is [B][tokens][Hq][d]."""
+    lib = load()
+    U = shape.batch * shape.num_kv_heads
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    _check(lib.seer_multi_gate_select(ctypes.byref(shape), tokens, _ptr(q), _ptr(pooled),
+                                      _ptr(lens), ctypes.byref(rule), k_max, _ptr(scores),
+                                      _ptr(sel_idx), _ptr(sel_cnt), _stream()))
+
+
+def multi_decode_workspace_size(shape: Shape, tokens: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.seer_multi_sparse_decode_workspace_size(ctypes.byref(shape), tokens,
+                                                       ctypes.byref(n)))
+    return int(n.value)
+
+
+def multi_sparse_decode(shape: Shape, tokens: int, q: torch.Tensor, kv: KV, lens: torch.Tensor,
+                        sel_idx: Optional[torch.Tensor], sel_cnt: Optional[torch.Tensor],
+                        k_max: int, out: torch.Tensor, lse: Optional[torch.Tensor],
+                        workspace: torch.Tensor, softmax_scale: float = 0.0):
+    """seer_multi_sparse_decode: q [B][tokens][Hq][d]; out [B][tokens][Hq][d]; lse [B][tokens][Hq]."""
+    lib = load()
+    rows = shape.batch * tokens * shape.num_q_heads
+    _need(out, torch.float32, rows * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, rows, "lse")
+    _check(lib.seer_multi_sparse_decode(ctypes.byref(shape), tokens, _ptr(q), ctypes.byref(kv),
+                                        _ptr(lens), _ptr(sel_idx), _ptr(sel_cnt), k_max,
+                                        softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel(), _stream()))
 
 
 def sparse_decode_partial(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,

@@ -286,6 +286,43 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream);
 
+/* Several new query tokens per sequence (speculative or chunked decode).
+ *
+ *  Sequence b has `tokens` = T new query tokens at positions
+ *  lens[b] - T .. lens[b] - 1, their keys and values already in the cache
+ *  (lens includes them; lens[b] >= T).  q is [B][T][Hq][d] (the dtype of the
+ *  shape).  Token t attends to the kept blocks' tokens at positions
+ *  <= lens[b] - T + t ("Sparse Attention Reasoning", Step 4, with query_len =
+ *  T and the causal mask of autoregressive decoding); one selection per
+ *  (sequence, KV head) serves all T tokens.  Supported: 1 <= T and
+ *  G * T <= 16 (SEER_ERR_UNSUPPORTED otherwise).
+ *
+ * seer_multi_gate_select -- seer_gate_select with the gate's query summed over
+ *  the T tokens and the group's heads (token-major, fp64): the query pooling of
+ *  SeerAttention, which "-R" removes for single-token decoding
+ *  ("SeerAttention-R", Abstract).  Other arguments as seer_gate_select.
+ *
+ * seer_multi_sparse_decode_workspace_size -- bytes of workspace the decode
+ *  below needs for this shape and token count on the current device.
+ *
+ * seer_multi_sparse_decode -- the attention of the T tokens over the given
+ *  selection (sel_idx/sel_cnt/k_max as in seer_sparse_decode; sel_idx NULL
+ *  means every block).  out: [B][T][Hq][d] fp32; lse: [B][T][Hq] fp32 natural
+ *  log, or NULL.  A token that sees no key gets out = 0 and lse = -inf.
+ *  Two launches (partial records, then their merge) on `stream`. */
+seer_status seer_multi_gate_select(const seer_shape* shape, int32_t tokens, const void* q,
+                                   const float* pooled, const int32_t* lens,
+                                   const seer_select* rule, int32_t k_max, double* scores,
+                                   int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
+seer_status seer_multi_sparse_decode_workspace_size(const seer_shape* shape, int32_t tokens,
+                                                    size_t* bytes);
+seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, const void* q,
+                                     const seer_kv* kv, const int32_t* lens,
+                                     const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     int32_t k_max, float softmax_scale, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Host helper: max(1, min(n, ceil(n * keep_num / keep_den))), or -1 for bad
  * arguments (n < 1, keep_num < 1, keep_den < keep_num). */
 int32_t seer_keep_blocks(int32_t n_blocks, int32_t keep_num, int32_t keep_den);

@@ -169,3 +169,20 @@ def test_learned_gate_validation(lib):
     assert lib.seer_learned_gate_select(*args(ctypes.byref(wide), sel)) == seer.SEER_ERR_UNSUPPORTED
     uni = seer.make_select(keep=(1, 10), unified=True)
     assert lib.seer_learned_gate_select(*args(ctypes.byref(w), uni)) == seer.SEER_ERR_UNSUPPORTED
+
+
+def test_multi_token_validation(lib):
+    sh = _shape()                                    # G = 4
+    sel = seer.make_select(keep=(1, 10))
+    args = lambda t: (ctypes.byref(sh), t, FAKE, FAKE, FAKE, ctypes.byref(sel), 10, FAKE, FAKE,
+                      FAKE, None)
+    assert lib.seer_multi_gate_select(*args(0)) == seer.SEER_ERR_INVALID_ARG
+    assert lib.seer_multi_gate_select(*args(5)) == seer.SEER_ERR_UNSUPPORTED   # 20 rows > 16
+    n = ctypes.c_size_t(0)
+    assert lib.seer_multi_sparse_decode_workspace_size(ctypes.byref(sh), 5, ctypes.byref(n)) \
+        == seer.SEER_ERR_UNSUPPORTED
+    kv = seer.KV(0x1000, 0x1000, None, 0)
+    st = lib.seer_multi_sparse_decode(ctypes.byref(sh), 4, FAKE, ctypes.byref(kv), FAKE, None,
+                                      None, 0, ctypes.c_float(0.0), None, None, FAKE, 1 << 20,
+                                      None)
+    assert st == seer.SEER_ERR_INVALID_ARG                                    # out is NULL
