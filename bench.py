@@ -91,6 +91,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-learned-gate", action="store_true",
+                    help="skip the learned gate network's step")
+    ap.add_argument("--no-multi-token", action="store_true",
+                    help="skip the step with several query tokens per sequence")
     ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -306,6 +310,99 @@ def run_workload(wl, args):
                  "speedup_sparse_vs_dense": dense_ms / ms_per_step}
     log(f"{wl.name}: gpu timing done: {ms_per_step:.4f} ms/step")
 
+    # ---- the learned gate network (seeded, untrained weights): its gate kernel,
+    # then the partial and combine kernels on its selection ----
+    learned = None
+    if not loop and not args.no_learned_gate:
+        from workloads import make_gate_weights
+        for layer, st in enumerate(states):
+            st.gate_weights = make_gate_weights(wl.num_kv_heads, d, seed=wl.seed + 77 + layer).to(dev)
+
+        def learned_gate_only(i):
+            st, case = layer_of(i)
+            q, lens_i = q_lens(i)
+            st.select(q, lens_i)
+
+        g_l = capture(step, n_steps)
+        timed(g_l)
+        l_ms = timed(g_l) / n_steps
+        del g_l
+        g_lg = capture(learned_gate_only, n_k)
+        timed(g_lg)
+        lg_ms = timed(g_lg, 3) / (3 * n_k)
+        del g_lg
+        for st in states:
+            st.gate_weights = None
+        H = 256
+        # algorithmic bytes of one gate launch: pooled table, query, each KV
+        # head's weights once; int8 operations of its first layer
+        lg_bytes = pooled_bytes + q_bytes + wl.num_kv_heads * H * (d + 4 * d + 8)
+        lg_ops = 2 * blocks * wl.num_kv_heads * H * d
+        learned = {"ms_per_step": l_ms, "tokens_per_s": wl.batch / (l_ms * 1e-3),
+                   "speedup_vs_dense": (dense["ms_per_step"] / l_ms) if dense else None,
+                   "gate_kernel": f"learned_gate_kernel<{wl.dtype},{d}>",
+                   "gate_launch_ms": lg_ms, "gate_bytes": lg_bytes,
+                   "gate_hbm_gbps": lg_bytes / (lg_ms * 1e-3) / 1e9,
+                   "gate_int8_tops": lg_ops / (lg_ms * 1e-3) / 1e12,
+                   "weights": "seeded, untrained"}
+        log(f"{wl.name}: learned gate step {l_ms:.4f} ms, gate kernel {lg_ms * 1e3:.2f} us")
+
+    # ---- several new query tokens per sequence: the same layers' K/V, 4 query
+    # tokens (16 query rows per KV head when G = 4), one selection per KV head ----
+    multi = None
+    TQ = 16 // wl.group if wl.group <= 16 else 0
+    TQ = min(TQ, 4)
+    if not loop and not args.no_multi_token and TQ > 1:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed + 4242)
+        mstates = []
+        for st, case in zip(states, cases):
+            ms = DecodeState(batch=wl.batch, num_q_heads=wl.num_q_heads,
+                             num_kv_heads=wl.num_kv_heads, head_dim=d, block_size=S,
+                             max_blocks=wl.max_blocks, dtype=DT, k=case.k, v=case.v,
+                             page_table=case.page_table, keep=wl.keep, top_k=case.top_k,
+                             query_tokens=TQ)
+            ms.build_pool(case.lens)
+            qm = torch.randn((wl.batch, TQ, wl.num_q_heads, d), generator=gen,
+                             device=dev).to(DT)
+            mstates.append((ms, qm, case))
+
+        def mstep(i):
+            ms, qm, case = mstates[i % n_layers]
+            ms.step(qm, case.lens)
+
+        def mdecode(i):
+            ms, qm, case = mstates[i % n_layers]
+            ms.attend(qm, case.lens)
+
+        g_m = capture(mstep, n_steps)
+        timed(g_m)
+        m_ms = timed(g_m) / n_steps
+        del g_m
+        g_md = capture(mdecode, n_k)
+        timed(g_md)
+        md_ms = timed(g_md, 3) / (3 * n_k)
+        del g_md
+        ms0 = mstates[0][0]
+        msel = ms0.sel_idx.cpu().numpy()
+        mcnt = ms0.sel_cnt.cpu().numpy()
+        mtok = 0
+        for u in range(msel.shape[0]):
+            L = int(lens[u // wl.num_kv_heads])
+            for j in msel[u, : mcnt[u]]:
+                mtok += min(S, L - int(j) * S)
+        m_bytes = mtok * d * e * 2 + wl.batch * TQ * wl.num_q_heads * d * e
+        multi = {"workload": f"{wl.name} K/V with {TQ} new query tokens per sequence",
+                 "query_tokens": TQ, "ms_per_step": m_ms,
+                 "tokens_per_s": wl.batch * TQ / (m_ms * 1e-3),
+                 "tokens_per_s_vs_one_token": (wl.batch * TQ / m_ms) / (wl.batch / ms_per_step),
+                 "decode_ms": md_ms, "decode_bytes": m_bytes,
+                 "decode_hbm_gbps": m_bytes / (md_ms * 1e-3) / 1e9,
+                 "kernels": f"gate_topk_kernel, decode_multi_kernel<{wl.dtype},{d}>, "
+                            f"decode_multi_combine_kernel<{d}>"}
+        del mstates
+        log(f"{wl.name}: {TQ}-token step {m_ms:.4f} ms")
+
     # ---- CPU baseline: the fp64 oracle on a bounded sample ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,6 +441,8 @@ def run_workload(wl, args):
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},
         "dense": dense,
+        "learned_gate": learned,
+        "multi_token": multi,
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
     }

@@ -370,53 +370,88 @@ void decode_multi_kernel(DecodeArgs a) {
   }
 }
 
-// Merges a unit's records row by row in wave order (a running maximum):
-//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l;
-// then out = o / l and lse = (M + log2 l) ln 2, for token t = row / G, head
-// g*G + row % G.  Empty waves and records without a valid token are skipped.
-constexpr int kMCombineThreads = 256;
+// Merges a unit's records for one query row (token t = row / G, head
+// g*G + row % G) per workgroup, one thread per dimension.  Up to 32 records:
+// every value loaded up front, then the maximum M of the records' maxima and
+// the scaled sums in record (wave) order,
+//   o = sum_w acc_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M),  out = o / l,
+// lse = (M + log2 l) ln 2.  More records: the same merge with a running
+// maximum.  Empty waves and records without a valid token are skipped; the
+// order is fixed, so the result is deterministic.
+template <int D, int NWB>
+__device__ __forceinline__ void multi_shot(const CombineArgs& a, const float* part, int nw,
+                                           int wlo, int W, int Tot, int row, int64_t oidx) {
+  constexpr int REC = MGeo<float, D>::REC;
+  const int dim = threadIdx.x;
+  float x[NWB], mv[NWB], lv[NWB];
+#pragma unroll
+  for (int t = 0; t < NWB; ++t) {
+    const float* r = part + (int64_t)min(t, nw - 1) * REC;  // past nw: re-read, unused
+    x[t] = r[row * D + dim];
+    mv[t] = r[kRows * D + row];
+    lv[t] = r[kRows * D + kRows + row];
+  }
+  uint32_t skip = 0;
+  if (Tot < W) {
+    const EqualSplit sp(Tot, W);
+    for (int t = 0; t < nw; ++t) skip |= wave_empty(sp, wlo + t) ? (1u << t) : 0u;
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int t = 0; t < NWB; ++t) M = (t < nw && !((skip >> t) & 1u)) ? fmaxf(M, mv[t]) : M;
+  float o = 0.f, l = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int t = 0; t < NWB; ++t) {
+      const bool use = t < nw && !((skip >> t) & 1u) && mv[t] != kNegInf;
+      const float sc = __builtin_amdgcn_exp2f(mv[t] - M);  // argument <= 0
+      o = use ? fmaf(x[t], sc, o) : o;
+      l = use ? fmaf(lv[t], sc, l) : l;
+    }
+  }
+  a.out[oidx * D + dim] = l > 0.f ? o / l : 0.f;
+  if (a.lse && dim == 0) a.lse[oidx] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+}
 
 template <int D>
-__global__ __launch_bounds__(kMCombineThreads) void decode_multi_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(D) void decode_multi_combine_kernel(CombineArgs a) {
   constexpr int REC = MGeo<float, D>::REC;
-  const int u = blockIdx.x, tid = threadIdx.x;
+  const int u = blockIdx.x, row = blockIdx.y, dim = threadIdx.x;
   const int U = a.B * a.Hkv, TQ = a.tokens, G = a.Hq / a.Hkv, R = G * TQ;
+  if (row >= R) return;
   const int tsh = 31 - __builtin_clz(a.S / kTile);
   const int W = a.hdr[0];
   const int Tot = a.prefix[U] << tsh;
   const int ylo = a.prefix[u] << tsh, yhi = a.prefix[u + 1] << tsh;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
-  auto out_index = [&](int row) {
-    const int t = row / G, h = row - t * G;
-    return ((int64_t)b * TQ + t) * a.Hq + (int64_t)g * G + h;
-  };
+  const int tq = row / G, hq = row - tq * G;
+  const int64_t oidx = ((int64_t)b * TQ + tq) * a.Hq + (int64_t)g * G + hq;
   if (yhi <= ylo) {  // no tokens: out = 0, lse = -inf
-    for (int idx = tid; idx < R * D; idx += kMCombineThreads)
-      a.out[out_index(idx / D) * D + idx % D] = 0.f;
-    if (a.lse && tid < R) a.lse[out_index(tid)] = kNegInf;
+    a.out[oidx * D + dim] = 0.f;
+    if (a.lse && dim == 0) a.lse[oidx] = kNegInf;
     return;
   }
   const int wlo = tile_owner(ylo, W, Tot), whi = tile_owner(yhi - 1, W, Tot);
-  const EqualSplit sp(Tot, W);
+  const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;
-  for (int idx = tid; idx < R * D; idx += kMCombineThreads) {
-    const int row = idx / D, dim = idx - row * D;
-    float M = kNegInf, l = 0.f, o = 0.f;
-    for (int t = 0; t <= whi - wlo; ++t) {
-      if (Tot < W && wave_empty(sp, wlo + t)) continue;  // wrote no record
-      const float* r = part + (int64_t)t * REC;
-      const float mw = r[kRows * D + row];
-      if (mw == kNegInf) continue;                        // no valid token in it
-      const float mn = fmaxf(M, mw);
-      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(mw - mn);
-      o = o * sa + r[row * D + dim] * sb;
-      l = l * sa + r[kRows * D + kRows + row] * sb;
-      M = mn;
-    }
-    a.out[out_index(row) * D + dim] = l > 0.f ? o / l : 0.f;
-    if (a.lse && dim == 0)
-      a.lse[out_index(row)] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+  if (nw <= 8) return multi_shot<D, 8>(a, part, nw, wlo, W, Tot, row, oidx);
+  if (nw <= 16) return multi_shot<D, 16>(a, part, nw, wlo, W, Tot, row, oidx);
+  if (nw <= 32) return multi_shot<D, 32>(a, part, nw, wlo, W, Tot, row, oidx);
+  const EqualSplit sp(Tot, W);
+  float M = kNegInf, l = 0.f, o = 0.f;
+  for (int t = 0; t < nw; ++t) {
+    if (Tot < W && wave_empty(sp, wlo + t)) continue;  // wrote no record
+    const float* r = part + (int64_t)t * REC;
+    const float mw = r[kRows * D + row];
+    if (mw == kNegInf) continue;                        // no valid token in it
+    const float mn = fmaxf(M, mw);
+    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(mw - mn);
+    o = o * sa + r[row * D + dim] * sb;
+    l = l * sa + r[kRows * D + kRows + row] * sb;
+    M = mn;
   }
+  a.out[oidx * D + dim] = l > 0.f ? o / l : 0.f;
+  if (a.lse && dim == 0) a.lse[oidx] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
 }
 
 template <typename T, int D>
@@ -448,7 +483,7 @@ hipError_t launch_decode_multi_combine(const CombineArgs& a, hipStream_t stream)
   void* params[] = {&args};
   const void* fn = a.D == 64 ? (const void*)&decode_multi_combine_kernel<64>
                              : (const void*)&decode_multi_combine_kernel<128>;
-  return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(kMCombineThreads), params, 0, stream);
+  return hipLaunchKernel(fn, dim3(a.B * a.Hkv, kRows), dim3(a.D), params, 0, stream);
 }
 
 }  // namespace seer
