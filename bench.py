@@ -396,8 +396,8 @@ def run_workload(wl, args):
                  "query_tokens": TQ, "ms_per_step": m_ms,
                  "tokens_per_s": wl.batch * TQ / (m_ms * 1e-3),
                  "tokens_per_s_vs_one_token": (wl.batch * TQ / m_ms) / (wl.batch / ms_per_step),
-                 "decode_ms": md_ms, "decode_bytes": m_bytes,
-                 "decode_hbm_gbps": m_bytes / (md_ms * 1e-3) / 1e9,
+                 "attend_ms": md_ms, "attend_bytes": m_bytes,
+                 "attend_hbm_gbps": m_bytes / (md_ms * 1e-3) / 1e9,
                  "kernels": f"gate_topk_kernel, decode_multi_kernel<{wl.dtype},{d}>, "
                             f"decode_multi_combine_kernel<{d}>"}
         del mstates
