@@ -148,6 +148,7 @@ def run_workload(wl, args):
     loop = wl.decode_steps > 0
     L0 = wl.context
     S, d = wl.block_size, wl.head_dim
+    T = wl.query_tokens        # new query tokens per sequence per step
 
     # one case per layer: the same shape, independent draws
     states, cases = [], []
@@ -156,7 +157,8 @@ def run_workload(wl, args):
         st = DecodeState(batch=wl.batch, num_q_heads=wl.num_q_heads,
                          num_kv_heads=wl.num_kv_heads, head_dim=d, block_size=S,
                          max_blocks=wl.max_blocks, dtype=DT, k=case.k, v=case.v,
-                         page_table=case.page_table, keep=wl.keep, top_k=case.top_k)
+                         page_table=case.page_table, keep=wl.keep, top_k=case.top_k,
+                         query_tokens=T)
         st.build_pool(case.lens)
         states.append(st)
         cases.append(case)
@@ -198,12 +200,25 @@ def run_workload(wl, args):
             return case.q[s], lens_seq[s + 1]
         return case.q, case.lens
 
+    # does the step select inside the attention kernel for this shape?
+    fused = T == 1 and seer.gated_decode_is_fused(states[0].shape, states[0].rule,
+                                                  states[0].k_max)
+
     def partial_only(i):
-        """The fused gate + partial-decode kernel alone (no combine)."""
+        """The step's dominant kernel alone (no combine): the fused gate +
+        partial-decode kernel, else the partial kernel (several query tokens:
+        the multi-token one) on the selection the step made."""
         st, case = layer_of(i)
         q, lens = q_lens(i)
-        seer.gated_sparse_decode(st.shape, q, st.kv, lens, st.pooled, st.rule, st.k_max,
-                                 st.scores, st.sel_idx, st.sel_cnt, None, None, st.workspace)
+        if T > 1:
+            seer.multi_sparse_decode_partial(st.shape, T, q, st.kv, lens, st.sel_idx, st.sel_cnt,
+                                             st.k_max, st.workspace)
+        elif fused:
+            seer.gated_sparse_decode(st.shape, q, st.kv, lens, st.pooled, st.rule, st.k_max,
+                                     st.scores, st.sel_idx, st.sel_cnt, None, None, st.workspace)
+        else:
+            seer.sparse_decode_partial(st.shape, q, st.kv, lens, st.sel_idx, st.sel_cnt,
+                                       st.k_max, st.workspace)
 
     def dense_step(i):
         st, case = layer_of(i)
@@ -253,23 +268,34 @@ def run_workload(wl, args):
     ms_total = timed(g_steps)
     wall = time.perf_counter() - wall0
     ms_per_step = ms_total / n_steps
-    tokens_per_s = wl.batch * n_steps / (ms_total / 1e3)
+    tokens_per_s = wl.batch * T * n_steps / (ms_total / 1e3)
     del g_steps
 
-    # ---- the same steps as three launches (gate kernel, partial, combine) ----
-    if loop:
-        reset_pools()
-    g_unf = capture(step_unfused, n_steps)
-    if loop:
-        reset_pools()
-    unfused_ms = timed(g_unf) / n_steps
-    del g_unf
-    if loop:
-        reset_pools()
+    # ---- the same steps as three launches (gate kernel, partial, combine);
+    # several query tokens have no fused gate, so their step is already that ----
+    unfused_ms = None
+    if T == 1:
+        if loop:
+            reset_pools()
+        g_unf = capture(step_unfused, n_steps)
+        if loop:
+            reset_pools()
+        unfused_ms = timed(g_unf) / n_steps
+        del g_unf
+        if loop:
+            reset_pools()
 
     # ---- fused-kernel timing: back-to-back launches in one graph, events
     # around it on the launch stream ----
     n_k = n_layers if loop else max(4 * n_layers, n_steps // 2)
+    if not fused:
+        # the partial kernel runs on each layer's selection for the lengths it
+        # is timed at (a decode loop's steps moved the lengths on)
+        for i in range(n_layers):
+            st, case = layer_of(i)
+            q, lens = q_lens(i)
+            st.select(q, lens)
+        torch.cuda.synchronize()
     g_part = capture(partial_only, n_k)
     timed(g_part)
     k_ms = timed(g_part, 3) / (3 * n_k)
@@ -289,10 +315,12 @@ def run_workload(wl, args):
         for j in sel[u, : cnt[u]]:
             tokens += min(S, L - int(j) * S)
     kv_bytes = tokens * d * e * 2
-    q_bytes = wl.batch * wl.num_q_heads * d * e
+    q_bytes = wl.batch * T * wl.num_q_heads * d * e
     blocks = int(sum(-(-int(L) // S) for L in lens))
     pooled_bytes = blocks * wl.num_kv_heads * d * 4
-    k_bytes = kv_bytes + q_bytes + pooled_bytes
+    # the fused kernel reads the pooled table; a partial kernel runs on a
+    # selection made before it
+    k_bytes = kv_bytes + q_bytes + (pooled_bytes if fused else 0)
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     step_gbps = k_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -305,7 +333,7 @@ def run_workload(wl, args):
         dense_ms = timed(g_dense) / n_d
         dense_bytes = int(lens.sum()) * wl.num_kv_heads * d * e * 2 + q_bytes
         dense = {"ms_per_step": dense_ms,
-                 "tokens_per_s": wl.batch / (dense_ms * 1e-3),
+                 "tokens_per_s": wl.batch * T / (dense_ms * 1e-3),
                  "hbm_gbps": dense_bytes / (dense_ms * 1e-3) / 1e9,
                  "speedup_sparse_vs_dense": dense_ms / ms_per_step}
     log(f"{wl.name}: gpu timing done: {ms_per_step:.4f} ms/step")
@@ -313,7 +341,7 @@ def run_workload(wl, args):
     # ---- the learned gate network (seeded, untrained weights): its gate kernel,
     # then the partial and combine kernels on its selection ----
     learned = None
-    if not loop and not args.no_learned_gate:
+    if not loop and not args.no_learned_gate and T == 1:
         from workloads import make_gate_weights
         for layer, st in enumerate(states):
             st.gate_weights = make_gate_weights(wl.num_kv_heads, d, seed=wl.seed + 77 + layer).to(dev)
@@ -352,7 +380,7 @@ def run_workload(wl, args):
     multi = None
     TQ = 16 // wl.group if wl.group <= 16 else 0
     TQ = min(TQ, 4)
-    if not loop and not args.no_multi_token and TQ > 1:
+    if not loop and not args.no_multi_token and TQ > 1 and T == 1:
         gen = torch.Generator(device=dev)
         gen.manual_seed(wl.seed + 4242)
         mstates = []
@@ -379,10 +407,19 @@ def run_workload(wl, args):
         timed(g_m)
         m_ms = timed(g_m) / n_steps
         del g_m
+        def mpartial(i):
+            ms, qm, case = mstates[i % n_layers]
+            seer.multi_sparse_decode_partial(ms.shape, TQ, qm, ms.kv, case.lens, ms.sel_idx,
+                                             ms.sel_cnt, ms.k_max, ms.workspace)
+
         g_md = capture(mdecode, n_k)
         timed(g_md)
         md_ms = timed(g_md, 3) / (3 * n_k)
         del g_md
+        g_mp = capture(mpartial, n_k)
+        timed(g_mp)
+        mp_ms = timed(g_mp, 3) / (3 * n_k)
+        del g_mp
         ms0 = mstates[0][0]
         msel = ms0.sel_idx.cpu().numpy()
         mcnt = ms0.sel_cnt.cpu().numpy()
@@ -398,6 +435,8 @@ def run_workload(wl, args):
                  "tokens_per_s_vs_one_token": (wl.batch * TQ / m_ms) / (wl.batch / ms_per_step),
                  "attend_ms": md_ms, "attend_bytes": m_bytes,
                  "attend_hbm_gbps": m_bytes / (md_ms * 1e-3) / 1e9,
+                 "partial_launch_ms": mp_ms,
+                 "partial_hbm_gbps": m_bytes / (mp_ms * 1e-3) / 1e9,
                  "kernels": f"gate_topk_kernel, decode_multi_kernel<{wl.dtype},{d}>, "
                             f"decode_multi_combine_kernel<{d}>"}
         del mstates
@@ -414,7 +453,7 @@ def run_workload(wl, args):
               "context": list(wl.variable_context) if wl.variable_context else wl.context,
               "kept_blocks": [int(kept.min()), int(kept.max())] if len(kept) else [0, 0],
               "blocks_max": int(-(-int(lens.max()) // S)),
-              "paged": wl.paged, "decode_loop_steps": wl.decode_steps,
+              "query_tokens": T, "paged": wl.paged, "decode_loop_steps": wl.decode_steps,
               "layers_cycled": n_layers}
     G = wl.group
     return {
@@ -433,10 +472,13 @@ def run_workload(wl, args):
         "config": config,
         "step_hbm_gbps": step_gbps,
         "step_pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
-        "unfused": {"ms_per_step": unfused_ms,
-                    "speedup_fused_vs_unfused": unfused_ms / ms_per_step},
+        "gate_fused": fused,
+        "unfused": None if unfused_ms is None else {
+            "ms_per_step": unfused_ms, "speedup_fused_vs_unfused": unfused_ms / ms_per_step},
         "roofline": {"bound": "hbm",
-                     "kernel": f"decode_partial_kernel<{wl.dtype},{d},{G},gated>",
+                     "kernel": (f"decode_multi_kernel<{wl.dtype},{d}>" if T > 1 else
+                                f"decode_partial_kernel<{wl.dtype},{d},{G},gated>" if fused else
+                                f"decode_partial_kernel<{wl.dtype},{d},{G}>"),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},
@@ -455,7 +497,7 @@ def cpu_baseline(wl, case, n_seqs, seconds):
 
     from oracle import seer_oracle as O
 
-    S, d, G = wl.block_size, wl.head_dim, wl.group
+    S, d, G, TQ = wl.block_size, wl.head_dim, wl.group, wl.query_tokens
     lens = case.lens.cpu().numpy()
     loop = wl.decode_steps > 0
     units = [(b, g) for b in range(n_seqs) for g in range(wl.num_kv_heads)]
@@ -474,7 +516,10 @@ def cpu_baseline(wl, case, n_seqs, seconds):
             v = case.v[pages][:, g].reshape(-1, d)[:T].double().cpu().numpy()
         p32, _, osum = O.pool_keys(k, L, S)
         qsrc = case.q[0] if loop else case.q
-        qg = qsrc[b, g * G:(g + 1) * G].double().cpu().numpy()
+        if TQ > 1:  # [B][TQ][Hq][d]: the group's heads of every token
+            qg = qsrc[b, :, g * G:(g + 1) * G].double().cpu().numpy()
+        else:
+            qg = qsrc[b, g * G:(g + 1) * G].double().cpu().numpy()
         data[(b, g)] = (k, v, p32, osum, qg, L)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -484,20 +529,24 @@ def cpu_baseline(wl, case, n_seqs, seconds):
                 if loop:     # append the new token, then decode at L + 1
                     p32, _ = O.pool_keys_append(p32, osum.copy(), k, L, L + 1, S)
                     L = L + 1
-                s = O.gate_scores(qg, p32, d)
+                s = O.gate_scores_tokens(qg, p32, d) if TQ > 1 else O.gate_scores(qg, p32, d)
                 n = O.block_count(L, S)
                 kk = O.clamp_count(wl.top_k, n) if wl.top_k else O.keep_count(n, *wl.keep)
                 sel = O.select_top_blocks(s, kk)
-                toks = O.selected_tokens(sel, L, S)
-                for h in range(G):
-                    O.attend(qg[h], k, v, toks)
+                if TQ > 1:
+                    O.attend_tokens(qg, k, v, sel, L, S)
+                else:
+                    toks = O.selected_tokens(sel, L, S)
+                    for h in range(G):
+                        O.attend(qg[h], k, v, toks)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds or reps >= 1000:
                 break
     sec_per_step = el / reps * (wl.batch / n_seqs)   # scaled to the full batch
-    return {"value": wl.batch / sec_per_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_seqs} of {wl.batch} sequences (all {wl.num_kv_heads} KV heads), "
+    return {"value": wl.batch * TQ / sec_per_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seqs} of {wl.batch} sequences (all {wl.num_kv_heads} KV heads"
+                      f"{f', {TQ} query tokens each' if TQ > 1 else ''}), "
                       f"{'pool append + ' if loop else ''}gate + top-k + attention in fp64 "
                       f"NumPy, {reps} repetitions in {el:.1f} s, scaled to the full batch; "
                       f"pooled tables built beforehand"}

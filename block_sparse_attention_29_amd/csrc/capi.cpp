@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -80,6 +81,36 @@ int wave_cap(const seer_shape* s) {
   return seer::decode_max_waves(s->dtype, s->head_dim, s->num_q_heads / s->num_kv_heads);
 }
 
+// Waves of a partial launch: all resident slots, but no more than an upper
+// bound of the 16-token tiles (blocks_per_unit blocks per unit), in whole
+// workgroups.
+int decode_waves(const seer_shape* s, int64_t blocks_per_unit, int wmax) {
+  const int64_t tiles_bound =
+      (int64_t)s->batch * s->num_kv_heads * blocks_per_unit * (s->block_size / 16);
+  int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
+  W = (W + seer::kDecodeWavesPerWG - 1) / seer::kDecodeWavesPerWG * seer::kDecodeWavesPerWG;
+  return (int)W;
+}
+
+// Whether the attention kernel selects its own blocks (one launch fewer) for
+// this shape, rule and wave count.  It pays while every workgroup gates about
+// one unit in a single pass over its pooled table: at most one unit per
+// workgroup (with more, a workgroup gates several units one after another,
+// each behind its own load round trip and selection, where the gate kernel
+// gates them all in parallel), and at most 256 blocks per unit (the blocks
+// one pass of the workgroup's loads covers; a longer table makes every
+// workgroup that shares the unit re-score all of it).
+// SEER_FUSED_GATE=1 fuses whenever the rule allows it, =0 never (both give
+// the same results; for tests and measurements).
+bool fused_gate_pays(const seer_shape* s, const seer_select* rule, int W) {
+  if (rule->mode != SEER_SELECT_TOPK || rule->unified) return false;
+  const char* env = getenv("SEER_FUSED_GATE");
+  if (env && env[0] == '1' && env[1] == 0) return true;
+  if (env && env[0] == '0' && env[1] == 0) return false;
+  const int U = s->batch * s->num_kv_heads;
+  return U <= W / seer::kDecodeWavesPerWG && s->max_blocks <= 256;
+}
+
 // Validates a decode call and fills the partial kernel's arguments.
 seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                            const int32_t* lens, const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -109,12 +140,7 @@ seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv
   if (workspace_bytes < need)
     return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
-  // Waves: all resident slots, but no more than an upper bound of the tiles.
-  const int64_t blocks_bound =
-      (int64_t)U * (sel_idx ? k_max : shape->max_blocks);
-  const int64_t tiles_bound = blocks_bound * (shape->block_size / 16);  // 16-token tiles
-  int64_t W = tiles_bound < wmax ? tiles_bound : wmax;
-  W = (W + seer::kDecodeWavesPerWG - 1) / seer::kDecodeWavesPerWG * seer::kDecodeWavesPerWG;
+  const int W = decode_waves(shape, sel_idx ? k_max : shape->max_blocks, wmax);
 
   const double scale = softmax_scale > 0.f ? (double)softmax_scale
                                            : 1.0 / sqrt((double)shape->head_dim);
@@ -379,9 +405,9 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
   const int ids_cap = seer::gated_decode_ids_cap(U, k_max, a.W);
   const size_t smem = seer::gated_decode_smem_bytes(U, shape->max_blocks, ids_cap);
   // The fused kernel selects by top-k per unit (forced blocks included); a
-  // threshold or a unified selection runs the gate kernel first.
-  const bool fusable = rule->mode == SEER_SELECT_TOPK && !rule->unified;
-  if (fusable && smem <= max_block_smem()) {
+  // threshold or a unified selection, or a shape where fusing does not pay,
+  // runs the gate kernel first.
+  if (fused_gate_pays(shape, rule, a.W) && smem <= max_block_smem()) {
     a.sel_idx = nullptr;
     a.sel_cnt = nullptr;
     a.pooled = pooled;
@@ -405,6 +431,24 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
     const hipError_t e = seer::launch_decode_partial(a, stream);
     if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   }
+  return ok();
+}
+
+seer_status seer_gated_decode_is_fused(const seer_shape* shape, const seer_select* rule,
+                                       int32_t k_max, int32_t* fused) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if (!rule || !fused) return fail(SEER_ERR_INVALID_ARG, "rule or fused is NULL");
+  if (k_max < 1 || k_max > shape->max_blocks)
+    return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks]", k_max);
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  // the same wave count and LDS test as seer_gated_sparse_decode_partial
+  const int U = shape->batch * shape->num_kv_heads;
+  const int W = decode_waves(shape, k_max, wmax);
+  const size_t smem = seer::gated_decode_smem_bytes(
+      U, shape->max_blocks, seer::gated_decode_ids_cap(U, k_max, W));
+  *fused = fused_gate_pays(shape, rule, W) && smem <= max_block_smem();
   return ok();
 }
 
@@ -485,13 +529,12 @@ seer_status seer_multi_sparse_decode_workspace_size(const seer_shape* shape, int
   return ok();
 }
 
-seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, const void* q,
-                                     const seer_kv* kv, const int32_t* lens,
-                                     const int32_t* sel_idx, const int32_t* sel_cnt,
-                                     int32_t k_max, float softmax_scale, float* out, float* lse,
-                                     void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
-  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+seer_status seer_multi_sparse_decode_partial(const seer_shape* shape, int32_t tokens,
+                                             const void* q, const seer_kv* kv,
+                                             const int32_t* lens, const int32_t* sel_idx,
+                                             const int32_t* sel_cnt, int32_t k_max,
+                                             float softmax_scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   seer_status st = check_shape(shape);
   if (st) return st;
   if ((st = check_tokens(shape, tokens))) return st;
@@ -504,23 +547,58 @@ seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, co
   if (workspace_bytes < need)
     return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   a.tokens = tokens;
-  hipError_t e = seer::launch_decode_multi(a, stream);
+  const hipError_t e = seer::launch_decode_multi(a, stream);
   if (e != hipSuccess) return hip_fail(e, "multi decode launch");
+  return ok();
+}
+
+seer_status seer_multi_sparse_decode_combine(const seer_shape* shape, int32_t tokens, float* out,
+                                             float* lse, const void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(SEER_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  const size_t need = seer::decode_multi_workspace_bytes(shape->batch, shape->num_kv_heads,
+                                                         shape->head_dim, wmax);
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int U = shape->batch * shape->num_kv_heads;
+  const char* ws = (const char*)workspace;
   seer::CombineArgs c{};
-  c.B = a.B;
-  c.Hq = a.Hq;
-  c.Hkv = a.Hkv;
-  c.D = a.D;
-  c.S = a.S;
+  c.B = shape->batch;
+  c.Hq = shape->num_q_heads;
+  c.Hkv = shape->num_kv_heads;
+  c.D = shape->head_dim;
+  c.S = shape->block_size;
   c.tokens = tokens;
-  c.hdr = a.hdr;
-  c.prefix = a.prefix;
-  c.part = a.part;
+  c.hdr = (const int32_t*)ws;
+  c.prefix = (const int32_t*)(ws + 64);
+  c.part = (const float*)(ws + seer::decode_part_offset(U));
   c.out = out;
   c.lse = lse;
-  e = seer::launch_decode_multi_combine(c, stream);
+  const hipError_t e = seer::launch_decode_multi_combine(c, stream);
   if (e != hipSuccess) return hip_fail(e, "multi combine launch");
   return ok();
+}
+
+seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, const void* q,
+                                     const seer_kv* kv, const int32_t* lens,
+                                     const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     int32_t k_max, float softmax_scale, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  const seer_status st = seer_multi_sparse_decode_partial(
+      shape, tokens, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale, workspace,
+      workspace_bytes, stream);
+  if (st) return st;
+  return seer_multi_sparse_decode_combine(shape, tokens, out, lse, workspace, workspace_bytes,
+                                          stream);
 }
 
 seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,

@@ -38,9 +38,12 @@ EXPORTS = (
     "seer_sparse_decode_combine",
     "seer_gated_sparse_decode",
     "seer_gated_sparse_decode_partial",
+    "seer_gated_decode_is_fused",
     "seer_multi_gate_select",
     "seer_multi_sparse_decode_workspace_size",
     "seer_multi_sparse_decode",
+    "seer_multi_sparse_decode_partial",
+    "seer_multi_sparse_decode_combine",
     "seer_keep_blocks",
     "seer_status_str",
     "seer_last_error",
@@ -150,11 +153,15 @@ def load(path: str = LIB_PATH):
                                                             ctypes.POINTER(ctypes.c_size_t)]
     lib.seer_multi_sparse_decode.argtypes = [SP, _I32, _P, KP, _P, _P, _P, _I32, ctypes.c_float,
                                              _P, _P, _P, ctypes.c_size_t, _P]
+    lib.seer_multi_sparse_decode_partial.argtypes = [SP, _I32, _P, KP, _P, _P, _P, _I32,
+                                                     ctypes.c_float, _P, ctypes.c_size_t, _P]
+    lib.seer_multi_sparse_decode_combine.argtypes = [SP, _I32, _P, _P, _P, ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P, RP, _I32, ctypes.c_float, _P,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
                                                      ctypes.c_float, _P, _P, _P, _P,
                                                      ctypes.c_size_t, _P]
+    lib.seer_gated_decode_is_fused.argtypes = [SP, RP, _I32, ctypes.POINTER(ctypes.c_int32)]
     lib.seer_keep_blocks.argtypes = [_I32, _I32, _I32]
     lib.seer_keep_blocks.restype = _I32
     lib.seer_status_str.argtypes = [_I32]
@@ -202,6 +209,18 @@ def _need(t: torch.Tensor, dtype, numel: int, name: str):
                          f"elements, got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
+def _need_q(shape: Shape, q: Optional[torch.Tensor], tokens: int = 1):
+    """q must hold exactly [B][tokens][Hq][d] elements of the shape's dtype (a
+    NULL q is left to the library, which rejects it)."""
+    if q is None:
+        return
+    want = {SEER_F32: torch.float32, SEER_BF16: torch.bfloat16}.get(shape.dtype)
+    n = shape.batch * tokens * shape.num_q_heads * shape.head_dim
+    if not q.is_cuda or q.dtype != want or not q.is_contiguous() or q.numel() != n:
+        raise ValueError(f"q: want a contiguous {want} device tensor of {n} elements "
+                         f"([B][{tokens}][Hq][d]), got {q.dtype} {tuple(q.shape)} on {q.device}")
+
+
 # ------------------------------------------------------------------ calls
 
 def keep_blocks(n_blocks: int, keep_num: int, keep_den: int) -> int:
@@ -225,6 +244,7 @@ def gate_scores_topk(shape: Shape, q: torch.Tensor, pooled: torch.Tensor, lens: 
                      top_k: Optional[torch.Tensor], keep_num: int, keep_den: int, k_max: int,
                      scores: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor):
     lib = load()
+    _need_q(shape, q)
     U = shape.batch * shape.num_kv_heads
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
     _need(lens, torch.int32, shape.batch, "lens")
@@ -242,6 +262,7 @@ def gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor, lens: torch
                 rule: Select, k_max: int, scores: torch.Tensor, sel_idx: torch.Tensor,
                 sel_cnt: torch.Tensor):
     lib = load()
+    _need_q(shape, q)
     U = shape.batch * shape.num_kv_heads
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
     _need(lens, torch.int32, shape.batch, "lens")
@@ -259,6 +280,7 @@ def learned_gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor,
     """seer_learned_gate_select; ``weights`` has device tensors w1 (int8), w1_scale,
     b1, wq (float32) in the layouts of include/seer.h."""
     lib = load()
+    _need_q(shape, q)
     U = shape.batch * shape.num_kv_heads
     H = int(weights.w1.shape[-2])
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
@@ -293,6 +315,7 @@ def sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
                   out: torch.Tensor, lse: Optional[torch.Tensor], workspace: torch.Tensor,
                   softmax_scale: float = 0.0):
     lib = load()
+    _need_q(shape, q)
     _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
     if lse is not None:
         _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
@@ -306,6 +329,7 @@ def multi_gate_select(shape: Shape, tokens: int, q: torch.Tensor, pooled: torch.
                       sel_idx: torch.Tensor, sel_cnt: torch.Tensor):
     """seer_multi_gate_select: q is [B][tokens][Hq][d]."""
     lib = load()
+    _need_q(shape, q, tokens)
     U = shape.batch * shape.num_kv_heads
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
     _need(lens, torch.int32, shape.batch, "lens")
@@ -331,6 +355,7 @@ def multi_sparse_decode(shape: Shape, tokens: int, q: torch.Tensor, kv: KV, lens
                         workspace: torch.Tensor, softmax_scale: float = 0.0):
     """seer_multi_sparse_decode: q [B][tokens][Hq][d]; out [B][tokens][Hq][d]; lse [B][tokens][Hq]."""
     lib = load()
+    _need_q(shape, q, tokens)
     rows = shape.batch * tokens * shape.num_q_heads
     _need(out, torch.float32, rows * shape.head_dim, "out")
     if lse is not None:
@@ -341,10 +366,35 @@ def multi_sparse_decode(shape: Shape, tokens: int, q: torch.Tensor, kv: KV, lens
                                         workspace.numel(), _stream()))
 
 
+def multi_sparse_decode_partial(shape: Shape, tokens: int, q: torch.Tensor, kv: KV,
+                                lens: torch.Tensor, sel_idx: Optional[torch.Tensor],
+                                sel_cnt: Optional[torch.Tensor], k_max: int,
+                                workspace: torch.Tensor, softmax_scale: float = 0.0):
+    """seer_multi_sparse_decode_partial: the partial records of the T tokens."""
+    lib = load()
+    _need_q(shape, q, tokens)
+    _check(lib.seer_multi_sparse_decode_partial(
+        ctypes.byref(shape), tokens, _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(sel_idx),
+        _ptr(sel_cnt), k_max, softmax_scale, _ptr(workspace), workspace.numel(), _stream()))
+
+
+def multi_sparse_decode_combine(shape: Shape, tokens: int, out: torch.Tensor,
+                                lse: Optional[torch.Tensor], workspace: torch.Tensor):
+    """seer_multi_sparse_decode_combine: out [B][tokens][Hq][d], lse [B][tokens][Hq]."""
+    lib = load()
+    rows = shape.batch * tokens * shape.num_q_heads
+    _need(out, torch.float32, rows * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, rows, "lse")
+    _check(lib.seer_multi_sparse_decode_combine(ctypes.byref(shape), tokens, _ptr(out), _ptr(lse),
+                                                _ptr(workspace), workspace.numel(), _stream()))
+
+
 def sparse_decode_partial(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
                           sel_idx: Optional[torch.Tensor], sel_cnt: Optional[torch.Tensor],
                           k_max: int, workspace: torch.Tensor, softmax_scale: float = 0.0):
     lib = load()
+    _need_q(shape, q)
     _check(lib.seer_sparse_decode_partial(ctypes.byref(shape), _ptr(q), ctypes.byref(kv),
                                           _ptr(lens), _ptr(sel_idx), _ptr(sel_cnt), k_max,
                                           softmax_scale, _ptr(workspace), workspace.numel(),
@@ -359,6 +409,16 @@ def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.T
                                           _ptr(workspace), workspace.numel(), _stream()))
 
 
+def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int) -> bool:
+    """seer_gated_decode_is_fused: whether gated_sparse_decode selects inside
+    the attention kernel for this shape and rule on the current device."""
+    lib = load()
+    f = ctypes.c_int32(0)
+    _check(lib.seer_gated_decode_is_fused(ctypes.byref(shape), ctypes.byref(rule), k_max,
+                                          ctypes.byref(f)))
+    return bool(f.value)
+
+
 def gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
                         pooled: torch.Tensor, rule: Select, k_max: int, scores: torch.Tensor,
                         sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
@@ -368,6 +428,7 @@ def gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tenso
     the first (the partial results stay in the workspace for
     sparse_decode_combine)."""
     lib = load()
+    _need_q(shape, q)
     U = shape.batch * shape.num_kv_heads
     _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
     _need(lens, torch.int32, shape.batch, "lens")

@@ -266,12 +266,24 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
  *  Arguments: as seer_gate_select (q, pooled, lens, rule, k_max, scores,
  *  sel_idx, sel_cnt, all outputs written) and seer_sparse_decode (kv,
  *  softmax_scale, out, lse, workspace).
- *  The selection is fused for top-k rules (forced blocks included); for a
- *  threshold or unified rule, or when one workgroup's selections would not
- *  fit in its LDS, the call runs the gate kernel first instead (same
- *  results).
- * _partial: the first launch alone (gate + partial results in the workspace,
- * selections written); seer_sparse_decode_combine finishes it. */
+ *  The selection is fused for top-k rules (forced blocks included) while
+ *  every workgroup gates about one unit in one pass: at most one (sequence,
+ *  KV head) unit per workgroup of the attention kernel and at most 256
+ *  blocks per unit.  For a threshold or unified rule, more units or longer
+ *  tables, or when one workgroup's selections would not fit in its LDS, the
+ *  call runs the gate kernel first instead (same results, one launch more).
+ *  seer_gated_decode_is_fused tells which for a shape.  The environment
+ *  variable SEER_FUSED_GATE=1 fuses whenever the rule allows it, =0 never
+ *  (read at every call; the results do not depend on it).
+ * _partial: the first launch(es) alone (gate + partial results in the
+ * workspace, selections written); seer_sparse_decode_combine finishes it. */
+/* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode with
+ * this shape, rule and k_max selects inside the attention kernel on the
+ * current device, 0 if it runs the gate kernel first (no launch; results are
+ * the same either way).  SEER_ERR_INVALID_ARG for NULL pointers or k_max
+ * outside [1, max_blocks]. */
+seer_status seer_gated_decode_is_fused(const seer_shape* shape, const seer_select* rule,
+                                       int32_t k_max, int32_t* fused);
 seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                                      const int32_t* lens, const float* pooled,
                                      const seer_select* rule, int32_t k_max,
@@ -322,6 +334,21 @@ seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, co
                                      int32_t k_max, float softmax_scale, float* out, float* lse,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/* The two stages of seer_multi_sparse_decode, as seer_sparse_decode_partial
+ * and seer_sparse_decode_combine are of seer_sparse_decode: _partial leaves
+ * 16-row partial results and the split plan in the workspace; _combine merges
+ * them into out/lse.  The same shape, token count, workspace and stream must
+ * be given to both. */
+seer_status seer_multi_sparse_decode_partial(const seer_shape* shape, int32_t tokens,
+                                             const void* q, const seer_kv* kv,
+                                             const int32_t* lens, const int32_t* sel_idx,
+                                             const int32_t* sel_cnt, int32_t k_max,
+                                             float softmax_scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+seer_status seer_multi_sparse_decode_combine(const seer_shape* shape, int32_t tokens, float* out,
+                                             float* lse, const void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 
 /* Host helper: max(1, min(n, ceil(n * keep_num / keep_den))), or -1 for bad
  * arguments (n < 1, keep_num < 1, keep_den < keep_num). */

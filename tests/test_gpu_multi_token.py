@@ -124,3 +124,35 @@ def test_multi_token_full_size():
     st = run_multi(case)
     for (b, g) in units_of(wl, limit=6, seed=5):
         check_multi_unit(st, case, b, g, tag="spec4_32k")
+
+
+def test_multi_token_two_stages():
+    """seer_multi_sparse_decode_partial then _combine on one workspace gives
+    the bits of seer_multi_sparse_decode."""
+    from block_sparse_attention_29_amd import seer
+    wl = CASES["planted_b2_t4"]
+    case = make_case(wl, "cuda")
+    st = run_multi(case)
+    T = wl.query_tokens
+    out = torch.full_like(st.out, float("nan"))
+    lse = torch.full_like(st.lse, float("nan"))
+    seer.multi_sparse_decode_partial(st.shape, T, case.q, st.kv, case.lens, st.sel_idx,
+                                     st.sel_cnt, st.k_max, st.workspace)
+    seer.multi_sparse_decode_combine(st.shape, T, out, lse, st.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st.out) and torch.equal(lse, st.lse)
+
+
+def test_query_shape_checked():
+    """The binding refuses a query whose element count is not [B][T][Hq][d]."""
+    from block_sparse_attention_29_amd import seer
+    wl = CASES["planted_b2_t4"]
+    case = make_case(wl, "cuda")
+    st = run_multi(case)
+    one = state_for(case)                   # one query token per sequence
+    with pytest.raises(ValueError):
+        seer.gate_select(one.shape, case.q, st.pooled, case.lens, one.rule, one.k_max,
+                         one.scores, one.sel_idx, one.sel_cnt)
+    with pytest.raises(ValueError):
+        seer.multi_sparse_decode_partial(st.shape, 2, case.q, st.kv, case.lens, st.sel_idx,
+                                         st.sel_cnt, st.k_max, st.workspace)

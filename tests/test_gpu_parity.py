@@ -154,11 +154,16 @@ def test_decode_with_oracle_selection():
         assert np.abs(out - ref["out"]).max() <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", sorted(SMALL) + ["budget_32k", "long_131k"])
-def test_gated_equals_separate_calls_bitwise(name):
+@pytest.mark.parametrize("name", sorted(SMALL) + ["budget_32k", "long_131k", "paged_var"])
+def test_gated_equals_separate_calls_bitwise(name, monkeypatch):
     """The fused gate + attention call writes exactly what the gate call
-    followed by the attention call writes: scores, ids, counts, out, lse."""
+    followed by the attention call writes: scores, ids, counts, out, lse.
+    The fused kernel is forced, also where the call would not choose it (more
+    than 256 blocks per unit, more units than workgroups)."""
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     wl = SMALL[name] if name in SMALL else WORKLOADS[name].with_(batch=2)
+    if name == "paged_var":
+        wl = WORKLOADS[name].with_(batch=48)     # 384 units on 256 workgroups
     print(f"[case] gated vs separate {name}", flush=True)
     case = make_case(wl, "cuda")
     q = case.q[0] if wl.decode_steps else case.q
@@ -172,9 +177,11 @@ def test_gated_equals_separate_calls_bitwise(name):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
 
 
-def test_gated_with_a_wide_block_table():
-    """8192 blocks per sequence (the largest table): the gated call matches the
-    separate calls and the oracle (its key buffer alone is 64 KiB of LDS)."""
+def test_gated_with_a_wide_block_table(monkeypatch):
+    """8192 blocks per sequence (the largest table): the gated call (fused
+    kernel forced) matches the separate calls and the oracle (its key buffer
+    alone is 64 KiB of LDS)."""
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     S, d, NB, L = 64, 64, 8192, 3000
     gen = torch.Generator(device="cuda")
     gen.manual_seed(8192)
@@ -505,7 +512,8 @@ def test_selection_rules(wname, rname, rule):
 
 @pytest.mark.parametrize("rule", [dict(force_first=True), dict(force_first=True, force_last=True)],
                          ids=["first", "both"])
-def test_fused_forced_blocks_equal_separate_calls(rule):
+def test_fused_forced_blocks_equal_separate_calls(rule, monkeypatch):
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     wl = SMALL["paged_small"]
     case = make_case(wl, "cuda")
     fused, sep = state_for(case, **rule), state_for(case, **rule)
@@ -516,3 +524,27 @@ def test_fused_forced_blocks_equal_separate_calls(rule):
     torch.cuda.synchronize()
     for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
+
+
+@pytest.mark.parametrize("name,want", [("sparse90_32k", True), ("budget_32k", True),
+                                       ("planted_8k", True), ("tiny_1k", True),
+                                       ("long_131k", False), ("paged_var", False)])
+def test_fusion_policy(name, want, monkeypatch):
+    """The gate is fused while each workgroup gates about one unit in one
+    pass (at most one unit per workgroup, at most 256 blocks per unit), and
+    never for a threshold or unified rule; the override forces either way."""
+    from block_sparse_attention_29_amd import seer
+    monkeypatch.delenv("SEER_FUSED_GATE", raising=False)
+    wl = WORKLOADS[name]
+    shape = seer.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                            wl.block_size, wl.max_blocks, DT[wl.dtype])
+    k_max = wl.top_k if wl.top_k else seer.keep_blocks(wl.max_blocks, *wl.keep)
+    rule = seer.make_select(keep=wl.keep) if wl.keep else seer.make_select(
+        top_k=torch.full((wl.batch,), wl.top_k, dtype=torch.int32, device="cuda"))
+    assert seer.gated_decode_is_fused(shape, rule, k_max) == want
+    thr = seer.make_select(threshold=0.0)
+    assert not seer.gated_decode_is_fused(shape, thr, k_max)
+    monkeypatch.setenv("SEER_FUSED_GATE", "0")
+    assert not seer.gated_decode_is_fused(shape, rule, k_max)
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+    assert seer.gated_decode_is_fused(shape, rule, k_max)      # these all fit in LDS
