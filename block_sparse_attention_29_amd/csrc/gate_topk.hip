@@ -8,11 +8,14 @@
 // Step 1: top-k over the gate's scores), ties to the lower block id, and
 // written in ascending id order.
 //
-// One kernel, one 1024-thread workgroup per unit: the scores (the pooled table
-// is d-major, so the 64 lanes of a wave read 64 consecutive blocks' entries
-// of one dimension per load, 256 contiguous bytes), then an exact radix select
-// of the kept set in LDS, compacted in id order with block-wide scans.
-// Deterministic; no sorting network needed.
+// Per-unit selections: the scores by 256-thread workgroups over chunks of 256
+// blocks (the pooled table is d-major, so a wave's lanes read consecutive
+// blocks of one dimension row), then an exact radix select of the kept set in
+// LDS, compacted in id order with block-wide scans -- in one launch, one
+// workgroup per unit, when a table is one chunk, else a score launch over
+// (unit, chunk) and a select launch per unit.  A selection unified over a sequence's KV heads takes one
+// 1024-thread workgroup per sequence for both.  Deterministic; no sorting
+// network needed.
 #include "seer_device.h"
 #include "seer_kernels.h"
 #include "select_device.h"
@@ -41,7 +44,7 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
 // above the threshold's key; then block_topk_ids (an exact radix select by the
 // whole workgroup); the ids go to the rows of KV heads g_lo .. g_hi - 1 (from
 // LDS when UNIFIED), the scores written out are the blocks' own.
-template <int NT, bool UNIFIED>
+template <int NT, bool UNIFIED, bool SCORES = true>
 __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, int g_hi, int n,
                                             uint64_t* s_key, int32_t* s_ids, int* s_hist,
                                             int* s_scan) {
@@ -81,8 +84,8 @@ __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, 
   } else {
     block_topk_ids<NT>(s_key, n, k, s_hist, s_scan, dst);
   }
-  if (nf > 0 || UNIFIED) __syncthreads();
-  if (nf > 0) {
+  if ((nf > 0 && SCORES) || UNIFIED) __syncthreads();
+  if (nf > 0 && SCORES) {
     if (tid == 0) {  // the forced blocks' own scores go out
       s_key[0] = key_first;
       s_key[n - 1] = key_last;
@@ -102,15 +105,17 @@ __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, 
     }
     if (tid == 0) a.sel_cnt[u] = k;
   }
-  for (int g = g_lo; g < g_hi; ++g) {
-    double* sc = a.scores + (int64_t)(b * a.Hkv + g) * a.NB;
-    for (int j = tid; j < n; j += NT) sc[j] = key_score(s_key[j]);
+  if constexpr (SCORES) {
+    for (int g = g_lo; g < g_hi; ++g) {
+      double* sc = a.scores + (int64_t)(b * a.Hkv + g) * a.NB;
+      for (int j = tid; j < n; j += NT) sc[j] = key_score(s_key[j]);
+    }
   }
 }
 
-// One workgroup per selection -- a unit (sequence b, KV head g), or a whole
-// sequence when the selection is unified over its KV heads: scores for all
-// blocks, then the selection.
+// One workgroup per selection -- a whole sequence when the selection is
+// unified over its KV heads (the only use; a per-unit selection is the same
+// code with one KV head): scores for all blocks, then the selection.
 //
 // Scores (all 16 waves): block j's dot product with the group-summed query is
 // split over 4 thread quarters of D/4 dimensions each (each a sequential fp64
@@ -206,6 +211,151 @@ __global__ __launch_bounds__(kTopkThreads) void gate_topk_kernel(GateArgs a) {
   }
 
   gate_finish<kTopkThreads, UNIFIED>(a, b, g_lo, g_hi, n, s_key, s_ids, &s_hist[0][0], s_scan);
+}
+
+// ---------------------------------------------------------------- split gate
+//
+// The per-unit gate in two launches, so that the scoring of long tables and
+// of many units spreads over the whole chip (one workgroup per unit leaves
+// most CUs idle when units are few and long, and takes several rounds when
+// they are many):
+//  gate_score_kernel: one 256-thread workgroup per (unit, chunk of 256
+//   blocks).  Wave w owns dimensions w*D/4 .. (w+1)*D/4 - 1; each lane four
+//   blocks of the chunk (16-byte loads of 4 consecutive blocks when the
+//   table's rows allow, else blocks l, l+64, l+128, l+192).  Per block the
+//   arithmetic is the one-kernel gate's: 4 fp64 FMA chains over the quarters
+//   of d, added in quarter order, times 1/sqrt(d); the score goes to `scores`
+//   (-0 written as +0, as the one-kernel gate does).
+//  gate_select_kernel: one 256-thread workgroup per unit reads the scores
+//   back as order keys and applies the selection rule (gate_finish).
+// A table of at most 256 blocks is one chunk: gate_unit_kernel scores it into
+// LDS and selects in the same workgroup, one launch.
+// Unified selections keep the one-kernel gate (their scores sum the KV heads
+// before the scaling).
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreChunk = 256;  // blocks per workgroup of the score kernel
+constexpr int kSelectThreads = 256;
+
+// Scores of blocks j0 .. j0 + 255 of unit u (n blocks in its sequence) by a
+// 256-thread workgroup; emit(j, score) is called once for every j < n of the
+// chunk, by thread j - j0.  s_q: [D], s_part: [4][256] doubles of LDS.
+template <typename T, int D, bool VEC4, typename Emit>
+__device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int g, int n, int j0,
+                                            double* s_q, double (*s_part)[kScoreChunk],
+                                            Emit emit) {
+  constexpr int DQ = D / 4;
+  const int tid = threadIdx.x, qd = tid >> 6, lane = tid & 63;
+  const int NB = a.NB;
+  const int G = a.Hq / a.Hkv;
+
+  // ---- pooled loads first (block ids clamped into [0, n), always in bounds) ----
+  const float* pu = a.pooled + ((int64_t)u * D + (int64_t)qd * DQ) * NB;
+  auto blk = [&](int e) { return VEC4 ? j0 + 4 * lane + e : j0 + lane + 64 * e; };
+  float pv[DQ][4];
+  if constexpr (VEC4) {
+    // an aligned group of 4 (NB % 4 == 0, so it stays inside the row)
+    const uint32_t jg = (uint32_t)min(j0 + 4 * lane, ((n - 1) >> 2) << 2);
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      const float4 v = *(const float4*)(pu + (uint32_t)(i * NB) + jg);
+      pv[i][0] = v.x; pv[i][1] = v.y; pv[i][2] = v.z; pv[i][3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DQ; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), n - 1))];
+  }
+
+  // ---- group-summed query, fp64, token-major then head order ----
+  if (tid < D) {
+    const int TQ = a.tokens;
+    const T* q0 = (const T*)a.q + ((int64_t)b * TQ * a.Hq + (int64_t)g * G) * D;
+    double sq = 0.0;
+    for (int t = 0; t < TQ; ++t) {
+      const T* q = q0 + (int64_t)t * a.Hq * D;
+      double x[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) x[h] = load_as_double<T>(q, (int64_t)min(h, G - 1) * D + tid);
+      sq = t == 0 ? x[0] : sq + x[0];
+#pragma unroll
+      for (int h = 1; h < 8; ++h) sq = h < G ? sq + x[h] : sq;
+    }
+    s_q[tid] = sq;
+  }
+  __syncthreads();
+
+  // ---- quarter dot products, then the blocks' sums in quarter order ----
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    double sp = 0.0;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) sp = fma(s_q[qd * DQ + i], (double)pv[i][e], sp);
+    s_part[qd][blk(e) - j0] = sp;
+  }
+  __syncthreads();
+  const int j = j0 + tid;
+  if (j < n) {
+    const double dot = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+    emit(j, dot * (1.0 / sqrt((double)D)));
+  }
+}
+
+template <typename T, int D, bool VEC4>
+__global__ __launch_bounds__(kScoreThreads) void gate_score_kernel(GateArgs a) {
+  __shared__ double s_q[D];
+  __shared__ double s_part[4][kScoreChunk];
+  const int nchunk = (a.NB + kScoreChunk - 1) / kScoreChunk;
+  const int u = (int)blockIdx.x / nchunk, c = (int)blockIdx.x - u * nchunk;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  const int j0 = c * kScoreChunk;
+  if (j0 >= n) return;  // the whole workgroup: nothing of this chunk is in the sequence
+  double* out = a.scores + (int64_t)u * a.NB;
+  score_chunk<T, D, VEC4>(a, u, b, g, n, j0, s_q, s_part,
+                          [&](int j, double sc) { out[j] = key_score(order_key(sc)); });
+}
+
+// Tables of at most 256 blocks: one workgroup per unit scores its chunk into
+// LDS keys and selects, in one launch.
+template <typename T, int D, bool VEC4>
+__global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
+  extern __shared__ uint64_t s_key[];  // [NB] order keys of the unit's scores
+  __shared__ double s_q[D];
+  __shared__ double s_part[4][kScoreChunk];
+  __shared__ int s_hist[3 * 256];
+  __shared__ int s_scan[kScoreThreads / 64 + 1];
+  const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  if (n > 0) {
+    score_chunk<T, D, VEC4>(a, u, b, g, n, 0, s_q, s_part,
+                            [&](int j, double sc) { s_key[j] = order_key(sc); });
+    __syncthreads();
+  }
+  gate_finish<kScoreThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+}
+
+__global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a) {
+  constexpr int NT = kSelectThreads;
+  extern __shared__ uint64_t s_key[];  // [NB] order keys of the unit's scores
+  __shared__ int s_hist[3 * 256];
+  __shared__ int s_scan[NT / 64 + 1];
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  const double* sc = a.scores + (int64_t)u * a.NB;
+  // four loads in flight per thread before their keys are stored
+  for (int j0 = tid; j0 < n; j0 += 4 * NT) {
+    double x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = sc[min(j0 + e * NT, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j0 + e * NT < n) s_key[j0 + e * NT] = order_key(x[e]);
+  }
+  __syncthreads();
+  gate_finish<NT, false, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }
 
 // ---------------------------------------------------------------- learned gate
@@ -418,25 +568,42 @@ size_t gate_smem_bytes(int NB, int k_max) {
   return (size_t)NB * sizeof(uint64_t) + (size_t)k_max * sizeof(int32_t);
 }
 
+template <typename T, int D>
+const void* score_fn(bool vec4, bool one_chunk) {
+  if (one_chunk)
+    return vec4 ? (const void*)&gate_unit_kernel<T, D, true>
+                : (const void*)&gate_unit_kernel<T, D, false>;
+  return vec4 ? (const void*)&gate_score_kernel<T, D, true>
+              : (const void*)&gate_score_kernel<T, D, false>;
+}
+
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
   const int U = a.B * a.Hkv;
   GateArgs args = a;
   void* params[] = {&args};
-  const void* fn = nullptr;
   if (a.unified) {
+    const void* fn;
     if (a.dtype == 1) fn = a.D == 64 ? (const void*)&gate_topk_kernel<uint16_t, 64, true>
                                      : (const void*)&gate_topk_kernel<uint16_t, 128, true>;
     else fn = a.D == 64 ? (const void*)&gate_topk_kernel<float, 64, true>
                         : (const void*)&gate_topk_kernel<float, 128, true>;
-  } else {
-    if (a.dtype == 1) fn = a.D == 64 ? (const void*)&gate_topk_kernel<uint16_t, 64, false>
-                                     : (const void*)&gate_topk_kernel<uint16_t, 128, false>;
-    else fn = a.D == 64 ? (const void*)&gate_topk_kernel<float, 64, false>
-                        : (const void*)&gate_topk_kernel<float, 128, false>;
+    return hipLaunchKernel(fn, dim3(a.B), dim3(kTopkThreads), params,
+                           gate_smem_bytes(a.NB, a.k_max), stream);
   }
-  const int grid = a.unified ? a.B : U;
-  return hipLaunchKernel(fn, dim3(grid), dim3(kTopkThreads), params,
-                         gate_smem_bytes(a.NB, a.k_max), stream);
+  const bool vec4 = a.NB % 4 == 0;
+  const int nchunk = (a.NB + kScoreChunk - 1) / kScoreChunk;
+  const bool one = nchunk == 1;
+  const void* sfn = a.dtype == 1 ? (a.D == 64 ? score_fn<uint16_t, 64>(vec4, one)
+                                              : score_fn<uint16_t, 128>(vec4, one))
+                                 : (a.D == 64 ? score_fn<float, 64>(vec4, one)
+                                              : score_fn<float, 128>(vec4, one));
+  if (one)  // scores and selection in one launch
+    return hipLaunchKernel(sfn, dim3(U), dim3(kScoreThreads), params,
+                           (size_t)a.NB * sizeof(uint64_t), stream);
+  hipError_t e = hipLaunchKernel(sfn, dim3(U * nchunk), dim3(kScoreThreads), params, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&gate_select_kernel, dim3(U), dim3(kSelectThreads), params,
+                         (size_t)a.NB * sizeof(uint64_t), stream);
 }
 
 }  // namespace seer
