@@ -44,6 +44,7 @@ HBM_PEAK_GBPS = 8000.0
 # whose digest the file records.
 KERNEL_SOURCES = ["block_sparse_attention_29_amd/csrc/sparse_decode.hip",
                   "block_sparse_attention_29_amd/csrc/decode_common.h",
+                  "block_sparse_attention_29_amd/csrc/gate_phase.h",
                   "block_sparse_attention_29_amd/csrc/seer_device.h",
                   "block_sparse_attention_29_amd/csrc/seer_kernels.h",
                   "block_sparse_attention_29_amd/csrc/select_device.h",
@@ -202,8 +203,7 @@ def run_workload(wl, args):
         return case.q, case.lens
 
     # does the step select inside the attention kernel for this shape?
-    fused = T == 1 and seer.gated_decode_is_fused(states[0].shape, states[0].rule,
-                                                  states[0].k_max)
+    fused = seer.gated_decode_is_fused(states[0].shape, states[0].rule, states[0].k_max, T)
 
     def partial_only(i):
         """The step's dominant kernel alone (no combine): the fused gate +
@@ -211,7 +211,11 @@ def run_workload(wl, args):
         the multi-token one) on the selection the step made."""
         st, case = layer_of(i)
         q, lens = q_lens(i)
-        if T > 1:
+        if T > 1 and fused:
+            seer.multi_gated_sparse_decode(st.shape, T, q, st.kv, lens, st.pooled, st.rule,
+                                           st.k_max, st.scores, st.sel_idx, st.sel_cnt, None,
+                                           None, st.workspace)
+        elif T > 1:
             seer.multi_sparse_decode_partial(st.shape, T, q, st.kv, lens, st.sel_idx, st.sel_cnt,
                                              st.k_max, st.workspace)
         elif fused:
@@ -422,6 +426,19 @@ def run_workload(wl, args):
         mp_ms = timed(g_mp, 3) / (3 * n_k)
         del g_mp
         ms0 = mstates[0][0]
+        m_fused = seer.gated_decode_is_fused(ms0.shape, ms0.rule, ms0.k_max, TQ)
+        mf_ms = None
+        if m_fused:
+            def mfused(i):
+                ms, qm, case = mstates[i % n_layers]
+                seer.multi_gated_sparse_decode(ms.shape, TQ, qm, ms.kv, case.lens, ms.pooled,
+                                               ms.rule, ms.k_max, ms.scores, ms.sel_idx,
+                                               ms.sel_cnt, None, None, ms.workspace)
+
+            g_mf = capture(mfused, n_k)
+            timed(g_mf)
+            mf_ms = timed(g_mf, 3) / (3 * n_k)
+            del g_mf
         msel = ms0.sel_idx.cpu().numpy()
         mcnt = ms0.sel_cnt.cpu().numpy()
         mtok = 0
@@ -438,8 +455,13 @@ def run_workload(wl, args):
                  "attend_hbm_gbps": m_bytes / (md_ms * 1e-3) / 1e9,
                  "partial_launch_ms": mp_ms,
                  "partial_hbm_gbps": m_bytes / (mp_ms * 1e-3) / 1e9,
-                 "kernels": f"gate_topk_kernel, decode_multi_kernel<{wl.dtype},{d}>, "
-                            f"decode_multi_combine_kernel<{d}>"}
+                 "gate_fused": m_fused,
+                 "fused_launch_ms": mf_ms,
+                 "fused_hbm_gbps": ((m_bytes + pooled_bytes) / (mf_ms * 1e-3) / 1e9
+                                    if mf_ms else None),
+                 "kernels": (f"decode_multi_kernel<{wl.dtype},{d},gated>, " if m_fused else
+                             f"gate_unit_kernel, decode_multi_kernel<{wl.dtype},{d}>, ")
+                            + f"decode_multi_combine_kernel<{d}>"}
         del mstates
         log(f"{wl.name}: {TQ}-token step {m_ms:.4f} ms")
 
@@ -477,9 +499,9 @@ def run_workload(wl, args):
         "unfused": None if unfused_ms is None else {
             "ms_per_step": unfused_ms, "speedup_fused_vs_unfused": unfused_ms / ms_per_step},
         "roofline": {"bound": "hbm",
-                     "kernel": (f"decode_multi_kernel<{wl.dtype},{d}>" if T > 1 else
-                                f"decode_partial_kernel<{wl.dtype},{d},{G},gated>" if fused else
-                                f"decode_partial_kernel<{wl.dtype},{d},{G}>"),
+                     "kernel": ((f"decode_multi_kernel<{wl.dtype},{d}" if T > 1 else
+                                 f"decode_partial_kernel<{wl.dtype},{d},{G}")
+                                + (",gated>" if fused else ">")),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},

@@ -210,6 +210,46 @@ size_t max_block_smem() {
   return (size_t)v;
 }
 
+// Static LDS of the attention kernel with the gate fused in (tokens > 1: the
+// multi-token kernel), or (size_t)-1.
+size_t gated_static_smem(const seer_shape* s, int tokens) {
+  if (tokens > 1) return seer::gated_decode_multi_static_smem(s->dtype, s->head_dim);
+  return seer::gated_decode_static_smem(s->dtype, s->head_dim, s->num_q_heads / s->num_kv_heads);
+}
+
+// Whether the call with W waves runs the attention kernel with the gate fused
+// in: the rule and shape make it pay, and its LDS (static + ids + keys) fits.
+bool fused_gate_runs(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
+                     int tokens) {
+  if (!fused_gate_pays(s, rule, W)) return false;
+  const int U = s->batch * s->num_kv_heads;
+  const size_t st = gated_static_smem(s, tokens);
+  if (st == (size_t)-1) return false;
+  const size_t dyn = seer::gated_decode_smem_bytes(U, s->max_blocks,
+                                                   seer::gated_decode_ids_cap(U, k_max, W));
+  return st + dyn <= max_block_smem();
+}
+
+// Turns the partial kernel's arguments into the fused gate's: the kernel
+// selects by the rule and writes scores, ids and counts.
+void set_fused_gate(const seer_shape* s, const float* pooled, const seer_select* rule,
+                    int32_t k_max, double* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                    seer::DecodeArgs& a) {
+  const int U = s->batch * s->num_kv_heads;
+  a.sel_idx = nullptr;
+  a.sel_cnt = nullptr;
+  a.pooled = pooled;
+  a.top_k = rule->top_k;
+  a.keep_num = rule->keep_num;
+  a.keep_den = rule->keep_den;
+  a.force_first = rule->force_first != 0;
+  a.force_last = rule->force_last != 0;
+  a.scores = scores;
+  a.sel_idx_out = sel_idx;
+  a.sel_cnt_out = sel_cnt;
+  a.ids_cap = seer::gated_decode_ids_cap(U, k_max, a.W);
+}
+
 
 // The gate kernels' arguments from a validated call.
 seer::GateArgs gate_args(const seer_shape* shape, const void* q, const float* pooled,
@@ -401,25 +441,11 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
   if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
                            workspace, workspace_bytes, &a)))
     return st;
-  const int U = shape->batch * shape->num_kv_heads;
-  const int ids_cap = seer::gated_decode_ids_cap(U, k_max, a.W);
-  const size_t smem = seer::gated_decode_smem_bytes(U, shape->max_blocks, ids_cap);
   // The fused kernel selects by top-k per unit (forced blocks included); a
   // threshold or a unified selection, or a shape where fusing does not pay,
   // runs the gate kernel first.
-  if (fused_gate_pays(shape, rule, a.W) && smem <= max_block_smem()) {
-    a.sel_idx = nullptr;
-    a.sel_cnt = nullptr;
-    a.pooled = pooled;
-    a.top_k = rule->top_k;
-    a.keep_num = rule->keep_num;
-    a.keep_den = rule->keep_den;
-    a.force_first = rule->force_first != 0;
-    a.force_last = rule->force_last != 0;
-    a.scores = scores;
-    a.sel_idx_out = sel_idx;
-    a.sel_cnt_out = sel_cnt;
-    a.ids_cap = ids_cap;
+  if (fused_gate_runs(shape, rule, k_max, a.W, 1)) {
+    set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
     const hipError_t e = seer::launch_gated_decode_partial(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
   } else {
@@ -434,21 +460,18 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
   return ok();
 }
 
-seer_status seer_gated_decode_is_fused(const seer_shape* shape, const seer_select* rule,
-                                       int32_t k_max, int32_t* fused) {
+seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
+                                       const seer_select* rule, int32_t k_max, int32_t* fused) {
   seer_status st = check_shape(shape);
   if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
   if (!rule || !fused) return fail(SEER_ERR_INVALID_ARG, "rule or fused is NULL");
   if (k_max < 1 || k_max > shape->max_blocks)
     return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks]", k_max);
   const int wmax = wave_cap(shape);
   if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
-  // the same wave count and LDS test as seer_gated_sparse_decode_partial
-  const int U = shape->batch * shape->num_kv_heads;
-  const int W = decode_waves(shape, k_max, wmax);
-  const size_t smem = seer::gated_decode_smem_bytes(
-      U, shape->max_blocks, seer::gated_decode_ids_cap(U, k_max, W));
-  *fused = fused_gate_pays(shape, rule, W) && smem <= max_block_smem();
+  // the same wave count and test as the gated decode calls
+  *fused = fused_gate_runs(shape, rule, k_max, decode_waves(shape, k_max, wmax), tokens);
   return ok();
 }
 
@@ -596,6 +619,51 @@ seer_status seer_multi_sparse_decode(const seer_shape* shape, int32_t tokens, co
   const seer_status st = seer_multi_sparse_decode_partial(
       shape, tokens, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale, workspace,
       workspace_bytes, stream);
+  if (st) return st;
+  return seer_multi_sparse_decode_combine(shape, tokens, out, lse, workspace, workspace_bytes,
+                                          stream);
+}
+
+seer_status seer_multi_gated_sparse_decode_partial(
+    const seer_shape* shape, int32_t tokens, const void* q, const seer_kv* kv,
+    const int32_t* lens, const float* pooled, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (st) return st;
+  if ((st = check_tokens(shape, tokens))) return st;
+  seer::DecodeArgs a;
+  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
+                           workspace, workspace_bytes, &a)))
+    return st;
+  const size_t need = seer::decode_multi_workspace_bytes(shape->batch, shape->num_kv_heads,
+                                                         shape->head_dim, wave_cap(shape));
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  a.tokens = tokens;
+  if (fused_gate_runs(shape, rule, k_max, a.W, tokens)) {
+    set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
+    const hipError_t e = seer::launch_gated_decode_multi(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gated multi decode launch");
+  } else {
+    if ((st = seer_multi_gate_select(shape, tokens, q, pooled, lens, rule, k_max, scores, sel_idx,
+                                     sel_cnt, stream)))
+      return st;
+    const hipError_t e = seer::launch_decode_multi(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "multi decode launch");
+  }
+  return ok();
+}
+
+seer_status seer_multi_gated_sparse_decode(
+    const seer_shape* shape, int32_t tokens, const void* q, const seer_kv* kv,
+    const int32_t* lens, const float* pooled, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, float* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  const seer_status st = seer_multi_gated_sparse_decode_partial(
+      shape, tokens, q, kv, lens, pooled, rule, k_max, softmax_scale, scores, sel_idx, sel_cnt,
+      workspace, workspace_bytes, stream);
   if (st) return st;
   return seer_multi_sparse_decode_combine(shape, tokens, out, lse, workspace, workspace_bytes,
                                           stream);

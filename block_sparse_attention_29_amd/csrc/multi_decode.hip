@@ -23,6 +23,7 @@
 //    column n -- output column n of dimension step e is dimension n*D/16 + e,
 //    and each lane's rows of the result are its rows of the softmax state.
 #include "decode_common.h"
+#include "gate_phase.h"
 #include "select_device.h"
 
 namespace seer {
@@ -58,7 +59,10 @@ __device__ __forceinline__ float v_elem<float, 2>(const uint4 (&v)[2], int e) {
   return chunk_elem<float>(v[e >> 2], e & 3);
 }
 
-template <typename T, int D>
+// GATED: every workgroup first scores and selects the blocks of the units it
+// streams (the gate of gate_phase.h with the query summed over the T tokens
+// and the group's heads), as the single-token kernel does.
+template <typename T, int D, bool GATED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_multi_kernel(DecodeArgs a) {
   using GE = MGeo<T, D>;
@@ -75,20 +79,29 @@ void decode_multi_kernel(DecodeArgs a) {
   int* s_scan = s_dyn + U + 1;                   // [kWavesPerWG + 1]
   int* s_len = s_dyn + U + 1 + kWavesPerWG + 1;  // [U]
 
+  const int nwg = (int)gridDim.x;
+  const int wg = (nwg % kXcds == 0)
+      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
+      : (int)blockIdx.x;
+  const int wg0 = wg * kWavesPerWG;
+  GatePreload<T, D, kRows> pre;  // the fused gate's entry loads
+  pre.u = -1;
+
   // ---- plan: block prefix over units (every workgroup computes the same) ----
   {
     const int per = (U + kThreads - 1) / kThreads;
     const int u_lo = min(U, tid * per), u_hi = min(U, u_lo + per);
+    // the thread's first unit's loads first, the gate's entry loads after them
+    const int u_f = min(u_lo, U - 1);
+    const int L_f = a.lens[u_f / a.Hkv];
+    const int aux_f = unit_aux<GATED>(a, u_f);
+    // (wg0 * U < 2^31: fewer than 2^15 waves, at most 2^13 units)
+    if constexpr (GATED)
+      issue_gate_preload<T, D, kRows, true>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
     int local = 0;
     for (int u = u_lo; u < u_hi; ++u) {
-      const int L = a.lens[u / a.Hkv];
-      int c;
-      if (a.sel_idx) {
-        c = a.sel_cnt[u];
-        c = c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
-      } else {
-        c = seq_blocks(L, a.S, a.NB);
-      }
+      const int L = u == u_lo ? L_f : a.lens[u / a.Hkv];
+      const int c = unit_blocks<GATED>(a, L, u == u_lo ? aux_f : unit_aux<GATED>(a, u));
       s_len[u] = L;
       s_prefix[u] = c;
       local += c;
@@ -110,14 +123,60 @@ void decode_multi_kernel(DecodeArgs a) {
 
   const int lane = tid & 63, wv = tid >> 6;
   const int r16 = lane >> 4, n16 = lane & 15;
-  const int nwg = (int)gridDim.x;
-  const int wg = (nwg % kXcds == 0)
-      ? (int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)
-      : (int)blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(wg * kWavesPerWG + wv);
   const int tsh = 31 - __builtin_clz(a.S / kTile);
   const int Tot = __builtin_amdgcn_readfirstlane(s_prefix[U]) << tsh;
   const EqualSplit split(Tot, a.W);
+
+  // ---- fused gate: the selections of every unit this workgroup streams, into
+  // LDS (a unit shared by workgroups is selected by each, bit-identically) ----
+  int32_t* s_ids = s_len + U;  // [ids_cap] kept ids of this workgroup's units, slot - ids_base
+  int ids_base = 0;
+  if constexpr (GATED) {
+    __shared__ double s_q[D];
+    __shared__ double s_part[4 * 256];  // quarter sums of one pass
+    __shared__ int s_hist[3 * 256];
+    __shared__ int s_sel_scan[kWavesPerWG + 1];
+    __shared__ int s_wgu[2];            // units of the workgroup's first and last tile
+    uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
+    const int Y0 = split.start(wg0);
+    const int Y1 = split.start(wg0 + kWavesPerWG);
+    if (Y0 < Y1) {
+      {
+        const int x0 = Y0 >> tsh, x1 = (Y1 - 1) >> tsh;  // their blocks
+        for (int uu = tid; uu < U; uu += kThreads) {
+          const int lo = s_prefix[uu], hi = s_prefix[uu + 1];
+          if (lo <= x0 && x0 < hi) s_wgu[0] = uu;
+          if (lo <= x1 && x1 < hi) s_wgu[1] = uu;
+        }
+        __syncthreads();
+      }
+      const int u0 = s_wgu[0], u1 = s_wgu[1];
+      ids_base = s_prefix[u0];
+      auto gate = [&](int u, auto pre_tag) {
+        const int k = s_prefix[u + 1] - s_prefix[u];
+        if (k == 0) return;
+        // the owner holds the unit's first tile
+        const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
+        fused_gate_unit<T, D, kRows, true, decltype(pre_tag)::value>(
+            a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
+            owner == wg, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
+      };
+      // The first unit may use the entry loads; peeled off, so that they are
+      // dead in the loop.
+      gate(u0, BoolTag<true>{});
+      for (int u = u0 + 1; u <= u1; ++u) gate(u, BoolTag<false>{});
+    }
+    // Units without a kept block (a sequence of length 0) belong to nobody:
+    // workgroup 0 writes their (empty) selection.
+    if (blockIdx.x == 0) {
+      for (int u = tid; u < U; u += kThreads) {
+        if (s_prefix[u] != s_prefix[u + 1]) continue;
+        for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)u * a.k_max + i] = -1;
+        a.sel_cnt_out[u] = 0;
+      }
+    }
+  }
   const int y0 = split.start(w), y1 = split.start(w + 1);
   if (y0 >= y1) return;
 
@@ -156,7 +215,9 @@ void decode_multi_kernel(DecodeArgs a) {
       int nv = 0, jj = 0;
       int64_t off = 0;
       if (slot < s_prefix[u + 1] - s_prefix[u]) {
-        const int j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
+        int j;
+        if constexpr (GATED) j = s_ids[s_prefix[u] - ids_base + slot];
+        else j = sparse ? a.sel_idx[(int64_t)u * a.k_max + slot] : slot;
         if (j >= 0 && j < NB && (int64_t)j * S < L) {
           nv = min(S, L - j * S);
           jj = j;
@@ -454,12 +515,14 @@ __global__ __launch_bounds__(D) void decode_multi_combine_kernel(CombineArgs a) 
   if (a.lse && dim == 0) a.lse[oidx] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
 }
 
-template <typename T, int D>
-const void* multi_fn() { return (const void*)&decode_multi_kernel<T, D>; }
+template <typename T, int D, bool GATED>
+const void* multi_fn() { return (const void*)&decode_multi_kernel<T, D, GATED>; }
 
+template <bool GATED>
 const void* multi_kernel(int dtype, int D) {
-  if (dtype == 1) return D == 64 ? multi_fn<uint16_t, 64>() : multi_fn<uint16_t, 128>();
-  return D == 64 ? multi_fn<float, 64>() : multi_fn<float, 128>();
+  if (dtype == 1)
+    return D == 64 ? multi_fn<uint16_t, 64, GATED>() : multi_fn<uint16_t, 128, GATED>();
+  return D == 64 ? multi_fn<float, 64, GATED>() : multi_fn<float, 128, GATED>();
 }
 
 }  // namespace
@@ -474,8 +537,23 @@ hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
   DecodeArgs args = a;
   void* params[] = {&args};
   const size_t smem = (size_t)(2 * U + 1 + kWavesPerWG + 1) * sizeof(int);
-  return hipLaunchKernel(multi_kernel(a.dtype, a.D), dim3(a.W / kWavesPerWG), dim3(kThreads),
-                         params, smem, stream);
+  return hipLaunchKernel(multi_kernel<false>(a.dtype, a.D), dim3(a.W / kWavesPerWG),
+                         dim3(kThreads), params, smem, stream);
+}
+
+hipError_t launch_gated_decode_multi(const DecodeArgs& a, hipStream_t stream) {
+  const int U = a.B * a.Hkv;
+  DecodeArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(multi_kernel<true>(a.dtype, a.D), dim3(a.W / kWavesPerWG),
+                         dim3(kThreads), params, gated_decode_smem_bytes(U, a.NB, a.ids_cap),
+                         stream);
+}
+
+size_t gated_decode_multi_static_smem(int dtype, int D) {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, multi_kernel<true>(dtype, D)) != hipSuccess) return (size_t)-1;
+  return attr.sharedSizeBytes;
 }
 
 hipError_t launch_decode_multi_combine(const CombineArgs& a, hipStream_t stream) {

@@ -73,8 +73,11 @@ int decode_max_waves(int dtype, int D, int G);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 // The same kernel with the gate and top-k fused in (a.pooled set).
 hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream);
-// Dynamic LDS bytes the gated kernel needs, and the ids one workgroup must hold.
+// Dynamic LDS bytes the gated kernels need (single- and multi-token: the same
+// layout), the ids one workgroup must hold, and the gated kernels' static LDS.
 size_t gated_decode_smem_bytes(int U, int NB, int ids_cap);
+size_t gated_decode_static_smem(int dtype, int D, int G);
+size_t gated_decode_multi_static_smem(int dtype, int D);
 int gated_decode_ids_cap(int U, int k_max, int W);
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 
@@ -83,6 +86,8 @@ hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 constexpr int kMultiRows = 16;
 size_t decode_multi_workspace_bytes(int B, int Hkv, int D, int wmax);
 hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);
+// The same with the gate fused in (a.pooled set, as launch_gated_decode_partial).
+hipError_t launch_gated_decode_multi(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_multi_combine(const CombineArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- gate

@@ -36,226 +36,11 @@
 #include <atomic>
 
 #include "decode_common.h"
+#include "gate_phase.h"
 #include "select_device.h"
 
 namespace seer {
 namespace {
-
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
-
-// The value a unit's block count needs besides its length: the explicit kept
-// count top_k[b] (fused gate) or the given selection's count sel_cnt[u].
-template <bool GATED>
-__device__ __forceinline__ int unit_aux(const DecodeArgs& a, int u) {
-  if constexpr (GATED) return a.top_k ? a.top_k[u / a.Hkv] : 0;
-  return a.sel_idx ? a.sel_cnt[u] : 0;
-}
-
-// Blocks a unit contributes: its kept count (given, or from the keep rule when
-// the gate is fused in), or all its blocks when dense.
-// L: the unit's sequence length; aux: unit_aux of the unit.
-template <bool GATED>
-__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int L, int aux) {
-  if constexpr (GATED) {
-    const int n = seq_blocks(L, a.S, a.NB);
-    return kept_count_forced_of(n, a.top_k != nullptr, aux, a.keep_num, a.keep_den, a.k_max,
-                                forced_count(n, a.force_first, a.force_last));
-  }
-  if (a.sel_idx) return aux < 0 ? 0 : (aux > a.k_max ? a.k_max : aux);
-  return seq_blocks(L, a.S, a.NB);
-}
-
-// The first gate pass's pooled-table and query loads of one unit, issued at
-// kernel entry, before the plan says which unit the workgroup gates: u is the
-// unit it gates first when every unit keeps as many blocks as any other (the
-// plan then confirms it; otherwise the values go unused).  Lane (qd, jq) holds
-// dimensions qd*D/4 .. of blocks 4jq .. 4jq+3, as fused_scores loads them.
-template <typename T, int D, int G>
-struct GatePreload {
-  int u;
-  float pv[D / 4][4];
-  T qr[G];
-};
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void issue_gate_preload(const DecodeArgs& a, int u,
-                                                   GatePreload<T, D, G>& pre) {
-  constexpr int DQ = D / 4;
-  const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
-  const int NB = a.NB;
-  pre.u = u;
-  // Aligned 16-byte loads need NB % 4 == 0; otherwise every lane re-reads the
-  // table's first 16 bytes (in bounds, unused) and the gate loads for itself.
-  const bool vec4 = NB % 4 == 0;
-  const float* row = vec4 ? a.pooled + ((int64_t)u * D + qd * DQ) * NB + min(4 * jq, NB - 4)
-                          : a.pooled;
-  const int64_t step = vec4 ? NB : 0;
-#pragma unroll
-  for (int i = 0; i < DQ; ++i) {
-    const float4 v = *(const float4*)(row + i * step);
-    pre.pv[i][0] = v.x; pre.pv[i][1] = v.y; pre.pv[i][2] = v.z; pre.pv[i][3] = v.w;
-  }
-  const int b = u / a.Hkv, g = u - b * a.Hkv;
-  const T* qg = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D + min(tid, D - 1);
-#pragma unroll
-  for (int h = 0; h < G; ++h) pre.qr[h] = qg[h * D];
-}
-
-// VEC consecutive pooled values of one dimension row (one 4*VEC-byte load).
-template <int VEC>
-__device__ __forceinline__ void load_pooled_vec(const float* p, float (&x)[VEC]) {
-  if constexpr (VEC == 4) {
-    const float4 v = *(const float4*)p;
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  } else if constexpr (VEC == 2) {
-    const float2 v = *(const float2*)p;
-    x[0] = v.x; x[1] = v.y;
-  } else {
-    x[0] = *p;
-  }
-}
-
-// Scores of unit (b, g)'s n blocks into s_key (order keys), VEC blocks per
-// lane per load: wave qd of the workgroup sums the dimensions qd*D/4 ..
-// qd*D/4 + D/4 - 1 of 64*VEC blocks per pass (one sequential fp64 FMA chain
-// per block), and the four partial sums of a block are added in quarter order
-// through LDS:
-//   s_j = (((c0 + c1) + c2) + c3) / sqrt(D),  c_q = sum_i qbar_i P_ij over quarter q,
-// qbar = sum of the group's query heads in head order (fp64): the same
-// arithmetic as the gate kernel.  The first pass's pooled loads go out before
-// the query's, so both round trips overlap.  VEC consecutive blocks are one
-// aligned load when NB is a multiple of VEC (no load crosses the table's end).
-// With PRE and use_pre the first pass takes its pooled and query values from
-// `pre` (VEC = 4 only), loaded at kernel entry.
-template <typename T, int D, int G, int VEC, bool PRE>
-__device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, const float* pu,
-                                             int n, double* s_q, double* s_part,
-                                             uint64_t* s_key, const GatePreload<T, D, G>& pre,
-                                             bool use_pre) {
-  constexpr int DQ = D / 4, PASS = 64 * VEC;
-  const int NB = a.NB;
-  const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
-  const double inv = 1.0 / sqrt((double)D);
-  // One pass over blocks j0 .. j0 + PASS - 1; the first (FIRST) also sums the
-  // query and may take the entry loads (peeled, so that they are dead after).
-  auto pass = [&](int j0, auto first_tag) {
-    constexpr bool FIRST = decltype(first_tag)::value;
-    // block ids past n are clamped to a valid, aligned group (read, unused)
-    const int jg = min(j0 + VEC * jq, ((n - 1) / VEC) * VEC);
-    float pv[DQ][VEC];
-    const float* row = pu + (int64_t)qd * DQ * NB + jg;
-    bool from_pre = false;
-    if constexpr (FIRST && PRE && VEC == 4) from_pre = use_pre;
-    if (from_pre) {
-#pragma unroll
-      for (int i = 0; i < DQ; ++i)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) pv[i][e] = pre.pv[i][e & 3];
-    } else {
-#pragma unroll
-      for (int i = 0; i < DQ; ++i) load_pooled_vec<VEC>(row + (int64_t)i * NB, pv[i]);
-    }
-    if constexpr (FIRST) {
-      if (tid < D) {
-        const T* qg = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D + tid;
-        double x[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          T qv;
-          if constexpr (PRE) qv = use_pre ? pre.qr[h] : qg[h * D];
-          else qv = qg[h * D];
-          if constexpr (sizeof(T) == 2) x[h] = (double)__uint_as_float((uint32_t)qv << 16);
-          else x[h] = (double)qv;
-        }
-        double sq = x[0];
-#pragma unroll
-        for (int h = 1; h < G; ++h) sq = sq + x[h];
-        s_q[tid] = sq;
-      }
-      __syncthreads();
-    }
-    // every load is in flight before the chains; values widen only where used
-    __builtin_amdgcn_sched_barrier(0);
-    double c[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) c[e] = 0.0;
-#pragma unroll
-    for (int i = 0; i < DQ; ++i)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) c[e] = fma(s_q[qd * DQ + i], (double)pv[i][e], c[e]);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) s_part[qd * PASS + VEC * jq + e] = c[e];
-    __syncthreads();
-    for (int t = tid; t < PASS; t += kThreads) {
-      const int j = j0 + t;
-      if (j < n) {
-        const double sc = ((s_part[t] + s_part[PASS + t]) + s_part[2 * PASS + t]) +
-                          s_part[3 * PASS + t];
-        s_key[j] = order_key(sc * inv);
-      }
-    }
-    __syncthreads();
-  };
-  pass(0, BoolTag<true>{});  // n >= 1
-  for (int j0 = PASS; j0 < n; j0 += PASS) pass(j0, BoolTag<false>{});
-}
-
-// Gate of unit u inside a decode workgroup (the fused mode): the fp64 scores
-// of its n blocks (fused_scores), then its k kept ids, ascending, into dst
-// (LDS).  The owner workgroup of the unit also writes the scores, ids and
-// count out.
-template <typename T, int D, int G, bool PRE>
-__device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
-                                                int32_t* dst,
-                                                bool owner, uint64_t* s_key, double* s_q,
-                                                double* s_part, int* s_hist,
-                                                int* s_scan, const GatePreload<T, D, G>& pre) {
-  const int tid = threadIdx.x;
-  const int b = u / a.Hkv, g = u - b * a.Hkv;
-  const int NB = a.NB;
-  const float* pu = a.pooled + (int64_t)u * D * NB;
-  const bool use_pre = u == pre.u;  // the entry loads are this unit's (uniform)
-  if (NB % 4 == 0) fused_scores<T, D, G, 4, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
-  else if (NB % 2 == 0) fused_scores<T, D, G, 2, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
-  else fused_scores<T, D, G, 1, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
-  // forced blocks rank above every score while the selection runs
-  const bool forced = a.force_first || a.force_last;  // uniform
-  uint64_t key_first = 0, key_last = 0;
-  if (forced) {
-    key_first = s_key[0];
-    key_last = s_key[n - 1];
-    __syncthreads();
-    if (tid == 0) {
-      if (a.force_first) s_key[0] = kForcedKey;
-      if (a.force_last) s_key[n - 1] = kForcedKey;
-    }
-    __syncthreads();
-  }
-  if (k >= n) {
-    for (int i = tid; i < n; i += kThreads) dst[i] = i;
-  } else {
-    block_topk_ids<kThreads>(s_key, n, k, s_hist, s_scan, dst);
-  }
-  __syncthreads();
-  if (forced) {
-    if (tid == 0) {  // the forced blocks' own scores go out
-      s_key[0] = key_first;
-      s_key[n - 1] = key_last;
-    }
-    __syncthreads();
-  }
-  if (owner) {
-    int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
-    for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
-    if (tid == 0) a.sel_cnt_out[u] = k;
-    double* sc = a.scores + (int64_t)u * NB;
-    for (int j = tid; j < n; j += kThreads) sc[j] = key_score(s_key[j]);
-  }
-  __syncthreads();  // s_key, s_q and s_part are reused by the next unit
-}
 
 template <typename T, int D, int G, bool GATED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -301,7 +86,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int aux_f = unit_aux<GATED>(a, u_f);
     // (wg0 * U < 2^31: fewer than 2^15 waves, at most 2^13 units)
     if constexpr (GATED)
-      issue_gate_preload<T, D, G>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
+      issue_gate_preload<T, D, G, false>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
     int local = 0;
     for (int u = u_lo; u < u_hi; ++u) {
       const int L = u == u_lo ? L_f : a.lens[u / a.Hkv];
@@ -372,7 +157,7 @@ void decode_partial_kernel(DecodeArgs a) {
         if (k == 0) return;
         // the owner holds the unit's first tile
         const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
-        fused_gate_unit<T, D, G, decltype(pre_tag)::value>(
+        fused_gate_unit<T, D, G, false, decltype(pre_tag)::value>(
             a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
             owner == wg, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
       };
@@ -934,6 +719,13 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   void* params[] = {&args};
   return hipLaunchKernel(fn, dim3(a.W / kWavesPerWG), dim3(kThreads), params,
                          prefix_smem_bytes(U), stream);
+}
+
+size_t gated_decode_static_smem(int dtype, int D, int G) {
+  const void* fn = gated_kernel(dtype, D, G);
+  hipFuncAttributes attr;
+  if (!fn || hipFuncGetAttributes(&attr, fn) != hipSuccess) return (size_t)-1;
+  return attr.sharedSizeBytes;
 }
 
 size_t gated_decode_smem_bytes(int U, int NB, int ids_cap) {

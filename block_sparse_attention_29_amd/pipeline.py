@@ -111,9 +111,15 @@ class DecodeState:
 
     def step(self, q: torch.Tensor, lens: torch.Tensor):
         """Gate, select and attend: one decode step over a built pooled table
-        (the parameter-free gate fused into the attention kernel)."""
-        if self.gate_weights is not None or self.T > 1:
+        (the parameter-free gate fused into the attention kernel where that
+        pays, for one or several query tokens)."""
+        if self.gate_weights is not None:
             return self.step_unfused(q, lens)
+        if self.T > 1:
+            seer.multi_gated_sparse_decode(self.shape, self.T, q, self.kv, lens, self.pooled,
+                                           self.rule, self.k_max, self.scores, self.sel_idx,
+                                           self.sel_cnt, self.out, self.lse, self.workspace)
+            return self.out, self.lse
         seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,
                                  self.lse, self.workspace)

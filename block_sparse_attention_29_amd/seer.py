@@ -44,6 +44,8 @@ EXPORTS = (
     "seer_multi_sparse_decode",
     "seer_multi_sparse_decode_partial",
     "seer_multi_sparse_decode_combine",
+    "seer_multi_gated_sparse_decode",
+    "seer_multi_gated_sparse_decode_partial",
     "seer_keep_blocks",
     "seer_status_str",
     "seer_last_error",
@@ -161,7 +163,13 @@ def load(path: str = LIB_PATH):
     lib.seer_gated_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
                                                      ctypes.c_float, _P, _P, _P, _P,
                                                      ctypes.c_size_t, _P]
-    lib.seer_gated_decode_is_fused.argtypes = [SP, RP, _I32, ctypes.POINTER(ctypes.c_int32)]
+    lib.seer_gated_decode_is_fused.argtypes = [SP, _I32, RP, _I32, ctypes.POINTER(ctypes.c_int32)]
+    lib.seer_multi_gated_sparse_decode.argtypes = [SP, _I32, _P, KP, _P, _P, RP, _I32,
+                                                   ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_size_t, _P]
+    lib.seer_multi_gated_sparse_decode_partial.argtypes = [SP, _I32, _P, KP, _P, _P, RP, _I32,
+                                                           ctypes.c_float, _P, _P, _P, _P,
+                                                           ctypes.c_size_t, _P]
     lib.seer_keep_blocks.argtypes = [_I32, _I32, _I32]
     lib.seer_keep_blocks.restype = _I32
     lib.seer_status_str.argtypes = [_I32]
@@ -409,14 +417,45 @@ def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.T
                                           _ptr(workspace), workspace.numel(), _stream()))
 
 
-def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int) -> bool:
-    """seer_gated_decode_is_fused: whether gated_sparse_decode selects inside
-    the attention kernel for this shape and rule on the current device."""
+def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int, tokens: int = 1) -> bool:
+    """seer_gated_decode_is_fused: whether gated_sparse_decode (tokens = 1) or
+    multi_gated_sparse_decode selects inside the attention kernel for this
+    shape and rule on the current device."""
     lib = load()
     f = ctypes.c_int32(0)
-    _check(lib.seer_gated_decode_is_fused(ctypes.byref(shape), ctypes.byref(rule), k_max,
+    _check(lib.seer_gated_decode_is_fused(ctypes.byref(shape), tokens, ctypes.byref(rule), k_max,
                                           ctypes.byref(f)))
     return bool(f.value)
+
+
+def multi_gated_sparse_decode(shape: Shape, tokens: int, q: torch.Tensor, kv: KV,
+                              lens: torch.Tensor, pooled: torch.Tensor, rule: Select, k_max: int,
+                              scores: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                              out: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                              workspace: torch.Tensor, softmax_scale: float = 0.0):
+    """seer_multi_gated_sparse_decode (out None: the _partial entry alone)."""
+    lib = load()
+    _need_q(shape, q, tokens)
+    U = shape.batch * shape.num_kv_heads
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    if out is None:
+        _check(lib.seer_multi_gated_sparse_decode_partial(
+            ctypes.byref(shape), tokens, _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
+            ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+            _ptr(workspace), workspace.numel(), _stream()))
+        return
+    rows = shape.batch * tokens * shape.num_q_heads
+    _need(out, torch.float32, rows * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, rows, "lse")
+    _check(lib.seer_multi_gated_sparse_decode(
+        ctypes.byref(shape), tokens, _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
+        ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
 
 
 def gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,

@@ -277,13 +277,14 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
  *  (read at every call; the results do not depend on it).
  * _partial: the first launch(es) alone (gate + partial results in the
  * workspace, selections written); seer_sparse_decode_combine finishes it. */
-/* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode with
- * this shape, rule and k_max selects inside the attention kernel on the
- * current device, 0 if it runs the gate kernel first (no launch; results are
- * the same either way).  SEER_ERR_INVALID_ARG for NULL pointers or k_max
- * outside [1, max_blocks]. */
-seer_status seer_gated_decode_is_fused(const seer_shape* shape, const seer_select* rule,
-                                       int32_t k_max, int32_t* fused);
+/* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode
+ * (tokens = 1) or seer_multi_gated_sparse_decode (tokens > 1) with this shape,
+ * rule and k_max selects inside the attention kernel on the current device,
+ * 0 if it runs the gate kernel first (no launch; results are the same either
+ * way).  SEER_ERR_INVALID_ARG for NULL pointers, k_max outside [1,
+ * max_blocks] or a token count outside [1, 16 / G]. */
+seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
+                                       const seer_select* rule, int32_t k_max, int32_t* fused);
 seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                                      const int32_t* lens, const float* pooled,
                                      const seer_select* rule, int32_t k_max,
@@ -349,6 +350,27 @@ seer_status seer_multi_sparse_decode_partial(const seer_shape* shape, int32_t to
 seer_status seer_multi_sparse_decode_combine(const seer_shape* shape, int32_t tokens, float* out,
                                              float* lse, const void* workspace,
                                              size_t workspace_bytes, hipStream_t stream);
+
+/* seer_multi_gated_sparse_decode -- one decode step of T new query tokens
+ * from the pooled table: seer_multi_gate_select followed by
+ * seer_multi_sparse_decode on its selection, with bit-identical results
+ * (scores, sel_idx, sel_cnt, out, lse), the gate fused into the attention
+ * kernel under the same conditions as seer_gated_sparse_decode (each
+ * workgroup selects the units it streams; otherwise the gate kernel runs
+ * first).  Arguments as those two calls; workspace:
+ * seer_multi_sparse_decode_workspace_size bytes.
+ * _partial: the selection and the partial results alone;
+ * seer_multi_sparse_decode_combine finishes it. */
+seer_status seer_multi_gated_sparse_decode(
+    const seer_shape* shape, int32_t tokens, const void* q, const seer_kv* kv,
+    const int32_t* lens, const float* pooled, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, float* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+seer_status seer_multi_gated_sparse_decode_partial(
+    const seer_shape* shape, int32_t tokens, const void* q, const seer_kv* kv,
+    const int32_t* lens, const float* pooled, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /* Host helper: max(1, min(n, ceil(n * keep_num / keep_den))), or -1 for bad
  * arguments (n < 1, keep_num < 1, keep_den < keep_num). */

@@ -156,3 +156,57 @@ def test_query_shape_checked():
     with pytest.raises(ValueError):
         seer.multi_sparse_decode_partial(st.shape, 2, case.q, st.kv, case.lens, st.sel_idx,
                                          st.sel_cnt, st.k_max, st.workspace)
+
+
+@pytest.mark.parametrize("name", sorted(CASES) + ["spec4_32k"])
+def test_multi_gated_equals_separate_calls_bitwise(name, monkeypatch):
+    """The multi-token step with the gate fused into the attention kernel
+    writes exactly what the gate call followed by the attention calls writes
+    (scores, ids, counts, out, lse); the fused kernel is forced."""
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+    wl = CASES[name] if name in CASES else WORKLOADS[name].with_(batch=2)
+    print(f"[case] multi gated vs separate {name}", flush=True)
+    case = make_case(wl, "cuda")
+    fused = state_for(case, query_tokens=wl.query_tokens)
+    sep = state_for(case, query_tokens=wl.query_tokens)
+    for st in (fused, sep):
+        st.build_pool(case.lens)
+    fused.step(case.q, case.lens)
+    sep.step_unfused(case.q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
+
+
+@pytest.mark.parametrize("rule", [dict(force_first=True), dict(force_first=True, force_last=True)],
+                         ids=["first", "both"])
+def test_multi_gated_forced_blocks(rule, monkeypatch):
+    """Forced blocks in the fused multi-token gate: bitwise the separate calls,
+    and the oracle's selection."""
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+    wl = CASES["paged_g5_t2"]
+    case = make_case(wl, "cuda")
+    fused = state_for(case, query_tokens=wl.query_tokens, **rule)
+    sep = state_for(case, query_tokens=wl.query_tokens, **rule)
+    for st in (fused, sep):
+        st.build_pool(case.lens)
+    fused.step(case.q, case.lens)
+    sep.step_unfused(case.q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
+
+
+def test_multi_fusion_policy():
+    """Several tokens follow the single-token rule: fused at 4 tokens of
+    sparse90_32k's shape, not with more units than workgroups."""
+    from block_sparse_attention_29_amd import seer
+    from tests.test_gpu_parity import DT
+    for name, want in [("spec4_32k", True), ("paged_var", False)]:
+        wl = WORKLOADS[name]
+        T = 4 if name == "spec4_32k" else 2
+        shape = seer.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, wl.max_blocks, DT[wl.dtype])
+        k_max = seer.keep_blocks(wl.max_blocks, *wl.keep)
+        rule = seer.make_select(keep=wl.keep)
+        assert seer.gated_decode_is_fused(shape, rule, k_max, T) == want, name
