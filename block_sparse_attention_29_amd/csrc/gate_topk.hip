@@ -343,15 +343,21 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
   __shared__ int s_scan[NT / 64 + 1];
   const int tid = threadIdx.x;
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
-  const int n = seq_blocks(a.lens[b], a.S, a.NB);
   const double* sc = a.scores + (int64_t)u * a.NB;
-  // four loads in flight per thread before their keys are stored
-  for (int j0 = tid; j0 < n; j0 += 4 * NT) {
-    double x[4];
+  // The first 8 * NT scores are requested with the length (ids clamped into
+  // the unit's row of NB; those past n are never used): one round trip.
+  double x[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = sc[min(j0 + e * NT, n - 1)];
+  for (int e = 0; e < 8; ++e) x[e] = sc[min(tid + e * NT, a.NB - 1)];
+  const int n = seq_blocks(a.lens[b], a.S, a.NB);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < 8; ++e)
+    if (tid + e * NT < n) s_key[tid + e * NT] = order_key(x[e]);
+  for (int j0 = tid + 8 * NT; j0 < n; j0 += 8 * NT) {  // longer tables: eight at a time
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[min(j0 + e * NT, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
       if (j0 + e * NT < n) s_key[j0 + e * NT] = order_key(x[e]);
   }
   __syncthreads();

@@ -68,11 +68,14 @@ __global__ __launch_bounds__(D) void pool_append_kernel(PoolArgs a) {
   const int u = blockIdx.x, i = threadIdx.x;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int64_t cap = (int64_t)a.NB * a.S;
+  // the open sum is requested with the lengths (one round trip for both; the
+  // empty asm keeps the compiler from sinking the load past the early return)
+  double acc = a.open_sum[(int64_t)u * D + i];
+  __asm__ volatile("" ::: "memory");
   const int lo = a.lens_old[b];
   int hi = a.lens_new[b];
   if (hi > cap) hi = (int)cap;
   if (lo < 0 || lo >= hi) return;
-  double acc = a.open_sum[(int64_t)u * D + i];
   for (int t = lo; t < hi; ++t) {
     const int j = t / a.S, pos = t - j * a.S;
     const int64_t r0 = block_row0(a, b, g, j, D);
