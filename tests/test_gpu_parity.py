@@ -548,3 +548,29 @@ def test_fusion_policy(name, want, monkeypatch):
     assert not seer.gated_decode_is_fused(shape, rule, k_max)
     monkeypatch.setenv("SEER_FUSED_GATE", "1")
     assert seer.gated_decode_is_fused(shape, rule, k_max)      # these all fit in LDS
+
+
+def test_usage_example():
+    """The decode loop as the documentation shows it: build the pooled table,
+    step, write the next token's K/V, append, step again; the second step
+    equals a step on a state built from scratch at the new lengths."""
+    torch.manual_seed(3)
+    B, Hq, Hkv, d, S, NB = 2, 8, 2, 128, 64, 20
+    k = torch.randn(B, Hkv, NB * S, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, Hkv, NB * S, d, device="cuda").to(torch.bfloat16)
+    lens = torch.tensor([700, 1111], dtype=torch.int32, device="cuda")
+    q = torch.randn(B, Hq, d, device="cuda").to(torch.bfloat16)
+    kw = dict(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, block_size=S,
+              max_blocks=NB, dtype=torch.bfloat16, k=k, v=v, keep=(1, 10))
+    st = DecodeState(**kw)
+    st.build_pool(lens)
+    out, lse = st.step(q, lens)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    st.append(lens, lens + 1)
+    st.step(q, lens + 1)
+    fresh = DecodeState(**kw)
+    fresh.build_pool(lens + 1)
+    fresh.step(q, lens + 1)
+    torch.cuda.synchronize()
+    for attr in ("pooled", "scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(st, attr), getattr(fresh, attr)), attr
