@@ -25,6 +25,118 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 
+// Largest n that wave_topk_ids takes (16 keys per lane).
+constexpr int kWaveSelectMax = 1024;
+
+// LDS operations of one wave complete in issue order; this keeps the compiler
+// from moving them across the point (no workgroup barrier involved).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// AND (AND_ = true) or OR of a 32-bit value over the 64 lanes, in every lane.
+template <bool AND_>
+__device__ __forceinline__ uint32_t wave_bits(uint32_t x) {
+  auto op = [](uint32_t p, uint32_t q) { return AND_ ? (p & q) : (p | q); };
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xF, 0xF, true));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xF, 0xF, true));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xF, 0xF, true));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xF, 0xF, true));
+  return op(op((uint32_t)readlane_i((int)x, 0), (uint32_t)readlane_i((int)x, 16)),
+            op((uint32_t)readlane_i((int)x, 32), (uint32_t)readlane_i((int)x, 48)));
+}
+
+// The selection of block_topk_ids (select_device.h) by one wave, for n <= kWaveSelectMax:
+// the ids of the k largest keys of s_key[0..n) (ties to the lower id),
+// ascending, to out[0..k).  Requires 0 < k < n.  Called by the 64 lanes of
+// one wave only -- no workgroup barrier, so the other waves of the workgroup
+// need not take part; s_hist: 256 ints of LDS this wave alone uses.  Lane l
+// owns the contiguous ids [l*m, l*m + m); each 8-bit pass histograms the
+// digit of the keys still matching the chosen prefix with LDS atomics, and a
+// wave scan of the bins from the top finds the digit holding the krem-th
+// largest key.  The kept set and its order are unique, so the output is the
+// workgroup version's bit for bit.
+__device__ void wave_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int m = (n + 63) / 64;
+  const int lo = min(n, lane * m), hi = min(n, lo + m);
+
+  uint64_t kand = ~0ull, kor = 0;
+  for (int j = lo; j < hi; ++j) {
+    const uint64_t key = s_key[j];
+    kand &= key;
+    kor |= key;
+  }
+  kand = ((uint64_t)wave_bits<true>((uint32_t)(kand >> 32)) << 32) | wave_bits<true>((uint32_t)kand);
+  kor = ((uint64_t)wave_bits<false>((uint32_t)(kor >> 32)) << 32) | wave_bits<false>((uint32_t)kor);
+  const uint64_t diff = kand ^ kor;
+
+  int top = diff ? 63 - __builtin_clzll(diff) : -1;  // highest bit where keys differ
+  uint64_t mask = top >= 63 ? 0ull : (~0ull << (top + 1));
+  uint64_t prefix = kand & mask;
+  int krem = k;
+  while (top >= 0) {
+    const int shift = top > 7 ? top - 7 : 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_hist[4 * lane + r] = 0;
+    wave_lds_sync();
+    for (int j = lo; j < hi; ++j) {
+      const uint64_t key = s_key[j];
+      if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 255)], 1);
+    }
+    wave_lds_sync();
+    // lane l holds digits 255-4l .. 252-4l (descending)
+    int c[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { c[r] = s_hist[255 - 4 * lane - r]; sum += c[r]; }
+    int larger = wave_incl_scan(sum) - sum;  // keys with a larger digit than this lane's first
+    int pick = -1, nk = 0, pc = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (larger < krem && krem <= larger + c[r]) {
+        pick = 255 - 4 * lane - r;
+        nk = krem - larger;
+        pc = c[r];
+      }
+      larger += c[r];
+    }
+    const int src = __builtin_ctzll(__ballot(pick >= 0));  // exactly one lane picked
+    const int dv = readlane_i(pick, src), cnt = readlane_i(pc, src);
+    krem = readlane_i(nk, src);
+    prefix |= (uint64_t)dv << shift;
+    mask |= (uint64_t)255 << shift;
+    if (cnt == krem) break;  // every remaining candidate is kept
+    top = shift - 1;
+    wave_lds_sync();  // every lane has read the bins before the next pass clears them
+  }
+
+  int gt = 0, eq = 0;
+  for (int j = lo; j < hi; ++j) {
+    const uint64_t mk = s_key[j] & mask;
+    gt += mk > prefix;
+    eq += mk == prefix;
+  }
+  const int packed = gt | (eq << 16);  // n <= 1024: the fields do not overflow
+  const int excl = wave_incl_scan(packed) - packed;
+  int gb = excl & 0xFFFF, eb = excl >> 16;
+  for (int j = lo; j < hi; ++j) {
+    const uint64_t mk = s_key[j] & mask;
+    // (positions are < k by construction; the checks keep every store inside
+    // the k slots whatever the keys hold)
+    if (mk > prefix) {
+      const int pos = gb + min(eb, krem);
+      if (pos < k) out[pos] = j;
+      ++gb;
+    } else if (mk == prefix) {
+      if (eb < krem && gb + eb < k) out[gb + eb] = j;
+      ++eb;
+    }
+  }
+}
+
+
 template <typename T>
 __device__ __forceinline__ double load_as_double(const T* p, int64_t i);
 
@@ -81,6 +193,10 @@ __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, 
   int32_t* dst = UNIFIED ? s_ids : row0;
   if (k >= n) {
     for (int j = tid; j < n; j += NT) dst[j] = j;
+  } else if (NT >= 1024 && n <= kWaveSelectMax) {
+    // one wave selects: with 16 waves a workgroup barrier costs more than the
+    // one wave's extra work (with 4 waves the workgroup select is faster)
+    if (tid < kWave) wave_topk_ids(s_key, n, k, s_hist, dst);
   } else {
     block_topk_ids<NT>(s_key, n, k, s_hist, s_scan, dst);
   }
