@@ -274,6 +274,16 @@ def run_workload(wl, args):
     wall = time.perf_counter() - wall0
     ms_per_step = ms_total / n_steps
     tokens_per_s = wl.batch * T * n_steps / (ms_total / 1e3)
+    # spread: five more replays of the same graph (a decode loop restarts from
+    # the prefill state each time), per-step means
+    reps = []
+    for _ in range(5):
+        if loop:
+            reset_pools()
+        reps.append(timed(g_steps) / n_steps)
+    reps.sort()
+    spread = {"replays": len(reps), "p10_ms": reps[0] + 0.4 * (reps[1] - reps[0]),
+              "p50_ms": reps[2], "p90_ms": reps[3] + 0.6 * (reps[4] - reps[3])}
     del g_steps
 
     # ---- the same steps as three launches (gate kernel, partial, combine);
@@ -493,6 +503,7 @@ def run_workload(wl, args):
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": config,
+        "step_spread": spread,
         "step_hbm_gbps": step_gbps,
         "step_pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "gate_fused": fused,
