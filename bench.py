@@ -111,8 +111,8 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is "
-                                   "described in DESIGN.md but not implemented",
+        print(json.dumps({"error": "the decode path runs on one GPU; sharding it over "
+                                   "several GPUs (by sequence or KV head) is not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
