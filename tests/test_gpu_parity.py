@@ -177,6 +177,38 @@ def test_gated_equals_separate_calls_bitwise(name, monkeypatch):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
 
 
+def test_max_units(monkeypatch):
+    """SEER_MAX_UNITS (sequence, KV head) pairs: 1024 paged sequences of 1..700
+    tokens on 8 KV heads.  Waves cross many units and most units hold one or two
+    partial records.  Every unit's kept count follows the keep rule, sampled
+    units match the oracle, and the fused call (forced: its workgroups gate
+    32 units each) equals the separate calls bitwise."""
+    wl = WORKLOADS["paged_var"].with_(batch=1024, num_q_heads=16, num_kv_heads=8, head_dim=64,
+                                      variable_context=(1, 700), keep=(1, 4))
+    assert wl.batch * wl.num_kv_heads == 8192          # SEER_MAX_UNITS
+    print("[case] max units: 1024 x 8 units", flush=True)
+    case = make_case(wl, "cuda")
+    sep = state_for(case)
+    sep.build_pool(case.lens)
+    monkeypatch.setenv("SEER_FUSED_GATE", "0")
+    sep.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    lens = case.lens.tolist()
+    want = [O.clamp_count(O.keep_count(O.block_count(L, wl.block_size), 1, 4),
+                          O.block_count(L, wl.block_size)) for L in lens]
+    got = sep.sel_cnt.view(wl.batch, wl.num_kv_heads).cpu().numpy()
+    assert (got == np.array(want)[:, None]).all()
+    for (b, g) in units_of(wl, limit=12, seed=7):
+        check_unit(sep, case, case.q, lens, b, g, tag="max units")
+    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+    fused = state_for(case)
+    fused.build_pool(case.lens)
+    fused.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
+
+
 def test_gated_with_a_wide_block_table(monkeypatch):
     """8192 blocks per sequence (the largest table): the gated call (fused
     kernel forced) matches the separate calls and the oracle (its key buffer
