@@ -111,6 +111,24 @@ bool fused_gate_pays(const seer_shape* s, const seer_select* rule, int W) {
   return U <= W / seer::kDecodeWavesPerWG && s->max_blocks <= 256;
 }
 
+// Whether the single-token combine runs one workgroup per query head instead
+// of one per unit: when the units average 8 or more partial records at full
+// width (few, long units: a workgroup per unit leaves most CUs idle and gives
+// each thread long chains of record loads) and there are at least 64 query
+// heads.  Measured per step: 32 units x 8 heads at 131K tokens 49.9 -> 49.0 us,
+// 64 units x 4 heads 18.3 -> 18.0 us; with 512 units (3-4 records each) the
+// 2560 small workgroups cost 2.7 us more, and one unit of 4 heads 3.9 us more.
+// SEER_COMBINE_HEADS=1 or =0 forces either (for tests and measurements; units
+// with at most 32 records merge bit-identically either way, longer ones in a
+// different order).
+bool combine_per_head(const seer_shape* s, int wmax) {
+  const char* env = getenv("SEER_COMBINE_HEADS");
+  if (env && env[0] == '1' && env[1] == 0) return true;
+  if (env && env[0] == '0' && env[1] == 0) return false;
+  const int64_t U = (int64_t)s->batch * s->num_kv_heads;
+  return U * 8 <= wmax && (int64_t)s->batch * s->num_q_heads >= 64;
+}
+
 // Validates a decode call and fills the partial kernel's arguments.
 seer_status prepare_decode(const seer_shape* shape, const void* q, const seer_kv* kv,
                            const int32_t* lens, const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -518,6 +536,7 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
   c.part = (const float*)(ws + seer::decode_part_offset(U));
   c.out = out;
   c.lse = lse;
+  c.per_head = combine_per_head(shape, wmax) ? 1 : 0;
   const hipError_t e = seer::launch_decode_combine(c, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
   return ok();

@@ -55,6 +55,7 @@ struct DecodeArgs {
 struct CombineArgs {
   int32_t B, Hq, Hkv, D, S;
   int32_t tokens;  // multi-token combine: query tokens per sequence
+  int32_t per_head;  // single-token combine: one workgroup per query head (else per unit)
   const int32_t* hdr;
   const int32_t* prefix;
   const float* part;

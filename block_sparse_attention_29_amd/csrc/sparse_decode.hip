@@ -34,6 +34,7 @@
 // and the V registers right after the PV product, so each wave keeps about one
 // tile of loads in flight while it computes.
 #include <atomic>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "gate_phase.h"
@@ -621,6 +622,86 @@ void decode_combine_kernel(CombineArgs a) {
   }
 }
 
+// The same merge with one workgroup per query head and one thread per element,
+// for units with many records (few, long units): a head's records share their
+// (m, l), so each thread loads only its element's values of every record.
+// Records are merged in chunks of up to 64 (8, 16 or 32 when the unit has no
+// more): the chunk's maximum Mc, then its values rescaled by 2^(m_w - M') and
+// summed in record order into the running state, M' = max(M, Mc), which is
+// rescaled once by 2^(M - M').  A unit with at most 64 records is one chunk:
+// the same arithmetic as combine_shot.
+constexpr int kHeadChunk = 64;
+
+template <int D, int G>
+__global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
+  constexpr int REC = G * D + 16;
+  const int u = (int)blockIdx.x / G, h = (int)blockIdx.x - u * G;
+  const int tid = threadIdx.x;  // element of head h
+  const int U = a.B * a.Hkv;
+  const int tsh = 31 - __builtin_clz(a.S / kTile);
+  const int W = a.hdr[0];
+  const int Tot = a.prefix[U] << tsh;
+  const int ylo = a.prefix[u] << tsh, yhi = a.prefix[u + 1] << tsh;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int64_t head = (int64_t)b * a.Hq + (int64_t)g * G + h;
+  if (yhi <= ylo) {  // no tokens: out = 0, lse = -inf
+    a.out[head * D + tid] = 0.f;
+    if (a.lse && tid == 0) a.lse[head] = kNegInf;
+    return;
+  }
+  const int wlo = tile_owner(ylo, W, Tot);
+  const int whi = tile_owner(yhi - 1, W, Tot);
+  const int nw = whi - wlo + 1;
+  const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
+  const EqualSplit sp(Tot, W);
+  float M = kNegInf, l = 0.f, o = 0.f;
+  auto chunk = [&](int t0, auto ch_tag) {
+    constexpr int CH = decltype(ch_tag)::value;
+    const int tn = min(CH, nw - t0);
+    float x[CH], mv[CH], lv[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const float* r = part + (int64_t)(t0 + min(t, tn - 1)) * REC;  // past tn: re-read, unused
+      x[t] = r[h * D + tid];
+      mv[t] = r[G * D + h];
+      lv[t] = r[G * D + 8 + h];
+    }
+    // Waves are only ever empty when there are fewer tiles than waves.
+    uint64_t skip = 0;
+    if (Tot < W)
+      for (int t = 0; t < tn; ++t) skip |= wave_empty(sp, wlo + t0 + t) ? (1ull << t) : 0ull;
+    float Mc = kNegInf;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const bool use = t < tn && !((skip >> t) & 1ull);
+      Mc = use ? fmaxf(Mc, mv[t]) : Mc;
+    }
+    if (Mc == kNegInf) return;  // no valid token in the chunk
+    const float Mn = fmaxf(M, Mc);
+    // Arguments are <= 0 (or -inf, giving 0): the hardware exp2 is accurate there.
+    const float s = __builtin_amdgcn_exp2f(M - Mn);
+    o *= s;
+    l *= s;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      // Records without a valid token (m = -inf) and skipped slots add nothing;
+      // stale slots may hold anything, so they are selected away, not scaled.
+      const bool use = t < tn && !((skip >> t) & 1ull) && mv[t] != kNegInf;
+      const float sc = __builtin_amdgcn_exp2f(mv[t] - Mn);
+      o = use ? fmaf(x[t], sc, o) : o;
+      l = use ? fmaf(lv[t], sc, l) : l;
+    }
+    M = Mn;
+  };
+  if (nw <= 8) chunk(0, std::integral_constant<int, 8>{});
+  else if (nw <= 16) chunk(0, std::integral_constant<int, 16>{});
+  else if (nw <= 32) chunk(0, std::integral_constant<int, 32>{});
+  else
+    for (int t0 = 0; t0 < nw; t0 += kHeadChunk) chunk(t0, std::integral_constant<int, kHeadChunk>{});
+  a.out[head * D + tid] = l > 0.f ? o / l : 0.f;
+  if (a.lse && tid == 0) a.lse[head] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
+}
+
 template <typename T, int D, int G, bool GATED>
 const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G, GATED>; }
 
@@ -654,17 +735,23 @@ const void* pick_kernel(int dtype, int D, int G) {
 const void* partial_kernel(int dtype, int D, int G) { return pick_kernel<false>(dtype, D, G); }
 const void* gated_kernel(int dtype, int D, int G) { return pick_kernel<true>(dtype, D, G); }
 
+template <int D, int G>
+const void* combine_fn(bool per_head) {
+  return per_head ? (const void*)&decode_combine_head_kernel<D, G>
+                  : (const void*)&decode_combine_kernel<D, G>;
+}
+
 template <int D>
-const void* combine_g(int G) {
+const void* combine_g(int G, bool per_head) {
   switch (G) {
-    case 1: return (const void*)&decode_combine_kernel<D, 1>;
-    case 2: return (const void*)&decode_combine_kernel<D, 2>;
-    case 3: return (const void*)&decode_combine_kernel<D, 3>;
-    case 4: return (const void*)&decode_combine_kernel<D, 4>;
-    case 5: return (const void*)&decode_combine_kernel<D, 5>;
-    case 6: return (const void*)&decode_combine_kernel<D, 6>;
-    case 7: return (const void*)&decode_combine_kernel<D, 7>;
-    case 8: return (const void*)&decode_combine_kernel<D, 8>;
+    case 1: return combine_fn<D, 1>(per_head);
+    case 2: return combine_fn<D, 2>(per_head);
+    case 3: return combine_fn<D, 3>(per_head);
+    case 4: return combine_fn<D, 4>(per_head);
+    case 5: return combine_fn<D, 5>(per_head);
+    case 6: return combine_fn<D, 6>(per_head);
+    case 7: return combine_fn<D, 7>(per_head);
+    case 8: return combine_fn<D, 8>(per_head);
   }
   return nullptr;
 }
@@ -755,10 +842,13 @@ hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream) 
 
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  const void* fn = a.D == 64 ? combine_g<64>(G) : a.D == 128 ? combine_g<128>(G) : nullptr;
+  const bool ph = a.per_head != 0;
+  const void* fn = a.D == 64 ? combine_g<64>(G, ph) : a.D == 128 ? combine_g<128>(G, ph) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   CombineArgs args = a;
   void* params[] = {&args};
+  if (ph)
+    return hipLaunchKernel(fn, dim3(a.B * a.Hq), dim3(a.D), params, 0, stream);
   return hipLaunchKernel(fn, dim3(a.B * a.Hkv), dim3(kCombineThreads), params, 0, stream);
 }
 

@@ -244,7 +244,13 @@ seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const see
  * _partial streams the kept K/V and leaves per-split partial results in the
  * workspace (with the split plan); _combine reads them and merges them by
  * log-sum-exp into out/lse.  _partial followed by _combine on the same
- * workspace and stream is exactly seer_sparse_decode. */
+ * workspace and stream is exactly seer_sparse_decode.
+ * The merge runs one workgroup per (sequence, KV head), or one per query head
+ * when the units are few for the device (at least 8 partial results each on
+ * average) and the query heads at least 64; the environment variable
+ * SEER_COMBINE_HEADS=1 or =0 forces either (read at every call; a head with
+ * more than 32 partial results is merged in another order, so its output may
+ * differ in the last bits). */
 seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
                                        const int32_t* lens, const int32_t* sel_idx,
                                        const int32_t* sel_cnt, int32_t k_max,

@@ -94,10 +94,41 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("heads", ["0", "1"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_full_chain_small(name):
+def test_full_chain_small(name, heads, monkeypatch):
+    """The whole step against the oracle, with the combine run per unit
+    (heads=0) and per query head (heads=1) on every shape."""
+    monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
     wl = SMALL[name]
-    print(f"[case] full chain {name}", flush=True)
+    print(f"[case] full chain {name} combine per head {heads}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case)
+    st.build_pool(case.lens)
+    st.step(case.q, case.lens)
+    torch.cuda.synchronize()
+    lens = case.lens.tolist()
+    for (b, g) in units_of(wl):
+        check_unit(st, case, case.q, lens, b, g, tag=name)
+
+
+FEW_UNITS = {
+    # one 32K sequence on 8 KV heads, 4K budget: 1024 tiles on 1024 waves, so
+    # every unit merges ~128 one-tile records (per head: two chunks of 64)
+    "budget_b1": WORKLOADS["budget_32k"].with_(batch=1),
+    # one 8K sequence at 90% sparsity: fewer tiles than waves, so empty waves
+    # sit between the records of a unit
+    "planted_b1": WORKLOADS["planted_8k"].with_(batch=1),
+}
+
+
+@pytest.mark.parametrize("heads", ["0", "1"])
+@pytest.mark.parametrize("name", sorted(FEW_UNITS))
+def test_few_long_units(name, heads, monkeypatch):
+    """Units with many partial records, merged per unit and per query head."""
+    monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
+    wl = FEW_UNITS[name]
+    print(f"[case] few long units {name} combine per head {heads}", flush=True)
     case = make_case(wl, "cuda")
     st = state_for(case)
     st.build_pool(case.lens)
