@@ -118,9 +118,8 @@ bool fused_gate_pays(const seer_shape* s, const seer_select* rule, int W) {
 // heads.  Measured per step: 32 units x 8 heads at 131K tokens 49.9 -> 49.0 us,
 // 64 units x 4 heads 18.3 -> 18.0 us; with 512 units (3-4 records each) the
 // 2560 small workgroups cost 2.7 us more, and one unit of 4 heads 3.9 us more.
-// SEER_COMBINE_HEADS=1 or =0 forces either (for tests and measurements; units
-// with at most 32 records merge bit-identically either way, longer ones in a
-// different order).
+// SEER_COMBINE_HEADS=1 or =0 forces either (for tests and measurements; the
+// two agree to fp32 rounding, not bit for bit).
 bool combine_per_head(const seer_shape* s, int wmax) {
   const char* env = getenv("SEER_COMBINE_HEADS");
   if (env && env[0] == '1' && env[1] == 0) return true;

@@ -248,9 +248,8 @@ seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const see
  * The merge runs one workgroup per (sequence, KV head), or one per query head
  * when the units are few for the device (at least 8 partial results each on
  * average) and the query heads at least 64; the environment variable
- * SEER_COMBINE_HEADS=1 or =0 forces either (read at every call; a head with
- * more than 32 partial results is merged in another order, so its output may
- * differ in the last bits). */
+ * SEER_COMBINE_HEADS=1 or =0 forces either (read at every call; the two
+ * agree to fp32 rounding, not bit for bit). */
 seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
                                        const int32_t* lens, const int32_t* sel_idx,
                                        const int32_t* sel_cnt, int32_t k_max,

@@ -112,6 +112,28 @@ def test_full_chain_small(name, heads, monkeypatch):
         check_unit(st, case, case.q, lens, b, g, tag=name)
 
 
+@pytest.mark.parametrize("name", ["tiny_1k", "paged_small", "long_small", "f32_d128_s128_g1",
+                                  "bf16_d64_g8", "bf16_g3_keep", "f32_g5_paged"])
+def test_combine_modes_agree(name, monkeypatch):
+    """Units with at most 32 partial records (at most W/U + 1 each on these
+    shapes): the merge per unit and per query head runs the same formulas in
+    the same record order, so the two agree to fp32 rounding (they are not
+    bit-identical: the kernels are compiled separately)."""
+    wl = SMALL[name]
+    print(f"[case] combine modes {name}", flush=True)
+    case = make_case(wl, "cuda")
+    res = []
+    for heads in ("0", "1"):
+        monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
+        st = state_for(case)
+        st.build_pool(case.lens)
+        st.step(case.q, case.lens)
+        torch.cuda.synchronize()
+        res.append(st)
+    assert torch.allclose(res[0].out, res[1].out, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(res[0].lse, res[1].lse, rtol=1e-5, atol=1e-6)
+
+
 FEW_UNITS = {
     # one 32K sequence on 8 KV heads, 4K budget: 1024 tiles on 1024 waves, so
     # every unit merges ~128 one-tile records (per head: two chunks of 64)
