@@ -507,6 +507,32 @@ seer_status seer_gated_sparse_decode(const seer_shape* shape, const void* q, con
   return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
 }
 
+seer_status seer_gated_sparse_decode_no_alloc(const seer_shape* shape, const void* q,
+                                              const seer_kv* kv, const int32_t* lens,
+                                              const float* pooled, const seer_select* rule,
+                                              int32_t k_max, float softmax_scale, double* scores,
+                                              int32_t* sel_idx, int32_t* sel_cnt, float* out,
+                                              float* lse, hipStream_t stream) {
+  seer_status st = check_shape(shape);
+  if (st) return st;
+  const int wmax = wave_cap(shape);
+  if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
+  const size_t need = seer::decode_workspace_bytes(
+      shape->batch, shape->num_kv_heads, shape->num_q_heads / shape->num_kv_heads,
+      shape->head_dim, wmax);
+  if (need > seer::kStaticScratchBytes)
+    return fail(SEER_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch, more than the %zu bytes of the static "
+                "scratch; use seer_gated_sparse_decode with a workspace",
+                need, seer::kStaticScratchBytes);
+  hipError_t e = hipSuccess;
+  void* ws = seer::decode_static_scratch(&e);
+  if (!ws) return hip_fail(e, "static scratch address");
+  return seer_gated_sparse_decode(shape, q, kv, lens, pooled, rule, k_max, softmax_scale, scores,
+                                  sel_idx, sel_cnt, out, lse, ws, seer::kStaticScratchBytes,
+                                  stream);
+}
+
 seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
                                        const void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {

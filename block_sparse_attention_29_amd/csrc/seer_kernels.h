@@ -67,6 +67,12 @@ struct CombineArgs {
 size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int wmax);
 size_t decode_part_offset(int U);
 
+// The allocation-free decode call's workspace: a static device array of
+// kStaticScratchBytes per GPU.  Returns its address on the current device
+// (looked up once per device), or nullptr with *err set.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+void* decode_static_scratch(hipError_t* err);
+
 // Number of resident waves of the partial kernel on the current device for
 // this instantiation (0 if the instantiation does not exist).
 int decode_max_waves(int dtype, int D, int G);

@@ -840,6 +840,37 @@ hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream) 
                          gated_decode_smem_bytes(U, a.NB, a.ids_cap), stream);
 }
 
+// ---------------------------------------------------------------- static scratch
+//
+// Device memory of the allocation-free decode call: the same workspace layout
+// as a caller's workspace, in a file-scope array that every GPU the library
+// runs on holds (at its own address) until the process ends.  In host code
+// the array's name only stands in for the symbol; its device address is
+// looked up once per device, with that device current, and kept per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+void* decode_static_scratch(hipError_t* err) {
+  *err = hipSuccess;
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  if (dev < 0 || dev >= kMaxDev) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  // Two threads that get here first on one device look up the same address.
+  if ((*err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return nullptr;
+  if (!p) {
+    *err = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 hipError_t launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const bool ph = a.per_head != 0;

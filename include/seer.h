@@ -21,7 +21,8 @@
  * ---------------------------------
  *  - Every pointer except `shape`/`kv` structs and host-only helpers is a
  *    device pointer.  The caller allocates and owns all memory; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing and keeps no state between calls, except the static
+ *    scratch array of seer_gated_sparse_decode_no_alloc (one per GPU).
  *  - Work is enqueued on `stream` and is asynchronous; no call synchronises.
  *  - Arguments are validated on the host before anything is enqueued: a bad
  *    argument returns SEER_ERR_INVALID_ARG / SEER_ERR_UNSUPPORTED /
@@ -303,6 +304,29 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
                                              int32_t* sel_idx, int32_t* sel_cnt,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream);
+
+/* seer_gated_sparse_decode_no_alloc -- seer_gated_sparse_decode without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The workspace is a static device array of 16 MiB that the
+ * library holds on every GPU it runs on until the process ends; its device
+ * address is looked up once per device, on the first call with that device
+ * current.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine) and writes the same scores, sel_idx, sel_cnt, out and lse as
+ * seer_gated_sparse_decode with a workspace.
+ *  Arguments: as seer_gated_sparse_decode, less the workspace.
+ *  A shape whose workspace (seer_sparse_decode_workspace_size) exceeds 16 MiB
+ *  returns SEER_ERR_WORKSPACE and enqueues nothing.
+ *  Every call on one GPU shares that GPU's array, and the array keeps the
+ *  last call's contents (nothing in it needs to start at zero): calls that
+ *  may overlap on one GPU (several streams, several host threads) race on it
+ *  and must be serialised by the caller. */
+seer_status seer_gated_sparse_decode_no_alloc(const seer_shape* shape, const void* q,
+                                              const seer_kv* kv, const int32_t* lens,
+                                              const float* pooled, const seer_select* rule,
+                                              int32_t k_max, float softmax_scale, double* scores,
+                                              int32_t* sel_idx, int32_t* sel_cnt, float* out,
+                                              float* lse, hipStream_t stream);
 
 /* Several new query tokens per sequence (speculative or chunked decode).
  *
