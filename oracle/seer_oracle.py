@@ -33,12 +33,16 @@ gate but give no weights or internals):
 * order: score descending, ties to the lower block index, -0 equal to +0;
   the kept block ids are reported in ascending order;
 * the new token's key and value are in the cache (its length includes it);
-* a second, learned gate (``learned_gate_scores``) has the shape of the pages'
-  gate network (Linear(d, 256), ReLU, then a 256-wide second layer whose
-  weights are a projection of the query, so the query stays unpooled); its
-  weights are given (seeded, untrained), stored int8 with per-row scales, and
-  its input is a per-block int8 image of the pooled keys with a power-of-two
-  block scale, so that the first layer is an exact integer product;
+* a second, learned gate (``learned_gate_scores``) is the pages' gate network
+  (Linear(d, 256), ReLU, Linear(256, 1)) applied to each block's stored fp32
+  pooled key, with the second layer's weights a projection of the group's
+  query so that the query stays unpooled; its weights are given (seeded,
+  untrained; the first layer stored int8 with per-row scales), and every step
+  runs in fp64 on the exact values;
+* reporting only (nothing is gated on them): the selection the gate would
+  make from the unrounded fp64 block means (``pure_selection``) and the gap
+  between the last kept and the first dropped score in units of the scores'
+  standard deviation (``boundary_gap``);
 * several new query tokens per sequence (T, speculative or chunked decode):
   token t sits at position length-T+t and sees the kept positions up to its
   own (causal), and one selection per KV head serves all T tokens, scored
@@ -237,51 +241,64 @@ def select_blocks(scores: np.ndarray, *, k: Optional[int] = None,
 GATE_HIDDEN = 256  # hidden width of the gate network ("Sparse Attention Reasoning", Step 1)
 
 
-def quantize_blocks(pooled32: np.ndarray):
-    """Per-block int8 image of the stored pooled keys, the learned gate's input.
-
-    pooled32: (n, d) float32.  Returns (q8 (n, d) int8, alpha (n,) float64):
-    alpha_j = 2^e_j with e_j the smallest integer such that
-    127 * 2^e_j >= max_i |P_ji| (e_j = 0 for an all-zero block), and
-    q8_ji = P_ji / alpha_j rounded to the nearest integer, ties to even.  A
-    power-of-two block scale (a shared exponent) makes the scaling exact.
-    """
-    p = np.asarray(pooled32, dtype=np.float32)
-    amax = np.max(np.abs(p), axis=1)
-    f, k = np.frexp(amax)                        # amax = f * 2^k, 0.5 <= f < 1
-    e = np.where(f <= np.float32(127.0 / 128.0), k - 7, k - 6)
-    e = np.where(amax > 0, e, 0).astype(np.int64)
-    q = np.rint(p.astype(np.float64) * np.ldexp(1.0, -e)[:, None]).astype(np.int8)
-    return q, np.ldexp(1.0, e)
-
-
 def learned_gate_scores(q_group: np.ndarray, pooled32: np.ndarray, w1: np.ndarray,
                         w1_scale: np.ndarray, b1: np.ndarray, wq: np.ndarray) -> np.ndarray:
     """Gate scores of one KV head from a two-layer gate network.
 
-    The network has the shape of the gate of "Sparse Attention Reasoning"
-    (Step 1: Linear(hidden, 256), ReLU, Linear(256, 1)) applied to each block's
-    pooled key; the second layer's weights are a projection of the group's
-    query, u = Wq qbar, so that the score depends on the unpooled decode query
-    ("SeerAttention-R", Abstract: a learned gate, query pooling removed):
+    The network is the gate of "Sparse Attention Reasoning" (Step 1:
+    Linear(hidden, 256), ReLU, Linear(256, 1)) applied to each block's pooled
+    key, hidden = d; the second layer's weights are a projection of the
+    group's query, u = Wq qbar, so that the score depends on the unpooled
+    decode query ("SeerAttention-R", Abstract: a learned gate, query pooling
+    removed):
 
-        h_j = relu(z_j),  z_jm = alpha_j * beta_m * (W1_m . q8_j) + b1_m,
-        s_j = u . h_j / sqrt(H),  u_m = Wq_m . qbar,  qbar = sum_h q_h,
+        z_jm = beta_m * (W1_m . P_j) + b1_m,   h_jm = max(z_jm, 0),
+        s_j  = sum_m u_m h_jm,                 u_m = Wq_m . qbar,  qbar = sum_h q_h,
 
-    with (q8, alpha) = quantize_blocks(pooled32), W1 (H, d) int8 with row
-    scales beta = w1_scale (H,) float32, b1 (H,) float32, Wq (H, d) float32,
-    q_group (G, d) float64.  The int8 dot products are exact integers and
-    alpha * beta is exact (a power of two times an fp32 value); the rest is
-    fp64 on the exact values.
+    evaluated in fp64 on the exact values of the stored fp32 pooled keys P
+    (pooled32 (n, d)), W1 (H, d) int8 with row scales beta = w1_scale (H,),
+    b1 (H,), Wq (H, d) and q_group (G, d).
     """
-    q8, alpha = quantize_blocks(pooled32)
-    dots = q8.astype(np.int64) @ np.asarray(w1, dtype=np.int64).T          # (n, H), exact
-    scale = alpha[:, None] * np.asarray(w1_scale, dtype=np.float64)[None, :]
-    z = scale * dots.astype(np.float64) + np.asarray(b1, dtype=np.float64)[None, :]
+    p = np.asarray(pooled32, dtype=np.float32).astype(np.float64)
+    w = np.asarray(w1, dtype=np.int8).astype(np.float64)
+    z = (p @ w.T) * np.asarray(w1_scale, dtype=np.float64)[None, :] \
+        + np.asarray(b1, dtype=np.float64)[None, :]
     h = np.maximum(z, 0.0)
     qbar = np.asarray(q_group, dtype=np.float64).sum(axis=0)
     u = np.asarray(wq, dtype=np.float64) @ qbar
-    return (h @ u) / np.sqrt(float(np.asarray(w1).shape[0]))
+    return h @ u
+
+
+# --------------------------------------------------------------------------
+# Reporting: selection from unrounded block means, boundary gap
+# --------------------------------------------------------------------------
+
+def pure_selection(q_group: np.ndarray, pooled64: np.ndarray, head_dim: int, k: int) -> np.ndarray:
+    """The top-k selection the gate would make from the unrounded fp64 block
+    means (``pool_keys``'s second result) instead of the stored fp32 ones.
+
+    Reported beside the selection, never required to equal it: the stored
+    table is fp32, and blocks whose means differ by less than fp32 resolution
+    tie there (the lower id wins) while they are ordered here.
+    """
+    return select_top_blocks(gate_scores(q_group, pooled64, head_dim), k)
+
+
+def boundary_gap(scores: np.ndarray, k: int) -> float:
+    """(s_(k) - s_(k+1)) / std(s): the gap between the k-th and the (k+1)-th
+    largest score, in units of the scores' standard deviation (population,
+    ddof = 0).  +inf when every block is kept (k >= n); 0 for a tie at the
+    boundary or when all scores are equal.  The smaller it is, the smaller a
+    perturbation of the scores that could change the selection.
+    """
+    s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
+    k = int(k)
+    if k >= s.shape[0]:
+        return float("inf")
+    sd = float(np.std(s))
+    if sd == 0.0:
+        return 0.0
+    return float((s[k - 1] - s[k]) / sd)
 
 
 # --------------------------------------------------------------------------

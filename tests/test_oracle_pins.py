@@ -450,26 +450,21 @@ def _gate_weights(rng, H, d):
     return w1, beta, b1, wq
 
 
-def test_quantize_blocks_hand_cases():
-    c = GOLD["learned_gate_quantize"]
-    q8, alpha = O.quantize_blocks(np.array(c["rows"], dtype=np.float32))
-    assert q8.dtype == np.int8
-    assert q8.tolist() == c["expected_q8"]
-    assert alpha.tolist() == [2.0 ** e for e in c["expected_exponent"]]
-
-
-def test_quantize_round_trip_bound():
-    rng = np.random.default_rng(11)
-    p = (rng.standard_t(3, size=(300, 128)) * 10.0 ** rng.uniform(-6, 6, size=(300, 1))).astype(np.float32)
-    q8, alpha = O.quantize_blocks(p)
-    a = alpha[:, None]
-    err = np.abs(q8.astype(np.float64) * a - p.astype(np.float64))
-    assert np.all(err <= a * 0.5)                     # exact scaling: only the rounding to integers
-    qmax = np.abs(q8.astype(np.int64)).max(axis=1)
-    assert qmax.max() <= 127 and qmax.min() >= 63     # the smallest power of two that fits
-    # alpha is a power of two and the next smaller one would not fit
-    assert np.all(np.frexp(alpha)[0] == 0.5)
-    assert np.all(127.0 * alpha / 2 < np.abs(p.astype(np.float64)).max(axis=1))
+def test_learned_gate_hand_case():
+    """The network on two blocks, worked by hand in exact rational arithmetic
+    (tests/golden): the scores depend on key bits far below a 7-bit image of
+    the block, and those bits decide the top-1 block."""
+    c = GOLD["learned_gate_network"]
+    p = np.array(c["pooled"], dtype=np.float64)
+    p32 = p.astype(np.float32)
+    assert np.array_equal(p32.astype(np.float64), p)          # the stored values are fp32
+    s = O.learned_gate_scores(np.array(c["q_group"]), p32, np.array(c["w1"], dtype=np.int8),
+                              np.array(c["w1_scale"], dtype=np.float32),
+                              np.array(c["b1"], dtype=np.float32),
+                              np.array(c["wq"], dtype=np.float32))
+    want = np.array([float(x) for x in c["expected_scores"]])
+    assert np.array_equal(s, want)                             # short dyadic values: exact
+    assert O.select_top_blocks(s, 1).tolist() == c["expected_top1"]
 
 
 def test_learned_gate_hidden_permutation_invariance():
@@ -493,13 +488,17 @@ def test_learned_gate_homogeneity():
     s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
     # the query enters linearly (through u only): 2q gives exactly 2s
     assert np.array_equal(O.learned_gate_scores(2.0 * qg, p, w1, beta, b1, wq), 2.0 * s)
-    # keys scaled by a power of two: alpha scales with them, the int8 image does not
-    q8, alpha = O.quantize_blocks(p)
-    q8b, alphab = O.quantize_blocks(p * np.float32(4.0))
-    assert np.array_equal(q8, q8b) and np.array_equal(alphab, alpha * 4.0)
+    # without a bias the network is positively homogeneous in the keys; a
+    # power-of-two factor scales every fp64 step exactly
     zb = np.zeros_like(b1)
     s0 = O.learned_gate_scores(qg, p, w1, beta, zb, wq)
     assert np.array_equal(O.learned_gate_scores(qg, p * np.float32(4.0), w1, beta, zb, wq), 4.0 * s0)
+    # and a negative factor moves every unit to the other side of the ReLU
+    neg = O.learned_gate_scores(qg, -p, w1, beta, zb, wq)
+    both = O.learned_gate_scores(qg, p, w1, beta, zb, wq) - neg
+    lin = O.gate_scores((((wq.astype(np.float64) @ qg.sum(axis=0)) * beta.astype(np.float64))
+                         @ w1.astype(np.float64))[None, :], p, d) * math.sqrt(d)
+    assert np.allclose(both, lin, rtol=0, atol=1e-11 * np.abs(lin).max())
 
 
 def test_learned_gate_bias_saturation():
@@ -515,25 +514,98 @@ def test_learned_gate_bias_saturation():
 
 def test_learned_gate_reduces_to_the_linear_gate():
     """With every hidden unit active the network is linear: s_j equals the
-    parameter-free gate on the dequantised keys with the effective query
-    w = sum_m u_m beta_m W1_m, plus a constant."""
+    parameter-free gate on the same fp32 keys with the effective query
+    w = sum_m u_m beta_m W1_m (times sqrt(d), undoing that gate's scale),
+    plus the constant u . b1."""
     rng = np.random.default_rng(15)
     H, d, n = 256, 128, 64
     w1, beta, _, wq = _gate_weights(rng, H, d)
     p = rng.normal(size=(n, d)).astype(np.float32)
     qg = rng.normal(size=(4, d))
-    q8, alpha = O.quantize_blocks(p)
-    zmax = (alpha[:, None] * beta[None, :].astype(np.float64)
-            * np.abs(q8.astype(np.float64) @ w1.astype(np.float64).T)).max()
+    zmax = (beta[None, :].astype(np.float64)
+            * np.abs(p.astype(np.float64) @ w1.astype(np.float64).T)).max()
     b1 = np.full(H, np.float32(2.0 * zmax + 1.0), dtype=np.float32)     # every z_jm > 0
     s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
     u = wq.astype(np.float64) @ qg.sum(axis=0)
     w = (u * beta.astype(np.float64)) @ w1.astype(np.float64)
-    c = float(u @ b1.astype(np.float64)) / math.sqrt(H)
-    deq = q8.astype(np.float64) * alpha[:, None]
-    lin = O.gate_scores(w[None, :], deq, d) * math.sqrt(d) / math.sqrt(H)
+    c = float(u @ b1.astype(np.float64))
+    lin = O.gate_scores(w[None, :], p, d) * math.sqrt(d)
     assert np.allclose(s - c, lin, rtol=0, atol=1e-9 * (abs(c) + np.abs(lin).max()))
     assert not np.allclose(lin, 0.0)
+
+
+def test_learned_gate_one_unit_by_brute_force():
+    """Random small networks against a scalar loop over units and dimensions
+    (exact fractions for the first layer, so no rounding order is shared)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(16)
+    for _ in range(5):
+        H, d, n = 7, 5, 6
+        w1 = rng.integers(-127, 128, size=(H, d)).astype(np.int8)
+        beta = rng.uniform(0.1, 2.0, size=H).astype(np.float32)
+        b1 = rng.normal(size=H).astype(np.float32)
+        wq = rng.normal(size=(H, d)).astype(np.float32)
+        p = rng.normal(size=(n, d)).astype(np.float32)
+        qg = rng.normal(size=(3, d))
+        s = O.learned_gate_scores(qg, p, w1, beta, b1, wq)
+        qbar = [sum(Fraction(float(qg[h, i])) for h in range(3)) for i in range(d)]
+        for j in range(n):
+            tot = Fraction(0)
+            for m in range(H):
+                z = Fraction(float(beta[m])) * sum(int(w1[m, i]) * Fraction(float(p[j, i]))
+                                                   for i in range(d)) + Fraction(float(b1[m]))
+                um = sum(Fraction(float(wq[m, i])) * qbar[i] for i in range(d))
+                tot += um * max(z, Fraction(0))
+            assert abs(s[j] - float(tot)) <= 1e-12 * max(1.0, abs(float(tot)))
+
+
+# ---------------------------------------------------------------- reporting
+
+def test_boundary_gap_hand_case():
+    c = GOLD["boundary_gap"]
+    assert O.boundary_gap(np.array(c["scores"]), c["k"]) == pytest.approx(c["expected"], rel=1e-15)
+
+
+def test_boundary_gap_properties():
+    rng = np.random.default_rng(31)
+    s = rng.normal(size=100)
+    g = O.boundary_gap(s, 10)
+    # invariant to a positive affine change of the scores, order-free
+    assert O.boundary_gap(3.0 * s - 7.0, 10) == pytest.approx(g, rel=1e-12)
+    assert O.boundary_gap(rng.permutation(s), 10) == g
+    # by brute force: the k-th minus the (k+1)-th largest over the std
+    srt = sorted(s.tolist(), reverse=True)
+    assert g == pytest.approx((srt[9] - srt[10]) / np.std(s), rel=1e-12)
+    assert O.boundary_gap(s, 100) == float("inf") and O.boundary_gap(s, 150) == float("inf")
+    t = s.copy()
+    t[np.argsort(-t)[10]] = t[np.argsort(-t)[9]]          # tie at the boundary
+    assert O.boundary_gap(t, 10) == 0.0
+    assert O.boundary_gap(np.full(8, 2.5), 3) == 0.0
+
+
+def test_pure_selection_hand_case():
+    c = GOLD["pure_selection_rounding_tie"]
+    S = c["block_size"]
+    keys = np.array(c["keys_col0"])[:, None]
+    p32, p64, _ = O.pool_keys(keys, len(keys), S)
+    q = np.array(c["q"])
+    assert p32[0, 0] == p32[1, 0] and p64[1, 0] > p64[0, 0]
+    assert O.select_top_blocks(O.gate_scores(q, p32, 1), c["k"]).tolist() == c["expected_selection"]
+    assert O.pure_selection(q, p64, 1, c["k"]).tolist() == c["expected_pure_selection"]
+
+
+def test_pure_selection_equals_stored_when_means_are_fp32():
+    """Blocks whose means are fp32 values (here: identical rows) give the same
+    selection from the stored and the unrounded table."""
+    rng = np.random.default_rng(32)
+    S, d, n = 8, 16, 30
+    rows = rng.normal(size=(n, d)).astype(np.float32).astype(np.float64)
+    keys = np.repeat(rows, S, axis=0)
+    p32, p64, _ = O.pool_keys(keys, n * S, S)
+    assert np.array_equal(p32.astype(np.float64), p64)
+    q = rng.normal(size=(4, d))
+    assert np.array_equal(O.pure_selection(q, p64, d, 7),
+                          O.select_top_blocks(O.gate_scores(q, p32, d), 7))
 
 
 # ---------------------------------------------------------------- several query tokens
