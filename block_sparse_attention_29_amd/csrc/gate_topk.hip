@@ -482,49 +482,60 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
 
 // ---------------------------------------------------------------- learned gate
 //
-// The gate network of "Sparse Attention Reasoning" (Step 1: Linear(hidden, 256),
-// ReLU, Linear(256, 1)) on each block's pooled key, with the second layer's
-// weights a projection of the group's query so that the decode query stays
-// unpooled ("SeerAttention-R", Abstract):
-//   z_jm = 2^e_j * beta_m * (W1_m . q8_j) + b1_m,  s_j = sum_m u_m relu(z_jm) / 16,
+// The gate network of "Sparse Attention Reasoning" (Step 1: Linear(hidden,
+// 256), ReLU, Linear(256, 1)) on each block's pooled key, with the second
+// layer's weights a projection of the group's query so that the decode query
+// stays unpooled ("SeerAttention-R", Abstract):
+//   z_jm = beta_m * (W1_m . P_j) + b1_m,  s_j = sum_m u_m relu(z_jm),
 //   u_m = Wq_m . qbar (fp64),
-// where q8_j = round-half-even(P_j / 2^e_j) is the block's int8 image, e_j the
-// smallest exponent with 127 * 2^e_j >= max_i |P_ji| (a shared power-of-two
-// block scale: the scaling is exact), and W1 is int8 with fp32 row scales
-// beta.  The first layer is an exact int32 product on int8 MFMA
-// (v_mfma_i32_16x16x64_i8: A = W1 rows, B = int8 blocks, both operands with
-// the same lane -> k assignment, so the dot products are exact whatever the
-// hardware's k order); the rest is fp64 (2^e * beta is exact).  One
-// 1024-thread workgroup per unit: wave w owns hidden units 16w .. 16w + 15
-// and every block tile of a chunk of 128 blocks; a score is summed over the
-// wave's units, then over the 16 waves in order.  Every global load that does
-// not wait on another is issued at entry, and a chunk's pooled loads go out
-// while the previous chunk is being scored.  The selection rule and outputs
-// are the gate kernel's.
+// W1 int8 with fp32 row scales beta, P the stored fp32 pooled keys.
+//
+// The first layer runs on int8 MFMA (v_mfma_i32_16x16x64_i8) over an image
+// of P in five int8 limbs.  Block j gets the shared exponent e_j, the
+// smallest integer with 127 * 2^e_j >= max_i |P_ji| (0 for a zero block);
+// x = P_ji * 2^-e_j (exact, |x| <= 127) is split as
+//   x = l0 + l1 2^-7 + l2 2^-14 + l3 2^-21 + l4 2^-28 + r,
+//   l0 = rint(x) in [-127, 127], then each next limb rint(128 * remainder)
+//   in [-64, 64], every remainder exact in fp32 and |r| <= 2^-29,
+// so the limbs hold P_ji to within 2^(e_j - 29).  Each limb's product with a
+// W1 row is an exact int32 (|sum| < 2^21); the five are recombined in fp64
+// exactly (multiples of 2^-28 below 2^21), scaled by 2^e_j, and the epilogue
+// z = (2^e_j beta_m) D + b1 (one rounding), relu, u_m * h runs in fp64.
+// Hence |s_j - s_j(exact)| <= 2^(e_j - 29) sum_m |u_m| beta_m ||W1_m||_1 plus
+// fp64 rounding.  A and B carry the same lane -> k assignment, so the dot
+// products do not depend on the hardware's k order.
+//
+// One 1024-thread workgroup per unit: wave w owns hidden units 16w .. 16w+15
+// (its W1 rows come straight from memory in the A operand's layout) and every
+// block tile of a chunk of 64 blocks; wave w also cuts dimensions
+// w*D/16 .. of the chunk's blocks into limbs.  A score is summed over the
+// wave's units, then over the 16 waves in order.  The next chunk's pooled
+// loads fly while a chunk is scored.  The selection rule and outputs are the
+// gate kernel's.
 
 constexpr int kLgThreads = 1024;  // 16 waves x 16 hidden units = 256
-constexpr int kLgChunk = 128;     // blocks quantised and scored per pass
+constexpr int kLgChunk = 64;      // blocks cut into limbs and scored per pass
+constexpr int kLgLimbs = 5;       // int8 limbs per key element
 constexpr int kLgPad = 16;        // bytes added to every LDS row of int8 data (bank spread)
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
 __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
-  constexpr int H = kGateHidden, JC = kLgChunk, NW = kLgThreads / 64;
+  constexpr int H = kGateHidden, JC = kLgChunk, NW = kLgThreads / 64, NL = kLgLimbs;
   constexpr int KS = D / 64;                 // MFMA k-steps
   constexpr int PD = D + kLgPad;             // LDS row pitch of int8 rows
-  constexpr int TPB = kLgThreads / JC;       // quantisation threads per block
-  constexpr int DQ = D / TPB;                // dimensions per quantisation thread
+  constexpr int DQ = D / NW;                 // dimensions a thread cuts (wave = dimension slice)
   constexpr int WPL = D / 16;                // Wq floats per lane (16 lanes, one DPP row, per row)
   constexpr int RPP = 4;                     // Wq rows per pass of a wave
   static_assert(H == 16 * NW, "one wave per 16 hidden units");
-  static_assert(DQ == 8 || DQ == 16, "8 or 16 int8 per quantisation thread");
-  extern __shared__ uint64_t s_key[];               // [NB] order keys of the scores
-  __shared__ __align__(16) int8_t s_w1[H * PD];     // W1 of the KV head: row m, k contiguous
-  __shared__ __align__(16) int8_t s_pq[JC * PD];    // int8 image of the chunk's blocks: row j
-  __shared__ double s_red[NW][JC];                  // per-wave sums of the chunk's scores
+  static_assert(JC == 64, "one chunk block per lane");
+  static_assert(DQ == 4 || DQ == 8, "4 or 8 int8 per thread and limb");
+  extern __shared__ uint64_t s_key[];                 // [NB] order keys of the scores
+  __shared__ __align__(16) int8_t s_pq[NL][JC * PD];  // limbs of the chunk's blocks: row j
+  __shared__ double s_red[NW][JC];                    // per-wave sums of the chunk's scores
   __shared__ double s_u[H];
   __shared__ double s_q[D];
-  __shared__ float s_beta[H], s_b1[H], s_amx[TPB][JC];
+  __shared__ float s_amx[NW][JC];
   __shared__ int s_exp[JC];
   __shared__ int s_hist[3 * 256];
   __shared__ int s_scan[NW + 1];
@@ -534,10 +545,11 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int NB = a.NB;
-  const int jl = tid % JC, part = tid / JC;  // quantisation: block jl of a chunk, dims part*DQ ..
+  const int jl = lane, part = wv;  // limbs: block jl of a chunk, dims part*DQ ..
 
   // ---- loads that wait on nothing: the first chunk's pooled columns (clamped
-  // to the table, masked once the length is known), Wq rows, W1, scales, query ----
+  // to the table, masked once the length is known), W1 rows in the A
+  // operand's layout, Wq rows, row scales, biases, query ----
   const float* pcol = a.pooled + ((int64_t)u * D + part * DQ) * NB;
   float x[DQ];
   auto load_chunk = [&](int j0) {
@@ -546,6 +558,13 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     for (int i = 0; i < DQ; ++i) x[i] = c[(int64_t)i * NB];
   };
   load_chunk(0);
+  // A operand: W1 row 16 wv + n16, bytes 64 s + 16 r16 .. + 15 of k-step s.
+  i32x4 wa[KS];
+  {
+    const int8_t* wrow = a.w1 + ((int64_t)g * H + wv * 16 + n16) * D + r16 * 16;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) wa[st] = *(const i32x4*)(wrow + st * 64);
+  }
   float4 wq4[16 / RPP][WPL / 4];
   const int lr = lane & 15, rp = lane >> 4;
 #pragma unroll
@@ -554,12 +573,13 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     for (int c = 0; c < WPL / 4; ++c)
       wq4[r][c] = *(const float4*)(a.wq + ((int64_t)g * H + wv * 16 + r * RPP + rp) * D +
                                    WPL * lr + 4 * c);
-  const int8_t* w1g = a.w1 + (int64_t)g * H * D;
-  for (int o = tid * 16; o < H * D; o += kLgThreads * 16)
-    *(int4*)(s_w1 + (o / D) * PD + o % D) = *(const int4*)(w1g + o);
-  if (tid < H) {
-    s_beta[tid] = a.w1_scale[(int64_t)g * H + tid];
-    s_b1[tid] = a.b1[(int64_t)g * H + tid];
+  // This lane's hidden units in the MFMA result: m = 16 wv + 4 r16 + i.
+  double bm[4], betam[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wv * 16 + 4 * r16 + i;
+    bm[i] = (double)a.b1[(int64_t)g * H + m];
+    betam[i] = (double)a.w1_scale[(int64_t)g * H + m];
   }
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
   if (tid < D) {  // the group-summed query, fp64, head order
@@ -588,24 +608,12 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     if (lr == 0) s_u[wv * 16 + r * RPP + rp] = c;
   }
   __syncthreads();
-
-  // This lane's hidden units in the MFMA result: m = 16 wv + 4 r16 + i.
-  double um[4], bm[4], betam[4];
+  double um[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = wv * 16 + 4 * r16 + i;
-    um[i] = s_u[m];
-    bm[i] = (double)s_b1[m];
-    betam[i] = (double)s_beta[m];
-  }
-  // A operand: W1 row 16 wv + n16, bytes 64 s + 16 r16 .. + 15 of k-step s.
-  i32x4 wa[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st)
-    wa[st] = *(const i32x4*)(s_w1 + (wv * 16 + n16) * PD + st * 64 + r16 * 16);
+  for (int i = 0; i < 4; ++i) um[i] = s_u[wv * 16 + 4 * r16 + i];
 
   for (int j0 = 0; j0 < n; j0 += JC) {
-    // ---- int8 image of blocks j0 .. j0 + JC - 1 ----
+    // ---- limbs of blocks j0 .. j0 + JC - 1 ----
     {
       const bool live = j0 + jl < n;
       float mx = 0.f;
@@ -618,44 +626,64 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
       __syncthreads();
       float amax = 0.f;
 #pragma unroll
-      for (int p = 0; p < TPB; ++p) amax = fmaxf(amax, s_amx[p][jl]);
+      for (int p = 0; p < NW; ++p) amax = fmaxf(amax, s_amx[p][jl]);
       int k2;
       const float f = frexpf(amax, &k2);  // amax = f * 2^k2, 0.5 <= f < 1
       const int e = amax > 0.f ? (f <= 127.f / 128.f ? k2 - 7 : k2 - 6) : 0;
-      uint32_t w[DQ / 4];
+      uint32_t w[NL][DQ / 4];
 #pragma unroll
       for (int i = 0; i < DQ / 4; ++i) {
-        uint32_t word = 0;
+        uint32_t word[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) word[l] = 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int qv = (int)rintf(ldexpf(x[4 * i + c], -e));  // exact scaling, |qv| <= 127
-          word |= (uint32_t)(qv & 0xFF) << (8 * c);
+          float r = ldexpf(x[4 * i + c], -e);  // exact, |r| <= 127
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            const float li = rintf(r);         // l0 in [-127, 127], later limbs in [-64, 64]
+            r = (r - li) * 128.f;              // exact: the remainder has fewer bits than r
+            word[l] |= (uint32_t)((int)li & 0xFF) << (8 * c);
+          }
         }
-        w[i] = word;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) w[l][i] = word[l];
       }
-      int8_t* dst = s_pq + jl * PD + part * DQ;
-      if constexpr (DQ == 16) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
-      else *(uint2*)dst = make_uint2(w[0], w[1]);
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        int8_t* dst = &s_pq[l][jl * PD + part * DQ];
+        if constexpr (DQ == 8) *(uint2*)dst = make_uint2(w[l][0], w[l][1]);
+        else *(uint32_t*)dst = w[l][0];
+      }
       if (part == 0) s_exp[jl] = e;
     }
     if (j0 + JC < n) load_chunk(j0 + JC);  // the next chunk's loads fly while this one is scored
     __syncthreads();
 
-    // ---- first layer on MFMA, the rest in fp64 ----
-#pragma unroll 2
+    // ---- first layer on MFMA, limb by limb; the rest in fp64 ----
+#pragma unroll 1
     for (int jt = 0; jt < JC / 16; ++jt) {
-      i32x4 acc = {0, 0, 0, 0};
+      i32x4 acc[NL];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const i32x4 pb = *(const i32x4*)(s_pq + (jt * 16 + n16) * PD + st * 64 + r16 * 16);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[st], pb, acc, 0, 0, 0);
+      for (int l = 0; l < NL; ++l) {
+        acc[l] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const i32x4 pb = *(const i32x4*)(&s_pq[l][(jt * 16 + n16) * PD + st * 64 + r16 * 16]);
+          acc[l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[st], pb, acc[l], 0, 0, 0);
+        }
       }
-      // lane (r16, n16) holds the products of units 16 wv + 4 r16 + i with block jt*16 + n16
+      // lane (r16, n16) holds the products of units 16 wv + 4 r16 + i with
+      // block jt*16 + n16, one int32 per limb
       const int e = s_exp[jt * 16 + n16];
       double sc = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double z = fma(ldexp(betam[i], e), (double)acc[i], bm[i]);
+        // W1_m . (limb image) / 2^e, exact: multiples of 2^-28 below 2^21
+        double dsum = (double)acc[NL - 1][i];
+#pragma unroll
+        for (int l = NL - 2; l >= 0; --l) dsum = fma(dsum, 0x1p-7, (double)acc[l][i]);
+        const double z = fma(ldexp(betam[i], e), dsum, bm[i]);
         sc = fma(um[i], fmax(z, 0.0), sc);
       }
       sc = cross_row_sum_f64(sc);  // the four row groups: units 16 wv .. 16 wv + 15
@@ -663,14 +691,14 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     }
     __syncthreads();
 
-    // ---- scores: the 16 waves' sums in order, 1/sqrt(256) = 1/16 exactly ----
+    // ---- scores: the 16 waves' sums in order ----
     if (tid < JC && j0 + tid < n) {
       double sj = s_red[0][tid];
 #pragma unroll
       for (int w = 1; w < NW; ++w) sj = sj + s_red[w][tid];
-      s_key[j0 + tid] = order_key(sj * (1.0 / 16.0));
+      s_key[j0 + tid] = order_key(sj);
     }
-    // (the next chunk rewrites s_red only after its barriers)
+    // (the next chunk rewrites s_red and s_amx only after its barriers)
   }
   __syncthreads();
   gate_finish<kLgThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);

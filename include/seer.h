@@ -155,6 +155,12 @@ seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const 
  *    "Shijie Cao"); scores[b][g] then holds the summed score for every g.
  *  The order is score descending, ties to the lower block id, as everywhere. */
 typedef enum seer_select_mode { SEER_SELECT_TOPK = 0, SEER_SELECT_THRESHOLD = 1 } seer_select_mode;
+/* How the gated decode calls run the selection (results are bit-identical
+ * either way): AUTO lets the library choose per shape (see
+ * seer_gated_sparse_decode), ALWAYS runs it inside the attention kernel
+ * whenever the rule allows that (top-k, not unified) and it fits in LDS,
+ * NEVER runs the gate kernel first.  Ignored by the gate-only calls. */
+typedef enum seer_fuse { SEER_FUSE_AUTO = 0, SEER_FUSE_ALWAYS = 1, SEER_FUSE_NEVER = 2 } seer_fuse;
 typedef struct seer_select {
   int32_t mode;            /* seer_select_mode */
   const int32_t* top_k;    /* TOPK: device [B] counts, or NULL for the keep fraction */
@@ -164,6 +170,7 @@ typedef struct seer_select {
   int32_t force_first;     /* nonzero: keep block 0 */
   int32_t force_last;      /* nonzero: keep block n_b - 1 */
   int32_t unified;         /* nonzero: one selection per sequence over its KV heads */
+  int32_t fuse;            /* seer_fuse (0 = SEER_FUSE_AUTO); other values: SEER_ERR_INVALID_ARG */
 } seer_select;
 
 /* seer_gate_select -- seer_gate_scores_topk under a general rule (above);
@@ -193,22 +200,26 @@ typedef struct seer_gate_weights {
 /* seer_learned_gate_select -- gate scores from a learned gate network, then
  * the selection rule of seer_gate_select.
  *
- *  The network has the shape of the gate of "Sparse Attention Reasoning"
- *  (Step 1: Linear(d, 256), ReLU, then a 256-wide second layer) applied to
- *  every block's pooled key; its second layer's weights are a projection of
- *  the group's query, so that the decode query is used unpooled
- *  ("SeerAttention-R", Abstract).  For KV head g of sequence b, block j:
- *    alpha_j = 2^e_j, e_j the smallest integer with 127 * 2^e_j >= max_i |P_ji|
- *              (e_j = 0 for an all-zero block): a power-of-two block scale,
- *    q8_ji   = P_ji / alpha_j rounded to the nearest integer, ties to even,
- *    z_jm    = alpha_j * w1_scale[m] * (w1[m] . q8_j) + b1[m],
- *    s_j     = sum_m u_m * max(z_jm, 0) / 16,  u_m = wq[m] . qbar,
- *  qbar the sum of the group's query heads.  The int8 products are exact;
- *  everything else is fp64.  scores (fp64), sel_idx, sel_cnt, lens, k_max and
- *  the rule are as in seer_gate_select; a unified rule is
- *  SEER_ERR_UNSUPPORTED, so are hidden != 256 and tables that need more LDS
- *  than one workgroup has.  Missing or misaligned weights:
- *  SEER_ERR_INVALID_ARG. */
+ *  The network is the gate of "Sparse Attention Reasoning" (Step 1:
+ *  Linear(d, 256), ReLU, Linear(256, 1)) applied to every block's pooled key;
+ *  its second layer's weights are a projection of the group's query, so that
+ *  the decode query is used unpooled ("SeerAttention-R", Abstract).  For KV
+ *  head g of sequence b, block j:
+ *    z_jm = w1_scale[m] * (w1[m] . P_j) + b1[m],
+ *    s_j  = sum_m u_m * max(z_jm, 0),  u_m = wq[m] . qbar,
+ *  qbar the sum of the group's query heads, P_j the stored fp32 pooled key.
+ *  Arithmetic and its error bound: the first layer runs on int8 matrix cores
+ *  over an image of P_j in five int8 limbs under the block exponent e_j (the
+ *  smallest integer with 127 * 2^e_j >= max_i |P_ji|, 0 for a zero block),
+ *  which holds every key element to within 2^(e_j - 29); the int32 products
+ *  are exact and everything after them is fp64.  So
+ *    |s_j - s_j(exact)| <= 2^(e_j - 29) * sum_m |u_m| w1_scale[m] ||w1[m]||_1
+ *  plus fp64 rounding, and the selection is that of the exact scores
+ *  wherever no two candidates are closer than twice that.
+ *  scores (fp64), sel_idx, sel_cnt, lens, k_max and the rule are as in
+ *  seer_gate_select; a unified rule is SEER_ERR_UNSUPPORTED, so are
+ *  hidden != 256 and tables that need more LDS than one workgroup has.
+ *  Missing or misaligned weights: SEER_ERR_INVALID_ARG. */
 seer_status seer_learned_gate_select(const seer_shape* shape, const void* q, const float* pooled,
                                      const int32_t* lens, const seer_gate_weights* weights,
                                      const seer_select* rule, int32_t k_max, double* scores,
@@ -248,9 +259,12 @@ seer_status seer_sparse_decode(const seer_shape* shape, const void* q, const see
  * workspace and stream is exactly seer_sparse_decode.
  * The merge runs one workgroup per (sequence, KV head), or one per query head
  * when the units are few for the device (at least 8 partial results each on
- * average) and the query heads at least 64; the environment variable
- * SEER_COMBINE_HEADS=1 or =0 forces either (read at every call; the two
- * agree to fp32 rounding, not bit for bit). */
+ * average) and the query heads at least 64.
+ * seer_sparse_decode_combine_mode is _combine with that choice made by the
+ * caller: SEER_COMBINE_AUTO (the rule above), SEER_COMBINE_PER_UNIT or
+ * SEER_COMBINE_PER_HEAD; any other mode is SEER_ERR_INVALID_ARG.  The modes
+ * run the same fp32 operations in the same record order and give
+ * bit-identical out and lse. */
 seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
                                        const int32_t* lens, const int32_t* sel_idx,
                                        const int32_t* sel_cnt, int32_t k_max,
@@ -259,6 +273,14 @@ seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, c
 seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
                                        const void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+typedef enum seer_combine_mode {
+  SEER_COMBINE_AUTO = 0,
+  SEER_COMBINE_PER_UNIT = 1,
+  SEER_COMBINE_PER_HEAD = 2
+} seer_combine_mode;
+seer_status seer_sparse_decode_combine_mode(const seer_shape* shape, int32_t mode, float* out,
+                                            float* lse, const void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
 
 /* seer_gated_sparse_decode -- one decode step from the pooled table: gate
  * scores, top-k selection and sparse attention, as seer_gate_scores_topk
@@ -278,9 +300,10 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
  *  blocks per unit.  For a threshold or unified rule, more units or longer
  *  tables, or when one workgroup's selections would not fit in its LDS, the
  *  call runs the gate kernel first instead (same results, one launch more).
- *  seer_gated_decode_is_fused tells which for a shape.  The environment
- *  variable SEER_FUSED_GATE=1 fuses whenever the rule allows it, =0 never
- *  (read at every call; the results do not depend on it).
+ *  seer_gated_decode_is_fused tells which for a shape.  rule->fuse
+ *  overrides the choice (SEER_FUSE_ALWAYS fuses whenever the rule allows it
+ *  and the selections fit in LDS, SEER_FUSE_NEVER never); the results do not
+ *  depend on it.
  * _partial: the first launch(es) alone (gate + partial results in the
  * workspace, selections written); seer_sparse_decode_combine finishes it. */
 /* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode
