@@ -100,30 +100,25 @@ int decode_waves(const seer_shape* s, int64_t blocks_per_unit, int wmax) {
 // gates them all in parallel), and at most 256 blocks per unit (the blocks
 // one pass of the workgroup's loads covers; a longer table makes every
 // workgroup that shares the unit re-score all of it).
-// SEER_FUSED_GATE=1 fuses whenever the rule allows it, =0 never (both give
-// the same results; for tests and measurements).
+// rule->fuse = SEER_FUSE_ALWAYS fuses whenever the rule allows it,
+// SEER_FUSE_NEVER never (the results are the same either way).
 bool fused_gate_pays(const seer_shape* s, const seer_select* rule, int W) {
   if (rule->mode != SEER_SELECT_TOPK || rule->unified) return false;
-  const char* env = getenv("SEER_FUSED_GATE");
-  if (env && env[0] == '1' && env[1] == 0) return true;
-  if (env && env[0] == '0' && env[1] == 0) return false;
+  if (rule->fuse == SEER_FUSE_ALWAYS) return true;
+  if (rule->fuse == SEER_FUSE_NEVER) return false;
   const int U = s->batch * s->num_kv_heads;
   return U <= W / seer::kDecodeWavesPerWG && s->max_blocks <= 256;
 }
 
 // Whether the single-token combine runs one workgroup per query head instead
-// of one per unit: when the units average 8 or more partial records at full
-// width (few, long units: a workgroup per unit leaves most CUs idle and gives
-// each thread long chains of record loads) and there are at least 64 query
-// heads.  Measured per step: 32 units x 8 heads at 131K tokens 49.9 -> 49.0 us,
-// 64 units x 4 heads 18.3 -> 18.0 us; with 512 units (3-4 records each) the
-// 2560 small workgroups cost 2.7 us more, and one unit of 4 heads 3.9 us more.
-// SEER_COMBINE_HEADS=1 or =0 forces either (for tests and measurements; the
-// two agree to fp32 rounding, not bit for bit).
+// of one per unit, when the caller leaves the choice to the library: when the
+// units average 8 or more partial records at full width (few, long units: a
+// workgroup per unit leaves most CUs idle and gives each thread long chains of
+// record loads) and there are at least 64 query heads.  Measured per step: 32
+// units x 8 heads at 131K tokens 49.9 -> 49.0 us, 64 units x 4 heads 18.3 ->
+// 18.0 us; with 512 units (3-4 records each) the 2560 small workgroups cost
+// 2.7 us more, and one unit of 4 heads 3.9 us more.
 bool combine_per_head(const seer_shape* s, int wmax) {
-  const char* env = getenv("SEER_COMBINE_HEADS");
-  if (env && env[0] == '1' && env[1] == 0) return true;
-  if (env && env[0] == '0' && env[1] == 0) return false;
   const int64_t U = (int64_t)s->batch * s->num_kv_heads;
   return U * 8 <= wmax && (int64_t)s->batch * s->num_q_heads >= 64;
 }
@@ -203,6 +198,9 @@ seer_status check_gate(const seer_shape* shape, const void* q, const float* pool
                 shape->max_blocks);
   if (rule->mode != SEER_SELECT_TOPK && rule->mode != SEER_SELECT_THRESHOLD)
     return fail(SEER_ERR_INVALID_ARG, "selection mode %d is not a seer_select_mode", rule->mode);
+  if (rule->fuse != SEER_FUSE_AUTO && rule->fuse != SEER_FUSE_ALWAYS &&
+      rule->fuse != SEER_FUSE_NEVER)
+    return fail(SEER_ERR_INVALID_ARG, "fuse %d is not a seer_fuse", rule->fuse);
   if (rule->mode == SEER_SELECT_THRESHOLD) {
     if (!(rule->threshold == rule->threshold) || isinf(rule->threshold))
       return fail(SEER_ERR_INVALID_ARG, "threshold is not finite");
@@ -483,6 +481,9 @@ seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
   if (st) return st;
   if ((st = check_tokens(shape, tokens))) return st;
   if (!rule || !fused) return fail(SEER_ERR_INVALID_ARG, "rule or fused is NULL");
+  if (rule->fuse != SEER_FUSE_AUTO && rule->fuse != SEER_FUSE_ALWAYS &&
+      rule->fuse != SEER_FUSE_NEVER)
+    return fail(SEER_ERR_INVALID_ARG, "fuse %d is not a seer_fuse", rule->fuse);
   if (k_max < 1 || k_max > shape->max_blocks)
     return fail(SEER_ERR_INVALID_ARG, "k_max %d outside [1, max_blocks]", k_max);
   const int wmax = wave_cap(shape);
@@ -533,11 +534,13 @@ seer_status seer_gated_sparse_decode_no_alloc(const seer_shape* shape, const voi
                                   stream);
 }
 
-seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
-                                       const void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+seer_status seer_sparse_decode_combine_mode(const seer_shape* shape, int32_t mode, float* out,
+                                            float* lse, const void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
   seer_status st = check_shape(shape);
   if (st) return st;
+  if (mode != SEER_COMBINE_AUTO && mode != SEER_COMBINE_PER_UNIT && mode != SEER_COMBINE_PER_HEAD)
+    return fail(SEER_ERR_INVALID_ARG, "combine mode %d is not a seer_combine_mode", mode);
   if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
   if (!workspace) return fail(SEER_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(SEER_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -561,10 +564,18 @@ seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, floa
   c.part = (const float*)(ws + seer::decode_part_offset(U));
   c.out = out;
   c.lse = lse;
-  c.per_head = combine_per_head(shape, wmax) ? 1 : 0;
+  c.per_head = mode == SEER_COMBINE_PER_HEAD ||
+               (mode == SEER_COMBINE_AUTO && combine_per_head(shape, wmax));
   const hipError_t e = seer::launch_decode_combine(c, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
   return ok();
+}
+
+seer_status seer_sparse_decode_combine(const seer_shape* shape, float* out, float* lse,
+                                       const void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  return seer_sparse_decode_combine_mode(shape, SEER_COMBINE_AUTO, out, lse, workspace,
+                                         workspace_bytes, stream);
 }
 
 seer_status seer_multi_gate_select(const seer_shape* shape, int32_t tokens, const void* q,

@@ -461,13 +461,13 @@ void decode_partial_kernel(DecodeArgs a) {
 //
 // The waves that wrote a record for unit u are the non-empty waves among
 // [wlo, whi], the first and last waves whose tile ranges meet the unit's
-// tiles.  Up to 32 records: one shot, every load up front, then the maximum
-// of the records' maxima and the scaled sums in record order.  More records:
-// (m, l) pairs staged through LDS in chunks, acc elements fetched 16 records
-// at a time, merged with a running maximum
-//   M' = max(M, m_w);  o = o * 2^(M - M') + acc_w * 2^(m_w - M');  same for l.
-// Either way out = o / l and the order is fixed, so the result is
-// deterministic.
+// tiles.  The merge: the maximum M of the used records' maxima, then
+//   o = sum_w acc_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M)
+// as fma chains in record order, out = o / l, lse = M + log2(l) (natural log
+// on output).  Up to 32 records it runs in one shot (every load up front);
+// beyond, in two passes over chunks of records.  The order is fixed, so the
+// result is deterministic, and the per-head kernel below runs the same
+// operations, so the two give identical bits.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass (general path)
 constexpr int kCombineBatch = 16;   // acc loads in flight per thread (general path)
@@ -564,15 +564,17 @@ void decode_combine_kernel(CombineArgs a) {
   if (nw <= 16) return combine_shot<D, G, 16>(a, part, nw, wlo, W, Tot, head0);
   if (nw <= kCombineFast) return combine_shot<D, G, kCombineFast>(a, part, nw, wlo, W, Tot, head0);
 
-  // General path (many records per unit): (m, l) staged through LDS in chunks,
-  // acc loads batched; same in-order running merge.
+  // General path (many records per unit): the one-shot merge's two passes
+  // over all records -- the maximum M of the used records' maxima, then the
+  // rescaled values summed in record order -- with (m, l) staged through LDS
+  // in chunks and the values fetched kCombineBatch records at a time.  The
+  // result does not depend on the chunking.
   float o[PER], M[PER], l[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) { o[r] = 0.f; M[r] = kNegInf; l[r] = 0.f; }
 
-  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
-    const int cn = min(kCombineChunk, nw - c0);
-    if (c0 > 0) __syncthreads();  // previous chunk's (m, l) fully consumed
+  auto stage = [&](int c0, int cn) {
+    __syncthreads();  // the previous chunk's (m, l) fully consumed
     for (int t = tid; t < cn; t += kCombineThreads) {
       const bool e = empty(c0 + t);
       const float* r = part + (int64_t)(c0 + t) * REC;
@@ -586,6 +588,23 @@ void decode_combine_kernel(CombineArgs a) {
       }
     }
     __syncthreads();
+  };
+  // pass 1: maxima (empty records staged as -inf change nothing)
+  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, nw - c0);
+    stage(c0, cn);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = r * kCombineThreads + tid;
+      if (idx >= G * D) continue;
+      const int h = idx / D;
+      for (int t = 0; t < cn; ++t) M[r] = fmaxf(M[r], s_mw[t][h]);
+    }
+  }
+  // pass 2: sums in record order (a single chunk stays staged from pass 1)
+  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, nw - c0);
+    if (nw > kCombineChunk) stage(c0, cn);
     for (int t0 = 0; t0 < cn; t0 += kCombineBatch) {
       const int tn = min(kCombineBatch, cn - t0);
 #pragma unroll
@@ -602,12 +621,12 @@ void decode_combine_kernel(CombineArgs a) {
         for (int t = 0; t < kCombineBatch; ++t) {
           if (t >= tn) break;
           const float mw = s_mw[t0 + t][h];
-          if (mw == kNegInf) continue;  // empty record or no valid token: skipped
-          const float mn = fmaxf(M[r], mw);
-          const float sa = __builtin_amdgcn_exp2f(M[r] - mn), sb = __builtin_amdgcn_exp2f(mw - mn);
-          o[r] = o[r] * sa + x[t] * sb;
-          l[r] = l[r] * sa + s_lw[t0 + t][h] * sb;
-          M[r] = mn;
+          // records without a valid token (m = -inf) and empty records add nothing
+          const bool use = mw != kNegInf;
+          // Arguments are <= 0: the hardware exp2 is accurate there.
+          const float sc = __builtin_amdgcn_exp2f(use ? mw - M[r] : 0.f);
+          o[r] = use ? fmaf(x[t], sc, o[r]) : o[r];
+          l[r] = use ? fmaf(s_lw[t0 + t][h], sc, l[r]) : l[r];
         }
       }
     }
@@ -625,11 +644,12 @@ void decode_combine_kernel(CombineArgs a) {
 // The same merge with one workgroup per query head and one thread per element,
 // for units with many records (few, long units): a head's records share their
 // (m, l), so each thread loads only its element's values of every record.
-// Records are merged in chunks of up to 64 (8, 16 or 32 when the unit has no
-// more): the chunk's maximum Mc, then its values rescaled by 2^(m_w - M') and
-// summed in record order into the running state, M' = max(M, Mc), which is
-// rescaled once by 2^(M - M').  A unit with at most 64 records is one chunk:
-// the same arithmetic as combine_shot.
+// The arithmetic is the per-unit kernel's, operation for operation: the
+// maximum M of the used records' maxima, then o = sum_t x_t 2^(m_t - M) and
+// l = sum_t l_t 2^(m_t - M) as fma chains in record order, out = o / l -- so
+// the two kernels give bit-identical results.  Up to 32 records every load is
+// issued up front (code paths sized to 8, 16 and 32); beyond, the maxima
+// first, then the values kHeadChunk records at a time.
 constexpr int kHeadChunk = 64;
 
 template <int D, int G>
@@ -654,8 +674,11 @@ __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
   const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
   const EqualSplit sp(Tot, W);
+  // Waves are only ever empty when there are fewer tiles than waves.
+  auto empty = [&](int t) { return Tot < W && wave_empty(sp, wlo + t); };
   float M = kNegInf, l = 0.f, o = 0.f;
-  auto chunk = [&](int t0, auto ch_tag) {
+  // records t0 .. t0 + CH - 1 (those below nw) summed into (o, l) under M
+  auto sums = [&](int t0, auto ch_tag) {
     constexpr int CH = decltype(ch_tag)::value;
     const int tn = min(CH, nw - t0);
     float x[CH], mv[CH], lv[CH];
@@ -666,38 +689,35 @@ __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
       mv[t] = r[G * D + h];
       lv[t] = r[G * D + 8 + h];
     }
-    // Waves are only ever empty when there are fewer tiles than waves.
     uint64_t skip = 0;
-    if (Tot < W)
-      for (int t = 0; t < tn; ++t) skip |= wave_empty(sp, wlo + t0 + t) ? (1ull << t) : 0ull;
-    float Mc = kNegInf;
+    for (int t = 0; t < tn; ++t) skip |= empty(t0 + t) ? (1ull << t) : 0ull;
+    if (t0 == 0 && nw <= CH) {  // one shot: the maximum from the same loads
 #pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const bool use = t < tn && !((skip >> t) & 1ull);
-      Mc = use ? fmaxf(Mc, mv[t]) : Mc;
+      for (int t = 0; t < CH; ++t) {
+        const bool use = t < tn && !((skip >> t) & 1ull);
+        M = use ? fmaxf(M, mv[t]) : M;
+      }
     }
-    if (Mc == kNegInf) return;  // no valid token in the chunk
-    const float Mn = fmaxf(M, Mc);
-    // Arguments are <= 0 (or -inf, giving 0): the hardware exp2 is accurate there.
-    const float s = __builtin_amdgcn_exp2f(M - Mn);
-    o *= s;
-    l *= s;
+    if (M == kNegInf) return;  // no valid token anywhere
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-      // Records without a valid token (m = -inf) and skipped slots add nothing;
-      // stale slots may hold anything, so they are selected away, not scaled.
+      // Records without a valid token (m = -inf) and empty records add
+      // nothing; stale slots may hold anything, so they are selected away.
       const bool use = t < tn && !((skip >> t) & 1ull) && mv[t] != kNegInf;
-      const float sc = __builtin_amdgcn_exp2f(mv[t] - Mn);
+      // Arguments are <= 0: the hardware exp2 is accurate there.
+      const float sc = __builtin_amdgcn_exp2f(mv[t] - M);
       o = use ? fmaf(x[t], sc, o) : o;
       l = use ? fmaf(lv[t], sc, l) : l;
     }
-    M = Mn;
   };
-  if (nw <= 8) chunk(0, std::integral_constant<int, 8>{});
-  else if (nw <= 16) chunk(0, std::integral_constant<int, 16>{});
-  else if (nw <= 32) chunk(0, std::integral_constant<int, 32>{});
-  else
-    for (int t0 = 0; t0 < nw; t0 += kHeadChunk) chunk(t0, std::integral_constant<int, kHeadChunk>{});
+  if (nw <= 8) sums(0, std::integral_constant<int, 8>{});
+  else if (nw <= 16) sums(0, std::integral_constant<int, 16>{});
+  else if (nw <= 32) sums(0, std::integral_constant<int, 32>{});
+  else {
+    for (int t = 0; t < nw; ++t)
+      if (!empty(t)) M = fmaxf(M, part[(int64_t)t * REC + G * D + h]);
+    for (int t0 = 0; t0 < nw; t0 += kHeadChunk) sums(t0, std::integral_constant<int, kHeadChunk>{});
+  }
   a.out[head * D + tid] = l > 0.f ? o / l : 0.f;
   if (a.lse && tid == 0) a.lse[head] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
 }

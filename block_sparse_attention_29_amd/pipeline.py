@@ -31,7 +31,8 @@ class DecodeState:
                  k_max: Optional[int] = None, keep: Optional[tuple] = None,
                  top_k: Optional[torch.Tensor] = None, threshold: Optional[float] = None,
                  force_first: bool = False, force_last: bool = False, unified: bool = False,
-                 gate_weights=None, query_tokens: int = 1):
+                 gate_weights=None, query_tokens: int = 1, fuse=None,
+                 combine: int = seer.SEER_COMBINE_AUTO):
         self.shape = seer.make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks, dtype)
         self.k, self.v, self.page_table = k, v, page_table
@@ -46,7 +47,9 @@ class DecodeState:
             raise ValueError("the learned gate takes one query token per sequence")
         self.rule = seer.make_select(top_k=top_k, keep=keep, threshold=threshold,
                                      force_first=force_first, force_last=force_last,
-                                     unified=unified)
+                                     unified=unified, fuse=fuse)
+        # single-token combine: the library's choice, or one kernel forced
+        self.combine = int(combine)
         if k_max is None:
             if keep is not None and threshold is None:
                 k_max = seer.keep_blocks(max_blocks, keep[0], keep[1])
@@ -104,6 +107,10 @@ class DecodeState:
         if self.T > 1:
             seer.multi_sparse_decode(self.shape, self.T, q, self.kv, lens, si, sc, km, self.out,
                                      self.lse, self.workspace)
+        elif self.combine != seer.SEER_COMBINE_AUTO:
+            seer.sparse_decode_partial(self.shape, q, self.kv, lens, si, sc, km, self.workspace)
+            seer.sparse_decode_combine(self.shape, self.out, self.lse, self.workspace,
+                                       self.combine)
         else:
             seer.sparse_decode(self.shape, q, self.kv, lens, si, sc, km, self.out, self.lse,
                                self.workspace)
@@ -119,6 +126,13 @@ class DecodeState:
             seer.multi_gated_sparse_decode(self.shape, self.T, q, self.kv, lens, self.pooled,
                                            self.rule, self.k_max, self.scores, self.sel_idx,
                                            self.sel_cnt, self.out, self.lse, self.workspace)
+            return self.out, self.lse
+        if self.combine != seer.SEER_COMBINE_AUTO:
+            seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
+                                     self.k_max, self.scores, self.sel_idx, self.sel_cnt, None,
+                                     None, self.workspace)
+            seer.sparse_decode_combine(self.shape, self.out, self.lse, self.workspace,
+                                       self.combine)
             return self.out, self.lse
         seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,

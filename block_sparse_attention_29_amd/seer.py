@@ -36,6 +36,7 @@ EXPORTS = (
     "seer_sparse_decode",
     "seer_sparse_decode_partial",
     "seer_sparse_decode_combine",
+    "seer_sparse_decode_combine_mode",
     "seer_gated_sparse_decode",
     "seer_gated_sparse_decode_partial",
     "seer_gated_decode_is_fused",
@@ -67,16 +68,26 @@ class Select(ctypes.Structure):
         ("force_first", ctypes.c_int32),
         ("force_last", ctypes.c_int32),
         ("unified", ctypes.c_int32),
+        ("fuse", ctypes.c_int32),
     ]
 
 
+SEER_FUSE_AUTO, SEER_FUSE_ALWAYS, SEER_FUSE_NEVER = 0, 1, 2
+SEER_COMBINE_AUTO, SEER_COMBINE_PER_UNIT, SEER_COMBINE_PER_HEAD = 0, 1, 2
+_FUSE = {None: SEER_FUSE_AUTO, "auto": SEER_FUSE_AUTO, True: SEER_FUSE_ALWAYS,
+         "always": SEER_FUSE_ALWAYS, False: SEER_FUSE_NEVER, "never": SEER_FUSE_NEVER}
+
+
 def make_select(*, top_k: Optional[torch.Tensor] = None, keep=None, threshold=None,
-                force_first=False, force_last=False, unified=False) -> Select:
+                force_first=False, force_last=False, unified=False, fuse=None) -> Select:
+    """seer_select; ``fuse`` None/"auto" (the library's choice), True/"always"
+    or False/"never" (whether the gated calls select inside the attention
+    kernel)."""
     num, den = keep if keep is not None else (1, 1)
     mode = SEER_SELECT_THRESHOLD if threshold is not None else SEER_SELECT_TOPK
     return Select(mode, None if top_k is None else top_k.data_ptr(), num, den,
                   0.0 if threshold is None else float(threshold), int(force_first),
-                  int(force_last), int(unified))
+                  int(force_last), int(unified), _FUSE[fuse])
 
 
 class GateWeightsC(ctypes.Structure):
@@ -147,6 +158,7 @@ def load(path: str = LIB_PATH):
     lib.seer_sparse_decode_partial.argtypes = [SP, _P, KP, _P, _P, _P, _I32, ctypes.c_float, _P,
                                                ctypes.c_size_t, _P]
     lib.seer_sparse_decode_combine.argtypes = [SP, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.seer_sparse_decode_combine_mode.argtypes = [SP, _I32, _P, _P, _P, ctypes.c_size_t, _P]
     RP = ctypes.POINTER(Select)
     lib.seer_gate_select.argtypes = [SP, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
     lib.seer_learned_gate_select.argtypes = [SP, _P, _P, _P, ctypes.POINTER(GateWeightsC), RP,
@@ -184,6 +196,7 @@ def load(path: str = LIB_PATH):
                  "seer_multi_sparse_decode_workspace_size", "seer_multi_sparse_decode",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
+                 "seer_sparse_decode_combine_mode",
                  "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial",
                  "seer_gated_sparse_decode_no_alloc"):
         getattr(lib, name).restype = _I32
@@ -414,11 +427,20 @@ def sparse_decode_partial(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Ten
 
 
 def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.Tensor],
-                          workspace: torch.Tensor):
+                          workspace: torch.Tensor, mode: int = SEER_COMBINE_AUTO):
+    """seer_sparse_decode_combine, or seer_sparse_decode_combine_mode with an
+    explicit mode (SEER_COMBINE_PER_UNIT / SEER_COMBINE_PER_HEAD)."""
     lib = load()
     _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
-    _check(lib.seer_sparse_decode_combine(ctypes.byref(shape), _ptr(out), _ptr(lse),
-                                          _ptr(workspace), workspace.numel(), _stream()))
+    if lse is not None:
+        _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
+    if mode == SEER_COMBINE_AUTO:
+        _check(lib.seer_sparse_decode_combine(ctypes.byref(shape), _ptr(out), _ptr(lse),
+                                              _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check(lib.seer_sparse_decode_combine_mode(ctypes.byref(shape), mode, _ptr(out),
+                                                   _ptr(lse), _ptr(workspace),
+                                                   workspace.numel(), _stream()))
 
 
 def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int, tokens: int = 1) -> bool:

@@ -117,15 +117,6 @@ def test_multi_token_causal_edge():
     assert torch.all(torch.isfinite(st.lse[0, 2:]))
 
 
-def test_multi_token_full_size():
-    wl = WORKLOADS["spec4_32k"]
-    print("[case] multi-token full size spec4_32k", flush=True)
-    case = make_case(wl, "cuda")
-    st = run_multi(case)
-    for (b, g) in units_of(wl, limit=6, seed=5):
-        check_multi_unit(st, case, b, g, tag="spec4_32k")
-
-
 def test_multi_token_two_stages():
     """seer_multi_sparse_decode_partial then _combine on one workspace gives
     the bits of seer_multi_sparse_decode."""
@@ -159,15 +150,14 @@ def test_query_shape_checked():
 
 
 @pytest.mark.parametrize("name", sorted(CASES) + ["spec4_32k"])
-def test_multi_gated_equals_separate_calls_bitwise(name, monkeypatch):
+def test_multi_gated_equals_separate_calls_bitwise(name):
     """The multi-token step with the gate fused into the attention kernel
     writes exactly what the gate call followed by the attention calls writes
     (scores, ids, counts, out, lse); the fused kernel is forced."""
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     wl = CASES[name] if name in CASES else WORKLOADS[name].with_(batch=2)
     print(f"[case] multi gated vs separate {name}", flush=True)
     case = make_case(wl, "cuda")
-    fused = state_for(case, query_tokens=wl.query_tokens)
+    fused = state_for(case, query_tokens=wl.query_tokens, fuse=True)
     sep = state_for(case, query_tokens=wl.query_tokens)
     for st in (fused, sep):
         st.build_pool(case.lens)
@@ -180,13 +170,12 @@ def test_multi_gated_equals_separate_calls_bitwise(name, monkeypatch):
 
 @pytest.mark.parametrize("rule", [dict(force_first=True), dict(force_first=True, force_last=True)],
                          ids=["first", "both"])
-def test_multi_gated_forced_blocks(rule, monkeypatch):
+def test_multi_gated_forced_blocks(rule):
     """Forced blocks in the fused multi-token gate: bitwise the separate calls,
     and the oracle's selection."""
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     wl = CASES["paged_g5_t2"]
     case = make_case(wl, "cuda")
-    fused = state_for(case, query_tokens=wl.query_tokens, **rule)
+    fused = state_for(case, query_tokens=wl.query_tokens, fuse=True, **rule)
     sep = state_for(case, query_tokens=wl.query_tokens, **rule)
     for st in (fused, sep):
         st.build_pool(case.lens)

@@ -94,44 +94,24 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("heads", ["0", "1"])
+COMBINE = {"unit": seer.SEER_COMBINE_PER_UNIT, "head": seer.SEER_COMBINE_PER_HEAD}
+
+
+@pytest.mark.parametrize("combine", sorted(COMBINE))
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_full_chain_small(name, heads, monkeypatch):
-    """The whole step against the oracle, with the combine run per unit
-    (heads=0) and per query head (heads=1) on every shape."""
-    monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
+def test_full_chain_small(name, combine):
+    """The whole step against the oracle, with the combine run per unit and
+    per query head on every shape."""
     wl = SMALL[name]
-    print(f"[case] full chain {name} combine per head {heads}", flush=True)
+    print(f"[case] full chain {name} combine per {combine}", flush=True)
     case = make_case(wl, "cuda")
-    st = state_for(case)
+    st = state_for(case, combine=COMBINE[combine])
     st.build_pool(case.lens)
     st.step(case.q, case.lens)
     torch.cuda.synchronize()
     lens = case.lens.tolist()
     for (b, g) in units_of(wl):
         check_unit(st, case, case.q, lens, b, g, tag=name)
-
-
-@pytest.mark.parametrize("name", ["tiny_1k", "paged_small", "long_small", "f32_d128_s128_g1",
-                                  "bf16_d64_g8", "bf16_g3_keep", "f32_g5_paged"])
-def test_combine_modes_agree(name, monkeypatch):
-    """Units with at most 32 partial records (at most W/U + 1 each on these
-    shapes): the merge per unit and per query head runs the same formulas in
-    the same record order, so the two agree to fp32 rounding (they are not
-    bit-identical: the kernels are compiled separately)."""
-    wl = SMALL[name]
-    print(f"[case] combine modes {name}", flush=True)
-    case = make_case(wl, "cuda")
-    res = []
-    for heads in ("0", "1"):
-        monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
-        st = state_for(case)
-        st.build_pool(case.lens)
-        st.step(case.q, case.lens)
-        torch.cuda.synchronize()
-        res.append(st)
-    assert torch.allclose(res[0].out, res[1].out, rtol=1e-5, atol=1e-6)
-    assert torch.allclose(res[0].lse, res[1].lse, rtol=1e-5, atol=1e-6)
 
 
 FEW_UNITS = {
@@ -144,15 +124,46 @@ FEW_UNITS = {
 }
 
 
-@pytest.mark.parametrize("heads", ["0", "1"])
-@pytest.mark.parametrize("name", sorted(FEW_UNITS))
-def test_few_long_units(name, heads, monkeypatch):
-    """Units with many partial records, merged per unit and per query head."""
-    monkeypatch.setenv("SEER_COMBINE_HEADS", heads)
-    wl = FEW_UNITS[name]
-    print(f"[case] few long units {name} combine per head {heads}", flush=True)
+COMBINE_CASES = sorted(SMALL) + ["budget_b1", "planted_b1", "budget_b2"]
+
+
+@pytest.mark.parametrize("name", COMBINE_CASES)
+def test_combine_modes_bitwise(name):
+    """The merge per unit and per query head run the same fp32 operations in
+    the same record order, so on one set of partial records they give the
+    same bits: shapes with few records per unit (one-shot merges), and with
+    ~64 and ~128 records per unit (two-pass merges), some with empty waves
+    between a unit's records."""
+    wl = SMALL.get(name) or FEW_UNITS.get(name) or WORKLOADS["budget_32k"].with_(batch=2)
+    print(f"[case] combine modes {name}", flush=True)
     case = make_case(wl, "cuda")
     st = state_for(case)
+    st.build_pool(case.lens)
+    seer.gated_sparse_decode(st.shape, case.q, st.kv, case.lens, st.pooled, st.rule, st.k_max,
+                             st.scores, st.sel_idx, st.sel_cnt, None, None, st.workspace)
+    outs = []
+    for mode in (seer.SEER_COMBINE_PER_UNIT, seer.SEER_COMBINE_PER_HEAD):
+        st.out.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        seer.sparse_decode_combine(st.shape, st.out, st.lse, st.workspace, mode)
+        torch.cuda.synchronize()
+        outs.append((st.out.clone(), st.lse.clone()))
+    (o0, l0), (o1, l1) = outs
+    bad = (o0.view(torch.int32) != o1.view(torch.int32)).sum().item()
+    assert bad == 0, f"{bad} output elements differ"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+
+
+@pytest.mark.parametrize("combine", sorted(COMBINE))
+@pytest.mark.parametrize("name", sorted(FEW_UNITS))
+def test_few_long_units(name, combine):
+    """Units with many partial records, merged per unit and per query head."""
+    wl = FEW_UNITS[name]
+    print(f"[case] few long units {name} combine per {combine}", flush=True)
+    case = make_case(wl, "cuda")
+    st = state_for(case, combine=COMBINE[combine])
     st.build_pool(case.lens)
     st.step(case.q, case.lens)
     torch.cuda.synchronize()
@@ -208,19 +219,18 @@ def test_decode_with_oracle_selection():
 
 
 @pytest.mark.parametrize("name", sorted(SMALL) + ["budget_32k", "long_131k", "paged_var"])
-def test_gated_equals_separate_calls_bitwise(name, monkeypatch):
+def test_gated_equals_separate_calls_bitwise(name):
     """The fused gate + attention call writes exactly what the gate call
     followed by the attention call writes: scores, ids, counts, out, lse.
     The fused kernel is forced, also where the call would not choose it (more
     than 256 blocks per unit, more units than workgroups)."""
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     wl = SMALL[name] if name in SMALL else WORKLOADS[name].with_(batch=2)
     if name == "paged_var":
         wl = WORKLOADS[name].with_(batch=48)     # 384 units on 256 workgroups
     print(f"[case] gated vs separate {name}", flush=True)
     case = make_case(wl, "cuda")
     q = case.q[0] if wl.decode_steps else case.q
-    fused, sep = state_for(case), state_for(case)
+    fused, sep = state_for(case, fuse=True), state_for(case)
     for st in (fused, sep):
         st.build_pool(case.lens)
     fused.step(q, case.lens)
@@ -230,7 +240,7 @@ def test_gated_equals_separate_calls_bitwise(name, monkeypatch):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
 
 
-def test_max_units(monkeypatch):
+def test_max_units():
     """SEER_MAX_UNITS (sequence, KV head) pairs: 1024 paged sequences of 1..700
     tokens on 8 KV heads.  Waves cross many units and most units hold one or two
     partial records.  Every unit's kept count follows the keep rule, sampled
@@ -241,9 +251,8 @@ def test_max_units(monkeypatch):
     assert wl.batch * wl.num_kv_heads == 8192          # SEER_MAX_UNITS
     print("[case] max units: 1024 x 8 units", flush=True)
     case = make_case(wl, "cuda")
-    sep = state_for(case)
+    sep = state_for(case, fuse=False)
     sep.build_pool(case.lens)
-    monkeypatch.setenv("SEER_FUSED_GATE", "0")
     sep.step(case.q, case.lens)
     torch.cuda.synchronize()
     lens = case.lens.tolist()
@@ -253,8 +262,7 @@ def test_max_units(monkeypatch):
     assert (got == np.array(want)[:, None]).all()
     for (b, g) in units_of(wl, limit=12, seed=7):
         check_unit(sep, case, case.q, lens, b, g, tag="max units")
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
-    fused = state_for(case)
+    fused = state_for(case, fuse=True)
     fused.build_pool(case.lens)
     fused.step(case.q, case.lens)
     torch.cuda.synchronize()
@@ -262,11 +270,10 @@ def test_max_units(monkeypatch):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
 
 
-def test_gated_with_a_wide_block_table(monkeypatch):
+def test_gated_with_a_wide_block_table():
     """8192 blocks per sequence (the largest table): the gated call (fused
     kernel forced) matches the separate calls and the oracle (its key buffer
     alone is 64 KiB of LDS)."""
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
     S, d, NB, L = 64, 64, 8192, 3000
     gen = torch.Generator(device="cuda")
     gen.manual_seed(8192)
@@ -278,7 +285,8 @@ def test_gated_with_a_wide_block_table(monkeypatch):
     lens = torch.tensor([L], dtype=torch.int32, device="cuda")
     top_k = torch.tensor([7], dtype=torch.int32, device="cuda")
     sts = [DecodeState(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=d, block_size=S,
-                       max_blocks=NB, dtype=torch.float32, k=k, v=v, k_max=16, top_k=top_k)
+                       max_blocks=NB, dtype=torch.float32, k=k, v=v, k_max=16, top_k=top_k,
+                       fuse=True)
            for _ in range(2)]
     for st in sts:
         st.build_pool(lens)
@@ -449,63 +457,7 @@ def test_incremental_pooling_bitwise():
             assert np.array_equal(got_open.view(np.uint64), open_sum.view(np.uint64))
 
 
-# ------------------------------------------------------------------ full sizes
-
-@pytest.mark.parametrize("name", ["planted_8k", "budget_32k", "sparse90_32k", "paged_var"])
-def test_full_size_workloads(name):
-    wl = WORKLOADS[name]
-    print(f"[case] full size {name}", flush=True)
-    case = make_case(wl, "cuda")
-    st = state_for(case)
-    st.build_pool(case.lens)
-    st.step(case.q, case.lens)
-    torch.cuda.synchronize()
-    lens = case.lens.tolist()
-    for (b, g) in units_of(wl, limit=6, seed=1):
-        check_unit(st, case, case.q, lens, b, g, tag=name)
-    if case.planted is not None:
-        U = wl.batch * wl.num_kv_heads
-        sel = st.sel_idx.cpu().numpy()
-        pl = case.planted.view(U, -1).cpu().numpy()
-        for u in range(U):
-            assert set(pl[u].tolist()) <= set(sel[u].tolist())
-    # every kept count follows the rule for its sequence
-    cnt = st.sel_cnt.view(wl.batch, wl.num_kv_heads).cpu().numpy()
-    for b in range(wl.batch):
-        n = O.block_count(lens[b], wl.block_size)
-        want = O.clamp_count(wl.top_k, n) if wl.top_k else O.keep_count(n, *wl.keep)
-        assert (cnt[b] == want).all()
-
-
-def test_long_decode_loop():
-    """256 decode steps at 131K context: pooling append + gate + sparse decode."""
-    wl = WORKLOADS["long_131k"]
-    print("[case] long decode loop", flush=True)
-    case = make_case(wl, "cuda")
-    st = state_for(case)
-    L0 = wl.context
-    lens = torch.full((wl.batch,), L0, dtype=torch.int32, device="cuda")
-    st.build_pool(lens)
-    check_steps = {0, 1, 126, 127, 128, 255}
-    sample = [(0, 0), (wl.batch - 1, wl.num_kv_heads - 1), (1, 3)]
-    for i in range(wl.decode_steps):
-        new = lens + 1
-        st.append(lens, new)
-        q = case.q[i]
-        st.step(q, new)
-        lens = new
-        if i in check_steps:
-            torch.cuda.synchronize()
-            lh = lens.tolist()
-            for (b, g) in sample:
-                check_unit(st, case, q, lh, b, g, tag=f"step{i}")
-    torch.cuda.synchronize()
-    fresh = state_for(case)
-    fresh.build_pool(lens)
-    torch.cuda.synchronize()
-    assert torch.equal(st.pooled, fresh.pooled)
-    assert torch.equal(st.open_sum, fresh.open_sum)
-
+# ------------------------------------------------------------------ graphs
 
 def test_graph_replay_matches_eager():
     """A captured decode step replays bit-identically, with eager work in between."""
@@ -597,11 +549,10 @@ def test_selection_rules(wname, rname, rule):
 
 @pytest.mark.parametrize("rule", [dict(force_first=True), dict(force_first=True, force_last=True)],
                          ids=["first", "both"])
-def test_fused_forced_blocks_equal_separate_calls(rule, monkeypatch):
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+def test_fused_forced_blocks_equal_separate_calls(rule):
     wl = SMALL["paged_small"]
     case = make_case(wl, "cuda")
-    fused, sep = state_for(case, **rule), state_for(case, **rule)
+    fused, sep = state_for(case, fuse=True, **rule), state_for(case, **rule)
     for st in (fused, sep):
         st.build_pool(case.lens)
     fused.step(case.q, case.lens)
@@ -614,25 +565,26 @@ def test_fused_forced_blocks_equal_separate_calls(rule, monkeypatch):
 @pytest.mark.parametrize("name,want", [("sparse90_32k", True), ("budget_32k", True),
                                        ("planted_8k", True), ("tiny_1k", True),
                                        ("long_131k", False), ("paged_var", False)])
-def test_fusion_policy(name, want, monkeypatch):
+def test_fusion_policy(name, want):
     """The gate is fused while each workgroup gates about one unit in one
     pass (at most one unit per workgroup, at most 256 blocks per unit), and
-    never for a threshold or unified rule; the override forces either way."""
-    from block_sparse_attention_29_amd import seer
-    monkeypatch.delenv("SEER_FUSED_GATE", raising=False)
+    never for a threshold or unified rule; the rule's fuse field forces
+    either way."""
     wl = WORKLOADS[name]
     shape = seer.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                             wl.block_size, wl.max_blocks, DT[wl.dtype])
     k_max = wl.top_k if wl.top_k else seer.keep_blocks(wl.max_blocks, *wl.keep)
-    rule = seer.make_select(keep=wl.keep) if wl.keep else seer.make_select(
-        top_k=torch.full((wl.batch,), wl.top_k, dtype=torch.int32, device="cuda"))
-    assert seer.gated_decode_is_fused(shape, rule, k_max) == want
-    thr = seer.make_select(threshold=0.0)
+    top_k = (None if wl.keep else
+             torch.full((wl.batch,), wl.top_k, dtype=torch.int32, device="cuda"))
+
+    def rule(fuse=None):
+        return seer.make_select(keep=wl.keep, top_k=top_k, fuse=fuse)
+
+    assert seer.gated_decode_is_fused(shape, rule(), k_max) == want
+    thr = seer.make_select(threshold=0.0, fuse=True)
     assert not seer.gated_decode_is_fused(shape, thr, k_max)
-    monkeypatch.setenv("SEER_FUSED_GATE", "0")
-    assert not seer.gated_decode_is_fused(shape, rule, k_max)
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
-    assert seer.gated_decode_is_fused(shape, rule, k_max)      # these all fit in LDS
+    assert not seer.gated_decode_is_fused(shape, rule(False), k_max)
+    assert seer.gated_decode_is_fused(shape, rule(True), k_max)      # these all fit in LDS
 
 
 def test_usage_example():

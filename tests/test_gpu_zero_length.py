@@ -39,11 +39,10 @@ def check_empty(st, case):
 
 
 @pytest.mark.parametrize("mode", ["fused", "separate"])
-def test_zero_length_one_token(mode, monkeypatch):
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+def test_zero_length_one_token(mode):
     case = zero_case()
     print(f"[case] zero length, one token, {mode}", flush=True)
-    st = state_for(case)
+    st = state_for(case, fuse=True)
     st.build_pool(case.lens)
     (st.step if mode == "fused" else st.step_unfused)(case.q, case.lens)
     torch.cuda.synchronize()
@@ -55,11 +54,10 @@ def test_zero_length_one_token(mode, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", ["fused", "separate"])
-def test_zero_length_tokens(mode, monkeypatch):
-    monkeypatch.setenv("SEER_FUSED_GATE", "1")
+def test_zero_length_tokens(mode):
     case = zero_case(tokens=2)
     print(f"[case] zero length, 2 tokens, {mode}", flush=True)
-    st = state_for(case, query_tokens=2)
+    st = state_for(case, query_tokens=2, fuse=True)
     st.build_pool(case.lens)
     (st.step if mode == "fused" else st.step_unfused)(case.q, case.lens)
     torch.cuda.synchronize()
