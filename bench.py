@@ -99,6 +99,12 @@ def parse():
                     help="skip the step with several query tokens per sequence")
     ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle processes for the CPU baseline (0: the host cores this "
+                         "process may run on, at most 16)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the timed step")
+    ap.add_argument("--parity-units", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -285,6 +291,20 @@ def run_workload(wl, args):
     spread = {"replays": len(reps), "p10_ms": reps[0] + 0.4 * (reps[1] - reps[0]),
               "p50_ms": reps[2], "p90_ms": reps[3] + 0.6 * (reps[4] - reps[3])}
     del g_steps
+
+    # ---- correctness of the timed step: one more step on layer 0, compared
+    # with the fp64 oracle on sampled units ----
+    parity = None
+    if not args.no_parity:
+        if loop:
+            s_last = wl.decode_steps - 1
+            q_chk, lens_chk = cases[0].q[s_last], lens_seq[s_last + 1]
+        else:
+            q_chk, lens_chk = cases[0].q, cases[0].lens
+        states[0].step(q_chk, lens_chk)
+        torch.cuda.synchronize()
+        parity = check_parity(wl, states[0], cases[0], q_chk, lens_chk, args.parity_units)
+        log(f"{wl.name}: parity {parity}")
 
     # ---- the same steps as three launches (gate kernel, partial, combine);
     # several query tokens have no fused gate, so their step is already that ----
@@ -478,7 +498,8 @@ def run_workload(wl, args):
     # ---- CPU baseline: the fp64 oracle on a bounded sample ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, cases[0], min(args.cpu_sample_seqs, wl.batch), args.cpu_seconds)
+        cpu = cpu_baseline(wl, cases[0], min(args.cpu_sample_seqs, wl.batch), args.cpu_seconds,
+                           args.cpu_workers)
 
     kept = cnt[cnt > 0]
     config = {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads,
@@ -519,53 +540,110 @@ def run_workload(wl, args):
         "dense": dense,
         "learned_gate": learned,
         "multi_token": multi,
+        "parity": parity,
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
     }
 
 
-def cpu_baseline(wl, case, n_seqs, seconds):
-    """Times the fp64 oracle's step (pool append for a decode loop, gate,
-    selection, attention) for n_seqs sequences, scaled to the whole batch."""
+def check_parity(wl, st, case, q, lens, n_units):
+    """The step's outputs against the fp64 oracle on n_units sampled units
+    (the first, the last and a seeded sample): max-abs error of out and lse,
+    how many selections are bit-exact, the smallest boundary gap
+    (s_k - s_k+1) / std(s), and how often the selection from the unrounded
+    fp64 block means agrees."""
+    import numpy as np
+
+    from oracle import seer_oracle as O
+
+    S, d, G, T = wl.block_size, wl.head_dim, wl.group, wl.query_tokens
+    Hkv = wl.num_kv_heads
+    U = wl.batch * Hkv
+    rng = np.random.default_rng(12345)
+    pick = sorted(set([0, U - 1] + rng.choice(U, size=min(U, n_units), replace=False).tolist()))
+    lens_h = lens.cpu().numpy()
+    sel_idx, sel_cnt = st.sel_idx.cpu().numpy(), st.sel_cnt.cpu().numpy()
+    out, lse = st.out.cpu().double().numpy(), st.lse.cpu().double().numpy()
+    qh = q.cpu().double().numpy()
+    err_o = err_l = 0.0
+    exact = pure = 0
+    gaps = []
+    for u in pick:
+        b, g = divmod(u, Hkv)
+        L = int(lens_h[b])
+        n = O.block_count(L, S)
+        if case.page_table is None:
+            k = case.k[b, g, :n * S].double().cpu().numpy()
+            v = case.v[b, g, :n * S].double().cpu().numpy()
+        else:
+            pages = case.page_table[b, :n].long()
+            k = case.k[pages][:, g].reshape(-1, d).double().cpu().numpy()
+            v = case.v[pages][:, g].reshape(-1, d).double().cpu().numpy()
+        p32, p64, _ = O.pool_keys(k, L, S)
+        kk = O.clamp_count(wl.top_k, n) if wl.top_k else O.keep_count(n, *wl.keep)
+        if T > 1:
+            qt = qh[b, :, g * G:(g + 1) * G]
+            s = O.gate_scores_tokens(qt, p32, d)
+            s_pure = O.gate_scores_tokens(qt, p64, d)
+        else:
+            qg = qh[b, g * G:(g + 1) * G]
+            s = O.gate_scores(qg, p32, d)
+            s_pure = O.gate_scores(qg, p64, d)
+        sel = O.select_top_blocks(s, kk)
+        exact += int(sel_cnt[u] == len(sel) and np.array_equal(sel_idx[u, :sel_cnt[u]], sel))
+        pure += int(np.array_equal(O.select_top_blocks(s_pure, kk), sel))
+        gaps.append(O.boundary_gap(s, kk))
+        if T > 1:
+            o_ref, l_ref = O.attend_tokens(qt, k, v, sel, L, S)
+            o_got = out[b, :, g * G:(g + 1) * G]
+            l_got = lse[b, :, g * G:(g + 1) * G]
+        else:
+            toks = O.selected_tokens(sel, L, S)
+            o_ref = np.stack([O.attend(qg[h], k, v, toks)[0] for h in range(G)])
+            l_ref = np.array([O.attend(qg[h], k, v, toks)[1] for h in range(G)])
+            o_got = out[b, g * G:(g + 1) * G]
+            l_got = lse[b, g * G:(g + 1) * G]
+        err_o = max(err_o, float(np.abs(o_got - o_ref).max()))
+        fin = np.isfinite(l_ref)
+        err_l = max(err_l, float(np.abs(l_got[fin] - l_ref[fin]).max(initial=0.0)))
+    return {"units_checked": len(pick), "max_abs_err_out": err_o, "max_abs_err_lse": err_l,
+            "tolerance": 2e-3 if wl.dtype == "bf16" else 1e-5,
+            "selection_bit_exact": f"{exact}/{len(pick)}",
+            "gap_min_std": float(min(gaps)),
+            "pure_fp64_selection_equal": f"{pure}/{len(pick)}"}
+
+
+def _cpu_worker(job):
+    """One oracle process of the CPU baseline: loads its units' inputs from
+    the .npy files the parent wrote, builds their pooled tables (setup), then
+    repeats the oracle's step over them for `seconds`.  Returns
+    (repetitions, seconds, units)."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import seer_oracle as O
 
-    S, d, G, TQ = wl.block_size, wl.head_dim, wl.group, wl.query_tokens
-    lens = case.lens.cpu().numpy()
-    loop = wl.decode_steps > 0
-    units = [(b, g) for b in range(n_seqs) for g in range(wl.num_kv_heads)]
-    # inputs on the host, pooled tables built with the oracle (setup, untimed)
-    data = {}
-    for (b, g) in units:
-        L = int(lens[b])
-        T = L + (1 if loop else 0)
-        if case.page_table is None:
-            k = case.k[b, g, :T].double().cpu().numpy()
-            v = case.v[b, g, :T].double().cpu().numpy()
-        else:
-            n = -(-T // S)
-            pages = case.page_table[b, :n].long()
-            k = case.k[pages][:, g].reshape(-1, d)[:T].double().cpu().numpy()
-            v = case.v[pages][:, g].reshape(-1, d)[:T].double().cpu().numpy()
+    folder, units, spec, seconds = job
+    S, d, G, TQ, loop, top_k, keep = spec
+    data = []
+    for u in units:
+        z = np.load(os.path.join(folder, f"unit{u}.npz"))
+        k = z["k"].astype(np.float64)
+        v = z["v"].astype(np.float64)
+        L = int(z["L"])
         p32, _, osum = O.pool_keys(k, L, S)
-        qsrc = case.q[0] if loop else case.q
-        if TQ > 1:  # [B][TQ][Hq][d]: the group's heads of every token
-            qg = qsrc[b, :, g * G:(g + 1) * G].double().cpu().numpy()
-        else:
-            qg = qsrc[b, g * G:(g + 1) * G].double().cpu().numpy()
-        data[(b, g)] = (k, v, p32, osum, qg, L)
+        data.append((k, v, p32, osum, z["q"], L))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            for (b, g), (k, v, p32, osum, qg, L) in data.items():
+            for (k, v, p32, osum, qg, L) in data:
                 if loop:     # append the new token, then decode at L + 1
                     p32, _ = O.pool_keys_append(p32, osum.copy(), k, L, L + 1, S)
                     L = L + 1
                 s = O.gate_scores_tokens(qg, p32, d) if TQ > 1 else O.gate_scores(qg, p32, d)
                 n = O.block_count(L, S)
-                kk = O.clamp_count(wl.top_k, n) if wl.top_k else O.keep_count(n, *wl.keep)
+                kk = O.clamp_count(top_k, n) if top_k else O.keep_count(n, *keep)
                 sel = O.select_top_blocks(s, kk)
                 if TQ > 1:
                     O.attend_tokens(qg, k, v, sel, L, S)
@@ -575,15 +653,66 @@ def cpu_baseline(wl, case, n_seqs, seconds):
                         O.attend(qg[h], k, v, toks)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= seconds or reps >= 1000:
+            if el >= seconds:
                 break
-    sec_per_step = el / reps * (wl.batch / n_seqs)   # scaled to the full batch
-    return {"value": wl.batch * TQ / sec_per_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_seqs} of {wl.batch} sequences (all {wl.num_kv_heads} KV heads"
-                      f"{f', {TQ} query tokens each' if TQ > 1 else ''}), "
+    return reps, el, len(units)
+
+
+def cpu_baseline(wl, case, n_seqs, seconds, workers):
+    """Times the fp64 oracle's step (pool append for a decode loop, gate,
+    selection, attention) on the host cores: one process per core, the
+    (sequence, KV head) units of the first n_seqs sequences dealt out to
+    them; throughput is the units all processes finish per second, scaled to
+    the whole batch."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    S, d, G, TQ = wl.block_size, wl.head_dim, wl.group, wl.query_tokens
+    lens = case.lens.cpu().numpy()
+    loop = wl.decode_steps > 0
+    units = [(b, g) for b in range(n_seqs) for g in range(wl.num_kv_heads)]
+    if workers <= 0:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    workers = max(1, min(workers, len(units)))
+    folder = tempfile.mkdtemp(prefix="seer_cpu_")
+    try:
+        import numpy as np
+        for i, (b, g) in enumerate(units):
+            L = int(lens[b])
+            T = L + (1 if loop else 0)
+            if case.page_table is None:
+                k = case.k[b, g, :T].float().cpu().numpy()
+                v = case.v[b, g, :T].float().cpu().numpy()
+            else:
+                n = -(-T // S)
+                pages = case.page_table[b, :n].long()
+                k = case.k[pages][:, g].reshape(-1, d)[:T].float().cpu().numpy()
+                v = case.v[pages][:, g].reshape(-1, d)[:T].float().cpu().numpy()
+            qsrc = case.q[0] if loop else case.q
+            if TQ > 1:  # [B][TQ][Hq][d]: the group's heads of every token
+                qg = qsrc[b, :, g * G:(g + 1) * G].double().cpu().numpy()
+            else:
+                qg = qsrc[b, g * G:(g + 1) * G].double().cpu().numpy()
+            np.savez(os.path.join(folder, f"unit{i}.npz"), k=k, v=v, q=qg, L=np.int64(L))
+        spec = (S, d, G, TQ, loop, wl.top_k, wl.keep)
+        jobs = [(folder, list(range(w, len(units), workers)), spec, seconds)
+                for w in range(workers)]
+        with mp.get_context("spawn").Pool(workers) as pool:
+            res = pool.map(_cpu_worker, jobs)
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    units_per_s = sum(reps * nu / el for reps, el, nu in res)
+    steps_per_s = units_per_s / wl.num_kv_heads          # one step = every KV head of a sequence
+    reps_min = min(r for r, _, _ in res)
+    return {"value": steps_per_s * TQ, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_seqs} of {wl.batch} sequences ({len(units)} (sequence, KV head) "
+                      f"units{f', {TQ} query tokens each' if TQ > 1 else ''}) dealt to "
+                      f"{workers} oracle processes of one thread each; "
                       f"{'pool append + ' if loop else ''}gate + top-k + attention in fp64 "
-                      f"NumPy, {reps} repetitions in {el:.1f} s, scaled to the full batch; "
-                      f"pooled tables built beforehand"}
+                      f"NumPy repeated for {seconds:.0f} s per process (at least {reps_min} "
+                      f"passes each), units per second summed over the processes and "
+                      f"scaled to tokens/s of the full batch; pooled tables built beforehand"}
 
 
 if __name__ == "__main__":
