@@ -1,9 +1,12 @@
 """Builds libseer.so (the gfx950 kernels and their C-ABI) in-tree with hipcc.
 
     python -m block_sparse_attention_29_amd.build
+    python -m block_sparse_attention_29_amd.build --host-sanitized
 
 Every source under csrc/ is compiled for gfx950 only, with packed-fp32
 instructions disabled, then linked into block_sparse_attention_29_amd/libseer.so.
+The second form builds a copy whose host layer carries AddressSanitizer and
+UndefinedBehaviorSanitizer (_build/host_sanitized/), for host-side tests.
 """
 
 from __future__ import annotations
@@ -63,6 +66,55 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "host_sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libseer_host_sanitized.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host side only (each
+# -fsanitize= right after -Xarch_host): GPU code is built without them.
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+             "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime a host process must preload to load
+    the sanitized library."""
+    import glob
+    cands = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return cands[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Builds a copy of libseer whose C++ host layer (capi.cpp: validation,
+    workspace sizing, launch geometry) carries AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernel objects of the regular
+    build (built first if missing).  For host-side checks only: load it with
+    sanitizer_runtime() preloaded."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(f)[0] + ".o"))
+               for f in SOURCES if f != "capi.cpp"):
+        build(verbose)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    obj = os.path.join(SAN_DIR, "capi.o")
+    flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS
+    r = subprocess.run([hipcc(), *flags, "-c", os.path.join(CSRC, "capi.cpp"), "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on capi.cpp (sanitized):\n{r.stdout}\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(f)[0] + ".o")
+                    for f in SOURCES if f != "capi.cpp"]
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+                        "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-o",
+                        SAN_LIB, *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)
