@@ -105,6 +105,10 @@ def parse():
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the oracle check of the timed step")
     ap.add_argument("--parity-units", type=int, default=8)
+    ap.add_argument("--fuse", choices=["auto", "always", "never"], default="auto",
+                    help="where the step selects: the library's choice (auto), inside the "
+                         "attention kernel whenever the rule allows (always), or in the gate "
+                         "kernel first (never)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -166,7 +170,7 @@ def run_workload(wl, args):
                          num_kv_heads=wl.num_kv_heads, head_dim=d, block_size=S,
                          max_blocks=wl.max_blocks, dtype=DT, k=case.k, v=case.v,
                          page_table=case.page_table, keep=wl.keep, top_k=case.top_k,
-                         query_tokens=T)
+                         query_tokens=T, fuse=args.fuse)
         st.build_pool(case.lens)
         states.append(st)
         cases.append(case)
@@ -189,10 +193,14 @@ def run_workload(wl, args):
         st, case = layer_of(i)
         if loop:
             s = i // n_layers                         # decode step of the loop
-            st.append(lens_seq[s], lens_seq[s + 1])
             q, lens = case.q[s], lens_seq[s + 1]
-        else:
-            q, lens = case.q, case.lens
+            if fused:                                 # append, gate and decode in one call
+                st.step_append(q, lens_seq[s], lens)
+            else:
+                st.append(lens_seq[s], lens)
+                st.step_unfused(q, lens)
+            return
+        q, lens = case.q, case.lens
         if fused:
             st.step(q, lens)
         else:

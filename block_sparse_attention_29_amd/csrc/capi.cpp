@@ -245,6 +245,17 @@ bool fused_gate_runs(const seer_shape* s, const seer_select* rule, int32_t k_max
   return st + dyn <= max_block_smem();
 }
 
+// How a gated call selects, for this shape, rule and wave count.
+enum GatePath {
+  kGateKernels = 0,  // the gate kernel(s) first, then the attention kernel
+  kGateFused = 1,    // scores and selection inside the attention kernel
+};
+
+GatePath gate_path(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
+                   int tokens) {
+  return fused_gate_runs(s, rule, k_max, W, tokens) ? kGateFused : kGateKernels;
+}
+
 // Turns the partial kernel's arguments into the fused gate's: the kernel
 // selects by the rule and writes scores, ids and counts.
 void set_fused_gate(const seer_shape* s, const float* pooled, const seer_select* rule,
@@ -443,6 +454,68 @@ seer_status seer_sparse_decode_partial(const seer_shape* shape, const void* q, c
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The gated partial step, with the pooling append of tokens lens_old[b] ..
+// lens[b] - 1 first when lens_old is given (pooled and open_sum updated as
+// seer_block_pool_keys would): the append runs inside the score kernel where
+// the gate has one (per-unit rules), else as its own launch.
+seer_status gated_partial(const seer_shape* shape, const void* q, const seer_kv* kv,
+                          const int32_t* lens_old, const int32_t* lens, float* pooled,
+                          double* open_sum, const seer_select* rule, int32_t k_max,
+                          float softmax_scale, double* scores, int32_t* sel_idx,
+                          int32_t* sel_cnt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (st) return st;
+  seer::DecodeArgs a;
+  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
+                           workspace, workspace_bytes, &a)))
+    return st;
+  const bool append = lens_old != nullptr;
+  if (append && (!open_sum || ((uintptr_t)open_sum & 7) != 0))
+    return fail(SEER_ERR_INVALID_ARG, "open_sum missing or not 8-byte aligned");
+  seer::GateArgs ga = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (append) {
+    ga.lens_old = lens_old;
+    ga.k = kv->k;
+    ga.page_table = kv->page_table;
+    ga.num_pages = kv->num_pages;
+    ga.pooled_out = pooled;
+    ga.open_sum = open_sum;
+  }
+  const GatePath path = gate_path(shape, rule, k_max, a.W, 1);
+  // a separate append launch where no score kernel takes it
+  const bool own_append = append && (path == kGateFused || !seer::gate_topk_appends(ga));
+  if (own_append &&
+      (st = seer_block_pool_keys(shape, kv, lens_old, lens, pooled, open_sum, stream)))
+    return st;
+  ga.append = append && !own_append;
+  hipError_t e = hipSuccess;
+  switch (path) {
+    case kGateFused:
+      set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
+      e = seer::launch_gated_decode_partial(a, stream);
+      if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
+      break;
+    default:
+      if (seer::gate_smem_bytes(ga.NB, k_max) > max_block_smem())
+        return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has",
+                    ga.NB);
+      e = seer::launch_gate_topk(ga, stream);
+      if (e != hipSuccess) return hip_fail(e, "gate_topk launch");
+      e = seer::launch_decode_partial(a, stream);
+      if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void* q,
                                              const seer_kv* kv, const int32_t* lens,
                                              const float* pooled, const seer_select* rule,
@@ -450,29 +523,26 @@ seer_status seer_gated_sparse_decode_partial(const seer_shape* shape, const void
                                              int32_t* sel_idx, int32_t* sel_cnt,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream) {
-  seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  return gated_partial(shape, q, kv, nullptr, lens, const_cast<float*>(pooled), nullptr, rule,
+                       k_max, softmax_scale, scores, sel_idx, sel_cnt, workspace,
+                       workspace_bytes, stream);
+}
+
+seer_status seer_gated_sparse_decode_append(const seer_shape* shape, const void* q,
+                                            const seer_kv* kv, const int32_t* lens_old,
+                                            const int32_t* lens, float* pooled, double* open_sum,
+                                            const seer_select* rule, int32_t k_max,
+                                            float softmax_scale, double* scores,
+                                            int32_t* sel_idx, int32_t* sel_cnt, float* out,
+                                            float* lse, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  if (!out) return fail(SEER_ERR_INVALID_ARG, "out is NULL");
+  if (!lens_old) return fail(SEER_ERR_INVALID_ARG, "lens_old is NULL");
+  const seer_status st = gated_partial(shape, q, kv, lens_old, lens, pooled, open_sum, rule,
+                                       k_max, softmax_scale, scores, sel_idx, sel_cnt, workspace,
+                                       workspace_bytes, stream);
   if (st) return st;
-  seer::DecodeArgs a;
-  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
-                           workspace, workspace_bytes, &a)))
-    return st;
-  // The fused kernel selects by top-k per unit (forced blocks included); a
-  // threshold or a unified selection, or a shape where fusing does not pay,
-  // runs the gate kernel first.
-  if (fused_gate_runs(shape, rule, k_max, a.W, 1)) {
-    set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
-    const hipError_t e = seer::launch_gated_decode_partial(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
-  } else {
-    // The gate kernel, then the partial kernel on its selection (the same
-    // results as the fused kernel where both apply).
-    if ((st = seer_gate_select(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt,
-                               stream)))
-      return st;
-    const hipError_t e = seer::launch_decode_partial(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
-  }
-  return ok();
+  return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
 }
 
 seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
@@ -489,7 +559,7 @@ seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
   const int wmax = wave_cap(shape);
   if (wmax <= 0) return fail(SEER_ERR_HIP, "cannot query the current device");
   // the same wave count and test as the gated decode calls
-  *fused = fused_gate_runs(shape, rule, k_max, decode_waves(shape, k_max, wmax), tokens);
+  *fused = (int32_t)gate_path(shape, rule, k_max, decode_waves(shape, k_max, wmax), tokens);
   return ok();
 }
 

@@ -356,10 +356,124 @@ constexpr int kSelectThreads = 256;
 // Scores of blocks j0 .. j0 + 255 of unit u (n blocks in its sequence) by a
 // 256-thread workgroup; emit(j, score) is called once for every j < n of the
 // chunk, by thread j - j0.  s_q: [D], s_part: [4][256] doubles of LDS.
-template <typename T, int D, bool VEC4, typename Emit>
+// The append of tokens lens_old[b] .. lens[b] - 1 to the blocks of one score
+// chunk [j0, j0 + 256), with pool_append_kernel's arithmetic: thread i < D
+// owns dimension i; the open block continues its fp64 sum from open_sum, a
+// block the append opens starts from its first token, tokens are added in
+// order, and each touched block's new mean is written to the pooled table and
+// handed to the scoring lanes (through LDS for the chunk's first kStash
+// touched blocks, else read back at device scope after the barrier).  Only
+// the workgroup holding block lens_old / S reads and writes open_sum (the new
+// value is the last touched block's sum, from its first token when that is a
+// later block), so no two workgroups race on it.  issue() runs right after the
+// pooled loads (the open sum and first key row of the chunk's first touched
+// block, so a one-token append waits on no round trip of its own), apply()
+// after the query loads, patch() after the barrier.  Tokens of a block
+// without a valid page are skipped.
+constexpr int kStash = 4;
+
+template <typename T, int D>
+struct ChunkAppend {
+  int lo, hi, jlo, jhi, ja, jb;  // the append's tokens and blocks, the chunk's touched range
+  double os0, x0;                // thread i: open sum and first key of block ja, dim i
+
+  __device__ __forceinline__ int64_t row_of(const GateArgs& a, int b, int g, int t) const {
+    const int S = a.S, j = t / S, pos = t - j * S;
+    if (a.page_table) {
+      const int pg = a.page_table[(int64_t)b * a.NB + j];
+      if (pg < 0 || pg >= a.num_pages) return -1;
+      return (((int64_t)pg * a.Hkv + g) * S + pos) * D;
+    }
+    return (((int64_t)b * a.Hkv + g) * ((int64_t)a.NB * S) + t) * D;
+  }
+
+  __device__ __forceinline__ void issue(const GateArgs& a, int u, int b, int g, int n, int j0,
+                                        int lens_old) {
+    const int S = a.S;
+    const int64_t cap = (int64_t)a.NB * S;
+    lo = lens_old;
+    hi = a.lens[b];
+    if (hi > cap) hi = (int)cap;
+    ja = 0;
+    jb = -1;
+    if (lo < 0 || lo >= hi) return;
+    jlo = lo / S;
+    jhi = (hi - 1) / S;
+    ja = max(jlo, j0);
+    jb = min(min(jhi, j0 + kScoreChunk - 1), n - 1);
+    const int tid = threadIdx.x;
+    if (ja > jb || tid >= D) return;
+    const int t0 = ja * S > lo ? ja * S : lo;
+    os0 = (ja == jlo && lo % S != 0) ? a.open_sum[(int64_t)u * D + tid] : 0.0;
+    const int64_t r = row_of(a, b, g, t0);
+    x0 = r < 0 ? __builtin_nan("") : load_as_double<T>((const T*)a.k, r + tid);
+  }
+
+  __device__ __forceinline__ void apply(const GateArgs& a, int u, int b, int g,
+                                        float (*s_new)[D]) {
+    const int tid = threadIdx.x;
+    if (ja > jb || tid >= D) return;
+    const int S = a.S, NB = a.NB;
+    const T* kc = (const T*)a.k;
+    auto block_sum = [&](int j, int t0, int t1, double& acc) {
+      for (int t = t0; t < t1; ++t) {
+        const int64_t r = row_of(a, b, g, t);
+        if (r < 0) continue;
+        const double x = load_as_double<T>(kc, r + tid);
+        acc = t == j * S ? x : acc + x;
+      }
+    };
+    for (int j = ja; j <= jb; ++j) {
+      const int t0 = j * S > lo ? j * S : lo;
+      const int t1 = j * S + S < hi ? j * S + S : hi;
+      double acc;
+      if (j == ja) {  // the prefetched open sum and first token
+        acc = __builtin_isnan(x0) ? os0 : (t0 == j * S ? x0 : os0 + x0);
+        block_sum(j, t0 + 1, t1, acc);
+      } else {
+        acc = 0.0;
+        block_sum(j, t0, t1, acc);
+      }
+      const float m = (float)(acc / (double)(t1 - j * S));
+      a.pooled_out[((int64_t)u * D + tid) * NB + j] = m;
+      if (j - ja < kStash) s_new[j - ja][tid] = m;
+      if (j == jlo) {
+        if (jhi != jlo) {
+          acc = 0.0;
+          block_sum(jhi, jhi * S, hi, acc);
+        }
+        a.open_sum[(int64_t)u * D + tid] = acc;
+      }
+    }
+  }
+
+  // the lane's pooled values of the touched blocks it holds
+  template <int DQ, typename Blk>
+  __device__ __forceinline__ void patch(const GateArgs& a, int u, int qd, Blk blk,
+                                        const float (*s_new)[D], float (&pv)[DQ][4]) const {
+    if (ja > jb) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = blk(e);
+      if (j < ja || j > jb) continue;
+      if (j - ja < kStash) {
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) pv[i][e] = s_new[j - ja][qd * DQ + i];
+      } else {
+        float* col = a.pooled_out + ((int64_t)u * D + qd * DQ) * a.NB + j;
+#pragma unroll
+        for (int i = 0; i < DQ; ++i)
+          pv[i][e] = __hip_atomic_load(col + (int64_t)i * a.NB, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+};
+
+template <typename T, int D, bool VEC4, bool APPEND = false, typename Emit>
 __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int g, int n, int j0,
                                             double* s_q, double (*s_part)[kScoreChunk],
-                                            Emit emit) {
+                                            Emit emit, int lens_old = 0) {
   constexpr int DQ = D / 4;
   const int tid = threadIdx.x, qd = tid >> 6, lane = tid & 63;
   const int NB = a.NB;
@@ -383,6 +497,9 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), n - 1))];
   }
+  ChunkAppend<T, D> ap;
+  __shared__ float s_new[APPEND ? kStash : 1][D];
+  if constexpr (APPEND) ap.issue(a, u, b, g, n, j0, lens_old);
 
   // ---- group-summed query, fp64, token-major then head order ----
   if (tid < D) {
@@ -400,7 +517,9 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
     }
     s_q[tid] = sq;
   }
+  if constexpr (APPEND) ap.apply(a, u, b, g, s_new);
   __syncthreads();
+  if constexpr (APPEND) ap.template patch<DQ>(a, u, qd, blk, s_new, pv);
 
   // ---- quarter dot products, then the blocks' sums in quarter order ----
 #pragma unroll
@@ -418,24 +537,26 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
   }
 }
 
-template <typename T, int D, bool VEC4>
+template <typename T, int D, bool VEC4, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void gate_score_kernel(GateArgs a) {
   __shared__ double s_q[D];
   __shared__ double s_part[4][kScoreChunk];
   const int nchunk = (a.NB + kScoreChunk - 1) / kScoreChunk;
   const int u = (int)blockIdx.x / nchunk, c = (int)blockIdx.x - u * nchunk;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
   const int j0 = c * kScoreChunk;
   if (j0 >= n) return;  // the whole workgroup: nothing of this chunk is in the sequence
   double* out = a.scores + (int64_t)u * a.NB;
-  score_chunk<T, D, VEC4>(a, u, b, g, n, j0, s_q, s_part,
-                          [&](int j, double sc) { out[j] = key_score(order_key(sc)); });
+  score_chunk<T, D, VEC4, APPEND>(a, u, b, g, n, j0, s_q, s_part,
+                                  [&](int j, double sc) { out[j] = key_score(order_key(sc)); },
+                                  lens_old);
 }
 
 // Tables of at most 256 blocks: one workgroup per unit scores its chunk into
 // LDS keys and selects, in one launch.
-template <typename T, int D, bool VEC4>
+template <typename T, int D, bool VEC4, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   extern __shared__ uint64_t s_key[];  // [NB] order keys of the unit's scores
   __shared__ double s_q[D];
@@ -443,10 +564,12 @@ __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   __shared__ int s_hist[3 * 256];
   __shared__ int s_scan[kScoreThreads / 64 + 1];
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
+  const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
   if (n > 0) {
-    score_chunk<T, D, VEC4>(a, u, b, g, n, 0, s_q, s_part,
-                            [&](int j, double sc) { s_key[j] = order_key(sc); });
+    score_chunk<T, D, VEC4, APPEND>(a, u, b, g, n, 0, s_q, s_part,
+                                    [&](int j, double sc) { s_key[j] = order_key(sc); },
+                                    lens_old);
     __syncthreads();
   }
   gate_finish<kScoreThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
@@ -718,20 +841,37 @@ size_t gate_smem_bytes(int NB, int k_max) {
   return (size_t)NB * sizeof(uint64_t) + (size_t)k_max * sizeof(int32_t);
 }
 
-template <typename T, int D>
-const void* score_fn(bool vec4, bool one_chunk) {
+template <typename T, int D, bool APPEND>
+const void* score_fn_a(bool vec4, bool one_chunk) {
   if (one_chunk)
-    return vec4 ? (const void*)&gate_unit_kernel<T, D, true>
-                : (const void*)&gate_unit_kernel<T, D, false>;
-  return vec4 ? (const void*)&gate_score_kernel<T, D, true>
-              : (const void*)&gate_score_kernel<T, D, false>;
+    return vec4 ? (const void*)&gate_unit_kernel<T, D, true, APPEND>
+                : (const void*)&gate_unit_kernel<T, D, false, APPEND>;
+  return vec4 ? (const void*)&gate_score_kernel<T, D, true, APPEND>
+              : (const void*)&gate_score_kernel<T, D, false, APPEND>;
 }
+
+template <typename T, int D>
+const void* score_fn(bool vec4, bool one_chunk, bool append) {
+  return append ? score_fn_a<T, D, true>(vec4, one_chunk) : score_fn_a<T, D, false>(vec4, one_chunk);
+}
+
+const void* pick_score_fn(const GateArgs& a, bool one_chunk) {
+  const bool vec4 = a.NB % 4 == 0, ap = a.append != 0;
+  if (a.dtype == 1)
+    return a.D == 64 ? score_fn<uint16_t, 64>(vec4, one_chunk, ap)
+                     : score_fn<uint16_t, 128>(vec4, one_chunk, ap);
+  return a.D == 64 ? score_fn<float, 64>(vec4, one_chunk, ap)
+                   : score_fn<float, 128>(vec4, one_chunk, ap);
+}
+
+bool gate_topk_appends(const GateArgs& a) { return !a.unified; }
 
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
   const int U = a.B * a.Hkv;
   GateArgs args = a;
   void* params[] = {&args};
   if (a.unified) {
+    if (a.append) return hipErrorInvalidValue;  // the caller appends first
     const void* fn;
     if (a.dtype == 1) fn = a.D == 64 ? (const void*)&gate_topk_kernel<uint16_t, 64, true>
                                      : (const void*)&gate_topk_kernel<uint16_t, 128, true>;
@@ -740,13 +880,9 @@ hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
     return hipLaunchKernel(fn, dim3(a.B), dim3(kTopkThreads), params,
                            gate_smem_bytes(a.NB, a.k_max), stream);
   }
-  const bool vec4 = a.NB % 4 == 0;
   const int nchunk = (a.NB + kScoreChunk - 1) / kScoreChunk;
   const bool one = nchunk == 1;
-  const void* sfn = a.dtype == 1 ? (a.D == 64 ? score_fn<uint16_t, 64>(vec4, one)
-                                              : score_fn<uint16_t, 128>(vec4, one))
-                                 : (a.D == 64 ? score_fn<float, 64>(vec4, one)
-                                              : score_fn<float, 128>(vec4, one));
+  const void* sfn = pick_score_fn(a, one);
   if (one)  // scores and selection in one launch
     return hipLaunchKernel(sfn, dim3(U), dim3(kScoreThreads), params,
                            (size_t)a.NB * sizeof(uint64_t), stream);

@@ -121,9 +121,23 @@ struct GateArgs {
   const float* w1_scale;
   const float* b1;
   const float* wq;
+  // Pooling append fused into the per-unit score kernels (append set): tokens
+  // lens_old[b] .. lens[b] - 1 of the cache k (page_table as in PoolArgs) are
+  // added to the open block's fp64 sum exactly as launch_pool_keys appends
+  // them; the touched blocks' pooled columns (pooled_out, the same table as
+  // pooled) and open_sum are rewritten and the scores use the new means.
+  int32_t append;
+  const int32_t* lens_old;
+  const void* k;
+  const int32_t* page_table;
+  int64_t num_pages;
+  float* pooled_out;
+  double* open_sum;
 };
 
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream);
+// Whether launch_gate_topk can take a.append (per-unit rules; not unified).
+bool gate_topk_appends(const GateArgs& a);
 // Dynamic LDS of the gate kernel.
 size_t gate_smem_bytes(int NB, int k_max);
 // The learned gate network's scores, then the same selection rule (not unified).

@@ -465,13 +465,14 @@ void decode_partial_kernel(DecodeArgs a) {
 //   o = sum_w acc_w 2^(m_w - M),  l = sum_w l_w 2^(m_w - M)
 // as fma chains in record order, out = o / l, lse = M + log2(l) (natural log
 // on output).  Up to 32 records it runs in one shot (every load up front);
-// beyond, in two passes over chunks of records.  The order is fixed, so the
-// result is deterministic, and the per-head kernel below runs the same
-// operations, so the two give identical bits.
+// beyond, over chunks of kHeadChunk records, each folded into a running
+// maximum.  The order is fixed, so the result is deterministic, and the
+// per-head kernel below runs the same schedule operation for operation, so
+// the two give identical bits.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineChunk = 256;  // records whose (m, l) are staged per pass (general path)
 constexpr int kCombineBatch = 16;   // acc loads in flight per thread (general path)
 constexpr int kCombineFast = 32;    // units with at most this many records: one-shot path
+constexpr int kHeadChunk = 64;      // records per chunk of the running merge (both kernels)
 
 // One-shot merge of a unit with at most NWB records: thread tid owns the EPT
 // consecutive elements tid*EPT.. of one head (EPT a power of two, so it
@@ -536,8 +537,8 @@ __global__ __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu
 void decode_combine_kernel(CombineArgs a) {
   constexpr int REC = G * D + 16;
   constexpr int PER = (G * D + kCombineThreads - 1) / kCombineThreads;
-  __shared__ float s_mw[kCombineChunk][G];  // record maxima (-inf: empty wave)
-  __shared__ float s_lw[kCombineChunk][G];  // record sums
+  __shared__ float s_mw[kHeadChunk][G];  // a chunk's record maxima (-inf: empty wave)
+  __shared__ float s_lw[kHeadChunk][G];  // and sums
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -564,17 +565,18 @@ void decode_combine_kernel(CombineArgs a) {
   if (nw <= 16) return combine_shot<D, G, 16>(a, part, nw, wlo, W, Tot, head0);
   if (nw <= kCombineFast) return combine_shot<D, G, kCombineFast>(a, part, nw, wlo, W, Tot, head0);
 
-  // General path (many records per unit): the one-shot merge's two passes
-  // over all records -- the maximum M of the used records' maxima, then the
-  // rescaled values summed in record order -- with (m, l) staged through LDS
-  // in chunks and the values fetched kCombineBatch records at a time.  The
-  // result does not depend on the chunking.
+  // General path (more than 32 records): the per-head kernel's schedule --
+  // chunks of kHeadChunk records in order, each merged into the running
+  // state by its maximum Mc: M' = max(M, Mc), the state rescaled by
+  // 2^(M - M'), then the chunk's values rescaled by 2^(m_w - M') and added as
+  // an fma chain in record order.  A chunk's (m, l) are staged through LDS,
+  // its values fetched kCombineBatch records at a time.
   float o[PER], M[PER], l[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) { o[r] = 0.f; M[r] = kNegInf; l[r] = 0.f; }
-
-  auto stage = [&](int c0, int cn) {
-    __syncthreads();  // the previous chunk's (m, l) fully consumed
+  for (int c0 = 0; c0 < nw; c0 += kHeadChunk) {
+    const int cn = min(kHeadChunk, nw - c0);
+    if (c0 > 0) __syncthreads();  // the previous chunk's (m, l) fully consumed
     for (int t = tid; t < cn; t += kCombineThreads) {
       const bool e = empty(c0 + t);
       const float* r = part + (int64_t)(c0 + t) * REC;
@@ -588,30 +590,21 @@ void decode_combine_kernel(CombineArgs a) {
       }
     }
     __syncthreads();
-  };
-  // pass 1: maxima (empty records staged as -inf change nothing)
-  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
-    const int cn = min(kCombineChunk, nw - c0);
-    stage(c0, cn);
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       const int idx = r * kCombineThreads + tid;
       if (idx >= G * D) continue;
       const int h = idx / D;
-      for (int t = 0; t < cn; ++t) M[r] = fmaxf(M[r], s_mw[t][h]);
-    }
-  }
-  // pass 2: sums in record order (a single chunk stays staged from pass 1)
-  for (int c0 = 0; c0 < nw; c0 += kCombineChunk) {
-    const int cn = min(kCombineChunk, nw - c0);
-    if (nw > kCombineChunk) stage(c0, cn);
-    for (int t0 = 0; t0 < cn; t0 += kCombineBatch) {
-      const int tn = min(kCombineBatch, cn - t0);
-#pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int idx = r * kCombineThreads + tid;
-        if (idx >= G * D) continue;
-        const int h = idx / D;
+      float Mc = kNegInf;
+      for (int t = 0; t < cn; ++t) Mc = fmaxf(Mc, s_mw[t][h]);
+      if (Mc == kNegInf) continue;  // no valid token in the chunk
+      const float Mn = fmaxf(M[r], Mc);
+      // Arguments are <= 0 (or -inf, giving 0): the hardware exp2 is accurate there.
+      const float sres = __builtin_amdgcn_exp2f(M[r] - Mn);
+      o[r] *= sres;
+      l[r] *= sres;
+      for (int t0 = 0; t0 < cn; t0 += kCombineBatch) {
+        const int tn = min(kCombineBatch, cn - t0);
         const float* base = part + (int64_t)(c0 + t0) * REC;  // uniform
         float x[kCombineBatch];
 #pragma unroll
@@ -619,16 +612,15 @@ void decode_combine_kernel(CombineArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kCombineBatch; ++t) {
-          if (t >= tn) break;
-          const float mw = s_mw[t0 + t][h];
+          const float mw = t < tn ? s_mw[t0 + t][h] : kNegInf;
           // records without a valid token (m = -inf) and empty records add nothing
           const bool use = mw != kNegInf;
-          // Arguments are <= 0: the hardware exp2 is accurate there.
-          const float sc = __builtin_amdgcn_exp2f(use ? mw - M[r] : 0.f);
+          const float sc = __builtin_amdgcn_exp2f(mw - Mn);
           o[r] = use ? fmaf(x[t], sc, o[r]) : o[r];
           l[r] = use ? fmaf(s_lw[t0 + t][h], sc, l[r]) : l[r];
         }
       }
+      M[r] = Mn;
     }
   }
 #pragma unroll
@@ -644,14 +636,13 @@ void decode_combine_kernel(CombineArgs a) {
 // The same merge with one workgroup per query head and one thread per element,
 // for units with many records (few, long units): a head's records share their
 // (m, l), so each thread loads only its element's values of every record.
-// The arithmetic is the per-unit kernel's, operation for operation: the
-// maximum M of the used records' maxima, then o = sum_t x_t 2^(m_t - M) and
-// l = sum_t l_t 2^(m_t - M) as fma chains in record order, out = o / l -- so
-// the two kernels give bit-identical results.  Up to 32 records every load is
-// issued up front (code paths sized to 8, 16 and 32); beyond, the maxima
-// first, then the values kHeadChunk records at a time.
-constexpr int kHeadChunk = 64;
-
+// Records are merged in chunks of up to kHeadChunk = 64 (8, 16 or 32 when the
+// unit has no more): the chunk's maximum Mc, then its values rescaled by
+// 2^(m_w - M') and summed in record order into the running state,
+// M' = max(M, Mc), which is rescaled once by 2^(M - M').  The per-unit kernel
+// runs the same schedule with the same chunks (a unit with at most 32 records
+// is one chunk there too: combine_shot), operation for operation, so the two
+// kernels give bit-identical results.
 template <int D, int G>
 __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
   constexpr int REC = G * D + 16;
@@ -674,11 +665,8 @@ __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
   const int nw = whi - wlo + 1;
   const float* part = a.part + (int64_t)(u + wlo) * REC;  // record of wave wlo + t at t * REC
   const EqualSplit sp(Tot, W);
-  // Waves are only ever empty when there are fewer tiles than waves.
-  auto empty = [&](int t) { return Tot < W && wave_empty(sp, wlo + t); };
   float M = kNegInf, l = 0.f, o = 0.f;
-  // records t0 .. t0 + CH - 1 (those below nw) summed into (o, l) under M
-  auto sums = [&](int t0, auto ch_tag) {
+  auto chunk = [&](int t0, auto ch_tag) {
     constexpr int CH = decltype(ch_tag)::value;
     const int tn = min(CH, nw - t0);
     float x[CH], mv[CH], lv[CH];
@@ -689,35 +677,38 @@ __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
       mv[t] = r[G * D + h];
       lv[t] = r[G * D + 8 + h];
     }
+    // Waves are only ever empty when there are fewer tiles than waves.
     uint64_t skip = 0;
-    for (int t = 0; t < tn; ++t) skip |= empty(t0 + t) ? (1ull << t) : 0ull;
-    if (t0 == 0 && nw <= CH) {  // one shot: the maximum from the same loads
-#pragma unroll
-      for (int t = 0; t < CH; ++t) {
-        const bool use = t < tn && !((skip >> t) & 1ull);
-        M = use ? fmaxf(M, mv[t]) : M;
-      }
-    }
-    if (M == kNegInf) return;  // no valid token anywhere
+    if (Tot < W)
+      for (int t = 0; t < tn; ++t) skip |= wave_empty(sp, wlo + t0 + t) ? (1ull << t) : 0ull;
+    float Mc = kNegInf;
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-      // Records without a valid token (m = -inf) and empty records add
-      // nothing; stale slots may hold anything, so they are selected away.
+      const bool use = t < tn && !((skip >> t) & 1ull);
+      Mc = use ? fmaxf(Mc, mv[t]) : Mc;
+    }
+    if (Mc == kNegInf) return;  // no valid token in the chunk
+    const float Mn = fmaxf(M, Mc);
+    // Arguments are <= 0 (or -inf, giving 0): the hardware exp2 is accurate there.
+    const float s = __builtin_amdgcn_exp2f(M - Mn);
+    o *= s;
+    l *= s;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      // Records without a valid token (m = -inf) and skipped slots add nothing;
+      // stale slots may hold anything, so they are selected away, not scaled.
       const bool use = t < tn && !((skip >> t) & 1ull) && mv[t] != kNegInf;
-      // Arguments are <= 0: the hardware exp2 is accurate there.
-      const float sc = __builtin_amdgcn_exp2f(mv[t] - M);
+      const float sc = __builtin_amdgcn_exp2f(mv[t] - Mn);
       o = use ? fmaf(x[t], sc, o) : o;
       l = use ? fmaf(lv[t], sc, l) : l;
     }
+    M = Mn;
   };
-  if (nw <= 8) sums(0, std::integral_constant<int, 8>{});
-  else if (nw <= 16) sums(0, std::integral_constant<int, 16>{});
-  else if (nw <= 32) sums(0, std::integral_constant<int, 32>{});
-  else {
-    for (int t = 0; t < nw; ++t)
-      if (!empty(t)) M = fmaxf(M, part[(int64_t)t * REC + G * D + h]);
-    for (int t0 = 0; t0 < nw; t0 += kHeadChunk) sums(t0, std::integral_constant<int, kHeadChunk>{});
-  }
+  if (nw <= 8) chunk(0, std::integral_constant<int, 8>{});
+  else if (nw <= 16) chunk(0, std::integral_constant<int, 16>{});
+  else if (nw <= 32) chunk(0, std::integral_constant<int, 32>{});
+  else
+    for (int t0 = 0; t0 < nw; t0 += kHeadChunk) chunk(t0, std::integral_constant<int, kHeadChunk>{});
   a.out[head * D + tid] = l > 0.f ? o / l : 0.f;
   if (a.lse && tid == 0) a.lse[head] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
 }

@@ -10,6 +10,8 @@ table, open-block sums, scores, selection, outputs, workspace) and enqueues:
     attend(q, lens)              sparse (or dense) decode attention
     step(q, lens)                select + attend, the gate fused into the attention
                                  kernel (two launches; with a learned gate, three)
+    step_append(q, old, new)     append, then step (the append inside the gate's score
+                                 kernel where there is one)
     step_unfused(q, lens)        select, then attend (three launches)
 
 all on torch's current stream, with no host synchronisation.
@@ -137,6 +139,18 @@ class DecodeState:
         seer.gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled, self.rule,
                                  self.k_max, self.scores, self.sel_idx, self.sel_cnt, self.out,
                                  self.lse, self.workspace)
+        return self.out, self.lse
+
+    def step_append(self, q: torch.Tensor, lens_old: torch.Tensor, lens_new: torch.Tensor):
+        """append(lens_old, lens_new) then step(q, lens_new), as one call (the
+        pooling append inside the gate's score kernel where it has one)."""
+        if self.gate_weights is not None or self.T > 1 or self.combine != seer.SEER_COMBINE_AUTO:
+            self.append(lens_old, lens_new)
+            return self.step(q, lens_new)
+        seer.gated_sparse_decode_append(self.shape, q, self.kv, lens_old, lens_new, self.pooled,
+                                        self.open_sum, self.rule, self.k_max, self.scores,
+                                        self.sel_idx, self.sel_cnt, self.out, self.lse,
+                                        self.workspace)
         return self.out, self.lse
 
     def step_unfused(self, q: torch.Tensor, lens: torch.Tensor):

@@ -41,6 +41,7 @@ EXPORTS = (
     "seer_gated_sparse_decode_partial",
     "seer_gated_decode_is_fused",
     "seer_gated_sparse_decode_no_alloc",
+    "seer_gated_sparse_decode_append",
     "seer_multi_gate_select",
     "seer_multi_sparse_decode_workspace_size",
     "seer_multi_sparse_decode",
@@ -178,6 +179,9 @@ def load(path: str = LIB_PATH):
                                                      ctypes.c_size_t, _P]
     lib.seer_gated_sparse_decode_no_alloc.argtypes = [SP, _P, KP, _P, _P, RP, _I32,
                                                       ctypes.c_float, _P, _P, _P, _P, _P, _P]
+    lib.seer_gated_sparse_decode_append.argtypes = [SP, _P, KP, _P, _P, _P, _P, RP, _I32,
+                                                    ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                                    ctypes.c_size_t, _P]
     lib.seer_gated_decode_is_fused.argtypes = [SP, _I32, RP, _I32, ctypes.POINTER(ctypes.c_int32)]
     lib.seer_multi_gated_sparse_decode.argtypes = [SP, _I32, _P, KP, _P, _P, RP, _I32,
                                                    ctypes.c_float, _P, _P, _P, _P, _P, _P,
@@ -198,7 +202,7 @@ def load(path: str = LIB_PATH):
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
                  "seer_sparse_decode_combine_mode",
                  "seer_gated_sparse_decode", "seer_gated_sparse_decode_partial",
-                 "seer_gated_sparse_decode_no_alloc"):
+                 "seer_gated_sparse_decode_no_alloc", "seer_gated_sparse_decode_append"):
         getattr(lib, name).restype = _I32
     _lib = lib
     return lib
@@ -537,3 +541,30 @@ def gated_sparse_decode_no_alloc(shape: Shape, q: torch.Tensor, kv: KV, lens: to
         ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
         ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(out), _ptr(lse), _stream()))
+
+
+def gated_sparse_decode_append(shape: Shape, q: torch.Tensor, kv: KV, lens_old: torch.Tensor,
+                               lens: torch.Tensor, pooled: torch.Tensor, open_sum: torch.Tensor,
+                               rule: Select, k_max: int, scores: torch.Tensor,
+                               sel_idx: torch.Tensor, sel_cnt: torch.Tensor, out: torch.Tensor,
+                               lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                               softmax_scale: float = 0.0):
+    """seer_gated_sparse_decode_append: pool the tokens lens_old .. lens - 1,
+    then the gated decode step at lens."""
+    lib = load()
+    _need_q(shape, q)
+    U = shape.batch * shape.num_kv_heads
+    _need(lens_old, torch.int32, shape.batch, "lens_old")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(open_sum, torch.float64, U * shape.head_dim, "open_sum")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
+    _check(lib.seer_gated_sparse_decode_append(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens_old), _ptr(lens), _ptr(pooled),
+        _ptr(open_sum), ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx),
+        _ptr(sel_cnt), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))

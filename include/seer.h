@@ -309,8 +309,8 @@ seer_status seer_sparse_decode_combine_mode(const seer_shape* shape, int32_t mod
 /* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode
  * (tokens = 1) or seer_multi_gated_sparse_decode (tokens > 1) with this shape,
  * rule and k_max selects inside the attention kernel on the current device,
- * 0 if it runs the gate kernel first (no launch; results are the same either
- * way).  SEER_ERR_INVALID_ARG for NULL pointers, k_max outside [1,
+ * 0 if it runs the gate kernel(s) first (no launch; results are the same
+ * either way).  SEER_ERR_INVALID_ARG for NULL pointers, k_max outside [1,
  * max_blocks] or a token count outside [1, 16 / G]. */
 seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
                                        const seer_select* rule, int32_t k_max, int32_t* fused);
@@ -350,6 +350,26 @@ seer_status seer_gated_sparse_decode_no_alloc(const seer_shape* shape, const voi
                                               int32_t k_max, float softmax_scale, double* scores,
                                               int32_t* sel_idx, int32_t* sel_cnt, float* out,
                                               float* lse, hipStream_t stream);
+
+/* seer_gated_sparse_decode_append -- one decode step after new tokens entered
+ * the cache: seer_block_pool_keys(kv, lens_old, lens, pooled, open_sum)
+ * followed by seer_gated_sparse_decode(lens, pooled, ...), with bit-identical
+ * results (pooled, open_sum, scores, sel_idx, sel_cnt, out, lse).  Where the
+ * step has a score kernel for per-unit rules, the pooling append runs inside
+ * it (the open block's new mean is computed, used and written there), one
+ * launch fewer; otherwise it is its own launch first.  The keys of tokens
+ * lens_old[b] .. lens[b] - 1 must be in the cache.
+ *  Arguments: as seer_block_pool_keys (kv, lens_old, pooled and open_sum in
+ *  and out) and seer_gated_sparse_decode (the rest; lens = lens_new).
+ *  Errors as those calls'; lens_old NULL is SEER_ERR_INVALID_ARG. */
+seer_status seer_gated_sparse_decode_append(const seer_shape* shape, const void* q,
+                                            const seer_kv* kv, const int32_t* lens_old,
+                                            const int32_t* lens, float* pooled, double* open_sum,
+                                            const seer_select* rule, int32_t k_max,
+                                            float softmax_scale, double* scores,
+                                            int32_t* sel_idx, int32_t* sel_cnt, float* out,
+                                            float* lse, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
 
 /* Several new query tokens per sequence (speculative or chunked decode).
  *

@@ -150,9 +150,8 @@ def test_long_decode_loop_every_unit():
     gaps = []
     for i in range(wl.decode_steps):
         new = lens + 1
-        st.append(lens, new)
         q = case.q[i]
-        st.step(q, new)
+        st.step_append(q, lens, new)       # pooling append inside the gate's score launch
         lens = new
         if i not in check_steps:
             continue

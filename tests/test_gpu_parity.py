@@ -218,19 +218,21 @@ def test_decode_with_oracle_selection():
         assert np.abs(out - ref["out"]).max() <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("fuse", [True, None], ids=["forced", "auto"])
 @pytest.mark.parametrize("name", sorted(SMALL) + ["budget_32k", "long_131k", "paged_var"])
-def test_gated_equals_separate_calls_bitwise(name):
-    """The fused gate + attention call writes exactly what the gate call
-    followed by the attention call writes: scores, ids, counts, out, lse.
-    The fused kernel is forced, also where the call would not choose it (more
-    than 256 blocks per unit, more units than workgroups)."""
+def test_gated_equals_separate_calls_bitwise(name, fuse):
+    """The gated call writes exactly what the gate call followed by the
+    attention call writes: scores, ids, counts, out, lse -- with the fused
+    kernel forced, also where the call would not choose it (more than 256
+    blocks per unit, more units than workgroups), and on the library's own
+    choice."""
     wl = SMALL[name] if name in SMALL else WORKLOADS[name].with_(batch=2)
     if name == "paged_var":
         wl = WORKLOADS[name].with_(batch=48)     # 384 units on 256 workgroups
     print(f"[case] gated vs separate {name}", flush=True)
     case = make_case(wl, "cuda")
     q = case.q[0] if wl.decode_steps else case.q
-    fused, sep = state_for(case, fuse=True), state_for(case)
+    fused, sep = state_for(case, fuse=fuse), state_for(case)
     for st in (fused, sep):
         st.build_pool(case.lens)
     fused.step(q, case.lens)
