@@ -20,6 +20,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Two floats rounded to bf16 (nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Element e of a 16-byte chunk holding bf16 (T = uint16_t) or fp32 (T = float).
 template <typename T>
 __device__ __forceinline__ float chunk_elem(const uint4& c, int e);

@@ -26,10 +26,18 @@
 //    product is q . k whatever order the unit uses internally.  The 16x16
 //    result holds logit (head 4*r + i, token n) in lane (r, n), register i.
 //  * takes the tile max per head with DPP row reductions, rescales, and
-//    writes exp2 probabilities to a 1 KiB LDS buffer per wave;
+//    writes exp2 probabilities to a 2 KiB LDS buffer per wave;
 //  * streams V rows fully coalesced (16 bytes per lane, whole rows per
-//    instruction) and accumulates p * v in fp32 on the VALU; probabilities stay
-//    in fp32 (no rounding to bf16 before the product).
+//    instruction) and multiplies:
+//    - bf16, d = 128: on the matrix cores, v_mfma_f32_16x16x32_bf16 with the
+//      tile's 32 tokens as k.  Each probability is split into two bf16 parts
+//      (p = hi + lo to 16 significant bits; the products are exact and summed
+//      in fp32), written to LDS as [head][token] and read back as the A
+//      operand; lane (r, n) loads tokens 8r .. 8r + 7 at dimensions 8n ..
+//      8n + 7, so the B operand of dimension step e is the e-th element of
+//      its 8 chunks, packed in pairs.  The accumulators hold O[head][dim]
+//      directly (no cross-lane sum at the end), in fp32.
+//    - fp32 or d = 64: fp32 FMAs on the VALU, probabilities in fp32.
 // The K registers are refilled with the next tile right after the QK product
 // and the V registers right after the PV product, so each wave keeps about one
 // tile of loads in flight while it computes.
@@ -50,6 +58,10 @@ void decode_partial_kernel(DecodeArgs a) {
   constexpr int EB = GE::EB, ROWB = GE::ROWB, E = GE::E, NKL = GE::NKL;
   constexpr int LPR = GE::LPR, RPI = GE::RPI, NVL = GE::NVL;
   constexpr int REC = G * D + 16;  // partial record: acc[G][D], m[8], l[8] (floats)
+  // bf16 caches with d = 128 multiply P V on the matrix cores (MPV); other
+  // caches on the VALU.
+  constexpr bool MPV = EB == 2 && D == 128;
+  static_assert(!MPV || NVL == 8, "MPV: one 16-byte V chunk per lane and token row");
 
   __shared__ __align__(16) float s_p[kWavesPerWG][kTile * 16];
   extern __shared__ int s_dyn[];
@@ -256,13 +268,21 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
     float m_run[4], l_run[4];
-    float acc[G][E];
+    float acc[MPV ? 1 : G][MPV ? 1 : E];  // VALU: (head, element of the lane's V chunk)
+    f32x4 oacc[MPV ? 8 : 1];              // MPV: dimension step e (see pv)
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m_run[i] = kNegInf; l_run[i] = 0.f; }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < (MPV ? 1 : G); ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+      for (int e = 0; e < (MPV ? 1 : E); ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < (MPV ? 8 : 1); ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Token of MFMA column n16 in the tile's 16-token column ct.  Any
+    // assignment gives the same logits; MPV pairs each lane's two tokens
+    // (2 n16, 2 n16 + 1) so that its probabilities go to LDS as whole words.
+    auto tok = [&](int ct) { return MPV ? 2 * n16 + ct : ct * 16 + n16; };
 
     uint4 kr[kCols][NKL];
     uint4 vr[NVL];
@@ -272,13 +292,17 @@ void decode_partial_kernel(DecodeArgs a) {
       for (int ct = 0; ct < kCols; ++ct)
 #pragma unroll
         for (int c = 0; c < NKL; ++c)
-          kr[ct][c] = *(const uint4*)(kb + (ct * 16 + n16) * ROWB + c * 64 + r16 * 16);
+          kr[ct][c] = *(const uint4*)(kb + tok(ct) * ROWB + c * 64 + r16 * 16);
     };
+    // VALU: chunk rr holds token rr * RPI + lane / LPR, bytes (lane % LPR) * 16..
+    // MPV: chunk j holds token 8 * r16 + j, dimensions 8 * n16 .. 8 * n16 + 7.
+    // Either way each load instruction reads whole token rows.
     auto issue_v = [&](int64_t row0) {
       const char* vb = vbase + row0 * EB;
 #pragma unroll
       for (int rr = 0; rr < NVL; ++rr)
-        vr[rr] = *(const uint4*)(vb + (rr * RPI + lane / LPR) * ROWB + (lane % LPR) * 16);
+        vr[rr] = MPV ? *(const uint4*)(vb + (8 * r16 + rr) * ROWB + n16 * 16)
+                     : *(const uint4*)(vb + (rr * RPI + lane / LPR) * ROWB + (lane % LPR) * 16);
     };
 
     // S = Q K^T for the tile's two 16-token columns.
@@ -313,7 +337,7 @@ void decode_partial_kernel(DecodeArgs a) {
         float mx = kNegInf;
 #pragma unroll
         for (int ct = 0; ct < kCols; ++ct) {
-          x[ct][i] = (ct * 16 + n16 < tv) ? sc[ct][i] * sl : kNegInf;
+          x[ct][i] = (tok(ct) < tv) ? sc[ct][i] * sl : kNegInf;
           mx = fmaxf(mx, x[ct][i]);
         }
         mx = row_max16(mx);
@@ -330,18 +354,38 @@ void decode_partial_kernel(DecodeArgs a) {
         l_run[i] = l_run[i] * alpha[i] + ps;
         m_run[i] = mn;
       }
-      // Every lane writes (rows of heads >= G are never read): no branch.
+      if constexpr (MPV) {
+        // p = hi + lo, both bf16 (lo = bf16(p - hi), p - hi exact in fp32):
+        // 16 significant bits, so the bf16 products stay within 2^-16 of p v.
+        // LDS as [part][head][token] bf16; the lane's two tokens are adjacent.
+        uint32_t* pb = (uint32_t*)pw;
 #pragma unroll
-      for (int ct = 0; ct < kCols; ++ct)
-        *(float4*)(pw + (ct * 16 + n16) * 16 + r16 * 4) =
-            make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
-      // Rescale acc (alpha is exactly 1 for a head whose max did not move).
-      // Unconditional: a branch here splits acc's live range into copies.
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t hi = pack_bf16_rne(x[0][i], x[1][i]);
+          const float r0 = x[0][i] - bf16_lo(hi), r1 = x[1][i] - bf16_hi(hi);
+          const int at = (4 * r16 + i) * (kTile / 2) + n16;
+          pb[at] = hi;
+          pb[16 * (kTile / 2) + at] = pack_bf16_rne(r0, r1);
+        }
+        // Rescale (row 4 r16 + i of every accumulator is head 4 r16 + i).
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
+        for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] *= ah;
+          for (int i = 0; i < 4; ++i) oacc[e][i] *= alpha[i];
+      } else {
+        // Every lane writes (rows of heads >= G are never read): no branch.
+#pragma unroll
+        for (int ct = 0; ct < kCols; ++ct)
+          *(float4*)(pw + (ct * 16 + n16) * 16 + r16 * 4) =
+              make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+        // Rescale acc (alpha is exactly 1 for a head whose max did not move).
+        // Unconditional: a branch here splits acc's live range into copies.
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[h][e] *= ah;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -359,33 +403,83 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) pr[h] = all[h];
     };
-    auto pv = [&](int tv) {
-      float pn[G];
-      read_p(0, pn);
+    // MPV: O += P V as v_mfma_f32_16x16x32_bf16 with k = the tile's 32 tokens
+    // (lane (r16, n16) holds k = 8 r16 .. 8 r16 + 7): A = P (row = head n16,
+    // read from LDS, hi and lo parts), B for dimension step e = V[k][8 n16 + e]
+    // (the e-th bf16 of the lane's 8 V chunks, packed in pairs).  Output
+    // column n16 of step e is dimension 8 n16 + e.  V rows past the length
+    // are zeroed (they may hold anything, even NaN).
+    auto pv_mfma = [&](int tv) {
+      const uint32_t* pb = (const uint32_t*)pw;
+      const uint4 ah = *(const uint4*)(pb + n16 * (kTile / 2) + 4 * r16);
+      const uint4 al = *(const uint4*)(pb + 16 * (kTile / 2) + n16 * (kTile / 2) + 4 * r16);
+      uint4 vv[8];
 #pragma unroll
-      for (int rr = 0; rr < NVL; ++rr) {
-        float pc[G];
+      for (int j = 0; j < 8; ++j) vv[j] = vr[j];
+      if (tv < kTile) {  // uniform
 #pragma unroll
-        for (int h = 0; h < G; ++h) pc[h] = pn[h];
-        if (rr + 1 < NVL) read_p(rr + 1, pn);
-        const int trow = rr * RPI + lane / LPR;
-        // Rows past the length may hold anything (even NaN): zero them.
-        const bool live = trow < tv;
-        uint4 vv = vr[rr];
-        vv.x = live ? vv.x : 0u;
-        vv.y = live ? vv.y : 0u;
-        vv.z = live ? vv.z : 0u;
-        vv.w = live ? vv.w : 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float ve = chunk_elem<T>(vv, e);
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pc[h], ve, acc[h][e]);
+        for (int j = 0; j < 8; ++j) {
+          const bool live = 8 * r16 + j < tv;
+          vv[j].x = live ? vv[j].x : 0u;
+          vv[j].y = live ? vv[j].y : 0u;
+          vv[j].z = live ? vv[j].z : 0u;
+          vv[j].w = live ? vv[j].w : 0u;
         }
-        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // bf16 e of each chunk: the low (e even) or high (e odd) half of word e / 2
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint4& c0 = vv[2 * jj];
+          const uint4& c1 = vv[2 * jj + 1];
+          const int q = e >> 1;
+          const uint32_t a0 = q == 0 ? c0.x : q == 1 ? c0.y : q == 2 ? c0.z : c0.w;
+          const uint32_t a1 = q == 0 ? c1.x : q == 1 ? c1.y : q == 2 ? c1.z : c1.w;
+          w[jj] = __builtin_amdgcn_perm(a1, a0, sel);
+        }
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bv,
+                                                          oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bv,
+                                                          oacc[e], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
+    };
+    auto pv = [&](int tv) {
+      if constexpr (MPV) {
+        pv_mfma(tv);
+      } else {
+        float pn[G];
+        read_p(0, pn);
+#pragma unroll
+        for (int rr = 0; rr < NVL; ++rr) {
+          float pc[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) pc[h] = pn[h];
+          if (rr + 1 < NVL) read_p(rr + 1, pn);
+          const int trow = rr * RPI + lane / LPR;
+          // Rows past the length may hold anything (even NaN): zero them.
+          const bool live = trow < tv;
+          uint4 vv = vr[rr];
+          vv.x = live ? vv.x : 0u;
+          vv.y = live ? vv.y : 0u;
+          vv.z = live ? vv.z : 0u;
+          vv.w = live ? vv.w : 0u;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float ve = chunk_elem<T>(vv, e);
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pc[h], ve, acc[h][e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
     };
 
     // ---- tiles: K and V each re-issued as soon as their registers are consumed.
@@ -422,26 +516,40 @@ void decode_partial_kernel(DecodeArgs a) {
     float lt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lt[i] = row_sum16(l_run[i]);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        // the lanes holding the same V columns: i, i ^ 8 (8 lanes per row),
-        // then the other rows (VALU swaps, no LDS round trip)
-        float x = acc[h][e];
-        if constexpr (LPR == 8) x = x + dpp_f32<kDppRowRor8>(x);
-        if constexpr (LPR <= 16) x = cross_row_sum_f32(x);
-        else x = cross_half_sum_f32(x);
-        acc[h][e] = x;
-      }
     float* rec = a.part + (int64_t)(u + w) * REC;
-    if (lane < LPR) {
+    if constexpr (MPV) {
+      // lane (r16, n16): heads 4 r16 + i, dimensions 8 n16 .. 8 n16 + 7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * r16 + i;
+        if (h < G) {
+          float* o = rec + h * D + 8 * n16;
+          *(float4*)o = make_float4(oacc[0][i], oacc[1][i], oacc[2][i], oacc[3][i]);
+          *(float4*)(o + 4) = make_float4(oacc[4][i], oacc[5][i], oacc[6][i], oacc[7][i]);
+        }
+      }
+    }
+    if constexpr (!MPV) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-          *(float4*)(rec + h * D + lane * E + e) =
-              make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+        for (int e = 0; e < E; ++e) {
+          // the lanes holding the same V columns: i, i ^ 8 (8 lanes per row),
+          // then the other rows (VALU swaps, no LDS round trip)
+          float x = acc[h][e];
+          if constexpr (LPR == 8) x = x + dpp_f32<kDppRowRor8>(x);
+          if constexpr (LPR <= 16) x = cross_row_sum_f32(x);
+          else x = cross_half_sum_f32(x);
+          acc[h][e] = x;
+        }
+      if (lane < LPR) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < E; e += 4)
+            *(float4*)(rec + h * D + lane * E + e) =
+                make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+      }
     }
     if (n16 == 0) {
 #pragma unroll
