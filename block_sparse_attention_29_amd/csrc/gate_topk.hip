@@ -353,9 +353,6 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreChunk = 256;  // blocks per workgroup of the score kernel
 constexpr int kSelectThreads = 256;
 
-// Scores of blocks j0 .. j0 + 255 of unit u (n blocks in its sequence) by a
-// 256-thread workgroup; emit(j, score) is called once for every j < n of the
-// chunk, by thread j - j0.  s_q: [D], s_part: [4][256] doubles of LDS.
 // The append of tokens lens_old[b] .. lens[b] - 1 to the blocks of one score
 // chunk [j0, j0 + 256), with pool_append_kernel's arithmetic: thread i < D
 // owns dimension i; the open block continues its fp64 sum from open_sum, a
@@ -375,7 +372,9 @@ constexpr int kStash = 4;
 template <typename T, int D>
 struct ChunkAppend {
   int lo, hi, jlo, jhi, ja, jb;  // the append's tokens and blocks, the chunk's touched range
-  double os0, x0;                // thread i: open sum and first key of block ja, dim i
+  double os0;                    // thread i: open sum of block ja, dim i
+  T xr;                          // and its first appended key, dim i (raw)
+  bool xok;                      // that key has a page
 
   __device__ __forceinline__ int64_t row_of(const GateArgs& a, int b, int g, int t) const {
     const int S = a.S, j = t / S, pos = t - j * S;
@@ -391,23 +390,27 @@ struct ChunkAppend {
                                         int lens_old) {
     const int S = a.S;
     const int64_t cap = (int64_t)a.NB * S;
+    const int tid = threadIdx.x;
     lo = lens_old;
     hi = a.lens[b];
     if (hi > cap) hi = (int)cap;
-    ja = 0;
-    jb = -1;
-    if (lo < 0 || lo >= hi) return;
-    jlo = lo / S;
-    jhi = (hi - 1) / S;
-    ja = max(jlo, j0);
-    jb = min(min(jhi, j0 + kScoreChunk - 1), n - 1);
-    const int tid = threadIdx.x;
-    if (ja > jb || tid >= D) return;
+    const bool any = lo >= 0 && lo < hi;  // (uniform)
+    jlo = any ? lo / S : 0;
+    jhi = any ? (hi - 1) / S : -1;
+    ja = any ? max(jlo, j0) : 0;
+    jb = any ? min(min(jhi, j0 + kScoreChunk - 1), n - 1) : -1;
+    const bool act = ja <= jb;
     const int t0 = ja * S > lo ? ja * S : lo;
-    os0 = (ja == jlo && lo % S != 0) ? a.open_sum[(int64_t)u * D + tid] : 0.0;
-    const int64_t r = row_of(a, b, g, t0);
-    x0 = r < 0 ? __builtin_nan("") : load_as_double<T>((const T*)a.k, r + tid);
+    // the open sum only where the chunk continues the open block (uniform)
+    os0 = (act && ja == jlo && lo % S != 0 && tid < D) ? a.open_sum[(int64_t)u * D + tid] : 0.0;
+    // The first appended key of block ja: loaded outside any branch and left
+    // unconverted, so nothing waits on it before apply() (an inactive chunk
+    // or a block without a page reads row 0 instead: in bounds, unused).
+    const int64_t r = act ? row_of(a, b, g, t0) : -1;
+    xok = r >= 0;
+    xr = ((const T*)a.k)[(xok ? r : 0) + (tid < D ? tid : 0)];
   }
+
 
   __device__ __forceinline__ void apply(const GateArgs& a, int u, int b, int g,
                                         float (*s_new)[D]) {
@@ -428,7 +431,8 @@ struct ChunkAppend {
       const int t1 = j * S + S < hi ? j * S + S : hi;
       double acc;
       if (j == ja) {  // the prefetched open sum and first token
-        acc = __builtin_isnan(x0) ? os0 : (t0 == j * S ? x0 : os0 + x0);
+        const double x0 = load_as_double<T>(&xr, 0);
+        acc = !xok ? os0 : (t0 == j * S ? x0 : os0 + x0);
         block_sum(j, t0 + 1, t1, acc);
       } else {
         acc = 0.0;
@@ -470,22 +474,29 @@ struct ChunkAppend {
   }
 };
 
-template <typename T, int D, bool VEC4, bool APPEND = false, typename Emit>
-__device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int g, int n, int j0,
-                                            double* s_q, double (*s_part)[kScoreChunk],
+// Scores of blocks j0 .. j0 + 255 of unit u by a 256-thread workgroup;
+// n_of() gives the blocks of its sequence (called once the pooled loads are
+// out), and emit(j, score) is called once for every j < n of the chunk, by
+// thread j - j0.  Returns at once, for the whole workgroup, when j0 >= n.
+// s_q: [D], s_part: [4][256] doubles of LDS.
+template <typename T, int D, bool VEC4, bool APPEND = false, typename NOf, typename Emit>
+__device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int g, NOf n_of,
+                                            int j0, double* s_q, double (*s_part)[kScoreChunk],
                                             Emit emit, int lens_old = 0) {
   constexpr int DQ = D / 4;
   const int tid = threadIdx.x, qd = tid >> 6, lane = tid & 63;
   const int NB = a.NB;
   const int G = a.Hq / a.Hkv;
 
-  // ---- pooled loads first (block ids clamped into [0, n), always in bounds) ----
+  // ---- pooled loads first, before the length is known: block ids clamped
+  // into the table's [0, NB), always in bounds; blocks at or past n are
+  // scored from whatever the table holds there and never emitted ----
   const float* pu = a.pooled + ((int64_t)u * D + (int64_t)qd * DQ) * NB;
   auto blk = [&](int e) { return VEC4 ? j0 + 4 * lane + e : j0 + lane + 64 * e; };
   float pv[DQ][4];
   if constexpr (VEC4) {
     // an aligned group of 4 (NB % 4 == 0, so it stays inside the row)
-    const uint32_t jg = (uint32_t)min(j0 + 4 * lane, ((n - 1) >> 2) << 2);
+    const uint32_t jg = (uint32_t)min(j0 + 4 * lane, NB - 4);
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
       const float4 v = *(const float4*)(pu + (uint32_t)(i * NB) + jg);
@@ -495,8 +506,10 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
 #pragma unroll
     for (int i = 0; i < DQ; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), n - 1))];
+      for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), NB - 1))];
   }
+  const int n = n_of();  // the sequence's blocks: the length's round trip overlaps the loads
+  if (j0 >= n) return;   // the whole workgroup: nothing of this chunk is in the sequence
   ChunkAppend<T, D> ap;
   __shared__ float s_new[APPEND ? kStash : 1][D];
   if constexpr (APPEND) ap.issue(a, u, b, g, n, j0, lens_old);
@@ -545,13 +558,10 @@ __global__ __launch_bounds__(kScoreThreads) void gate_score_kernel(GateArgs a) {
   const int u = (int)blockIdx.x / nchunk, c = (int)blockIdx.x - u * nchunk;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
-  const int n = seq_blocks(a.lens[b], a.S, a.NB);
-  const int j0 = c * kScoreChunk;
-  if (j0 >= n) return;  // the whole workgroup: nothing of this chunk is in the sequence
   double* out = a.scores + (int64_t)u * a.NB;
-  score_chunk<T, D, VEC4, APPEND>(a, u, b, g, n, j0, s_q, s_part,
-                                  [&](int j, double sc) { out[j] = key_score(order_key(sc)); },
-                                  lens_old);
+  score_chunk<T, D, VEC4, APPEND>(
+      a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, c * kScoreChunk, s_q, s_part,
+      [&](int j, double sc) { out[j] = key_score(order_key(sc)); }, lens_old);
 }
 
 // Tables of at most 256 blocks: one workgroup per unit scores its chunk into
@@ -565,13 +575,11 @@ __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   __shared__ int s_scan[kScoreThreads / 64 + 1];
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
+  score_chunk<T, D, VEC4, APPEND>(
+      a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, 0, s_q, s_part,
+      [&](int j, double sc) { s_key[j] = order_key(sc); }, lens_old);
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
-  if (n > 0) {
-    score_chunk<T, D, VEC4, APPEND>(a, u, b, g, n, 0, s_q, s_part,
-                                    [&](int j, double sc) { s_key[j] = order_key(sc); },
-                                    lens_old);
-    __syncthreads();
-  }
+  __syncthreads();
   gate_finish<kScoreThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }
 
