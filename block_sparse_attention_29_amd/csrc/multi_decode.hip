@@ -68,6 +68,10 @@ void decode_multi_kernel(DecodeArgs a) {
   using GE = MGeo<T, D>;
   constexpr int EB = GE::EB, ROWB = GE::ROWB, NKL = GE::NKL, VB = GE::VB, DPL = GE::DPL;
   constexpr int NVQ = GE::NVQ, REC = GE::REC;
+  // bf16 caches with d = 128 multiply P V on bf16 matrix cores (MPV, as the
+  // single-token kernel does); other caches on fp32 matrix cores.
+  constexpr bool MPV = EB == 2 && D == 128;
+  static_assert(!MPV || (NVQ == 1 && DPL == 8), "MPV: one 16-byte V chunk per lane and row");
 
   __shared__ __align__(16) float s_p[kWavesPerWG][kTile * kRows];
   extern __shared__ int s_dyn[];
@@ -279,21 +283,24 @@ void decode_multi_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Token of MFMA column n16 in 16-token column ct (any assignment gives the
+    // same logits; MPV pairs each lane's two tokens for whole-word LDS writes).
+    auto tok = [&](int ct) { return MPV ? 2 * n16 + ct : ct * 16 + n16; };
     uint4 kr[kCols][NKL];
-    uint4 vr[8][NVQ];  // token 4k + r16 of the tile, bytes n16 * VB ..
+    uint4 vr[8][NVQ];  // token 4k + r16 (MPV: 8 r16 + k) of the tile, bytes n16 * VB ..
     auto issue_k = [&](int64_t row0) {
       const char* kb = kbase + row0 * EB;
 #pragma unroll
       for (int ct = 0; ct < kCols; ++ct)
 #pragma unroll
         for (int c = 0; c < NKL; ++c)
-          kr[ct][c] = *(const uint4*)(kb + (ct * 16 + n16) * ROWB + c * 64 + r16 * 16);
+          kr[ct][c] = *(const uint4*)(kb + tok(ct) * ROWB + c * 64 + r16 * 16);
     };
     auto issue_v = [&](int64_t row0) {
       const char* vb = vbase + row0 * EB;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const char* src = vb + (4 * k + r16) * ROWB + n16 * VB;
+        const char* src = vb + (MPV ? 8 * r16 + k : 4 * k + r16) * ROWB + n16 * VB;
         if constexpr (VB == 8) {
           const uint2 h = *(const uint2*)src;
           vr[k][0] = make_uint4(h.x, h.y, 0u, 0u);
@@ -327,7 +334,8 @@ void decode_multi_kernel(DecodeArgs a) {
     };
 
     // Online softmax of the lane's rows 4 r16 + i over the tile's tokens
-    // ct*16 + n16; p (fp32) to LDS as [token][row]; acc rows rescaled.
+    // tok(ct); p to LDS (fp32 as [token][row], or split in bf16 parts for
+    // MPV); acc rows rescaled.
     auto softmax = [&](const f32x4 (&sc)[kCols], int tv, int tp0) {
       float x[kCols][4];
 #pragma unroll
@@ -336,7 +344,7 @@ void decode_multi_kernel(DecodeArgs a) {
         float mx = kNegInf;
 #pragma unroll
         for (int ct = 0; ct < kCols; ++ct) {
-          x[ct][i] = (ct * 16 + n16 < tvr) ? sc[ct][i] * sl : kNegInf;
+          x[ct][i] = (tok(ct) < tvr) ? sc[ct][i] * sl : kNegInf;
           mx = fmaxf(mx, x[ct][i]);
         }
         mx = row_max16(mx);
@@ -355,19 +363,33 @@ void decode_multi_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e][i] *= alpha;
       }
+      if constexpr (MPV) {
+        store_p_split((uint32_t*)pw, x, r16, n16);
+      } else {
 #pragma unroll
-      for (int ct = 0; ct < kCols; ++ct)
-        *(float4*)(pw + (ct * 16 + n16) * kRows + r16 * 4) =
-            make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+        for (int ct = 0; ct < kCols; ++ct)
+          *(float4*)(pw + (ct * 16 + n16) * kRows + r16 * 4) =
+              make_float4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // O += P V on fp32 MFMA: k-step k takes tokens 4k .. 4k + 3 (lane row
-    // group r16 = token 4k + r16); V rows past the length are zeroed (they may
-    // hold anything, even NaN).
+    // O += P V: MPV on bf16 matrix cores (pv_bf16; acc[e] is its oacc[e]);
+    // else on fp32 MFMA, k-step k taking tokens 4k .. 4k + 3 (lane row group
+    // r16 = token 4k + r16).  V rows past the length are zeroed (they may hold
+    // anything, even NaN).
     auto pv = [&](int tv) {
+      if constexpr (MPV) {
+        uint4 v8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v8[k] = vr[k][0];
+        pv_bf16((const uint32_t*)pw, v8, tv, acc, r16, n16);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        return;
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float ap = pw[(4 * k + r16) * kRows + n16];

@@ -355,18 +355,7 @@ void decode_partial_kernel(DecodeArgs a) {
         m_run[i] = mn;
       }
       if constexpr (MPV) {
-        // p = hi + lo, both bf16 (lo = bf16(p - hi), p - hi exact in fp32):
-        // 16 significant bits, so the bf16 products stay within 2^-16 of p v.
-        // LDS as [part][head][token] bf16; the lane's two tokens are adjacent.
-        uint32_t* pb = (uint32_t*)pw;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t hi = pack_bf16_rne(x[0][i], x[1][i]);
-          const float r0 = x[0][i] - bf16_lo(hi), r1 = x[1][i] - bf16_hi(hi);
-          const int at = (4 * r16 + i) * (kTile / 2) + n16;
-          pb[at] = hi;
-          pb[16 * (kTile / 2) + at] = pack_bf16_rne(r0, r1);
-        }
+        store_p_split((uint32_t*)pw, x, r16, n16);
         // Rescale (row 4 r16 + i of every accumulator is head 4 r16 + i).
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -403,55 +392,11 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) pr[h] = all[h];
     };
-    // MPV: O += P V as v_mfma_f32_16x16x32_bf16 with k = the tile's 32 tokens
-    // (lane (r16, n16) holds k = 8 r16 .. 8 r16 + 7): A = P (row = head n16,
-    // read from LDS, hi and lo parts), B for dimension step e = V[k][8 n16 + e]
-    // (the e-th bf16 of the lane's 8 V chunks, packed in pairs).  Output
-    // column n16 of step e is dimension 8 n16 + e.  V rows past the length
-    // are zeroed (they may hold anything, even NaN).
-    auto pv_mfma = [&](int tv) {
-      const uint32_t* pb = (const uint32_t*)pw;
-      const uint4 ah = *(const uint4*)(pb + n16 * (kTile / 2) + 4 * r16);
-      const uint4 al = *(const uint4*)(pb + 16 * (kTile / 2) + n16 * (kTile / 2) + 4 * r16);
-      uint4 vv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vv[j] = vr[j];
-      if (tv < kTile) {  // uniform
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool live = 8 * r16 + j < tv;
-          vv[j].x = live ? vv[j].x : 0u;
-          vv[j].y = live ? vv[j].y : 0u;
-          vv[j].z = live ? vv[j].z : 0u;
-          vv[j].w = live ? vv[j].w : 0u;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // bf16 e of each chunk: the low (e even) or high (e odd) half of word e / 2
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t w[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint4& c0 = vv[2 * jj];
-          const uint4& c1 = vv[2 * jj + 1];
-          const int q = e >> 1;
-          const uint32_t a0 = q == 0 ? c0.x : q == 1 ? c0.y : q == 2 ? c0.z : c0.w;
-          const uint32_t a1 = q == 0 ? c1.x : q == 1 ? c1.y : q == 2 ? c1.z : c1.w;
-          w[jj] = __builtin_amdgcn_perm(a1, a0, sel);
-        }
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bv,
-                                                          oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bv,
-                                                          oacc[e], 0, 0, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    };
     auto pv = [&](int tv) {
       if constexpr (MPV) {
-        pv_mfma(tv);
+        pv_bf16((const uint32_t*)pw, vr, tv, oacc, r16, n16);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
       } else {
         float pn[G];
         read_p(0, pn);
