@@ -43,6 +43,7 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE, calibrated on a plain copy), valid only for the kernel sources
 # whose digest the file records.
 KERNEL_SOURCES = ["block_sparse_attention_29_amd/csrc/sparse_decode.hip",
+                  "block_sparse_attention_29_amd/csrc/multi_decode.hip",
                   "block_sparse_attention_29_amd/csrc/decode_common.h",
                   "block_sparse_attention_29_amd/csrc/gate_phase.h",
                   "block_sparse_attention_29_amd/csrc/seer_device.h",
