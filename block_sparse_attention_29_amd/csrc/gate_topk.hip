@@ -475,11 +475,15 @@ struct ChunkAppend {
 };
 
 // Scores of blocks j0 .. j0 + 255 of unit u by a 256-thread workgroup;
-// n_of() gives the blocks of its sequence (called once the pooled loads are
-// out), and emit(j, score) is called once for every j < n of the chunk, by
-// thread j - j0.  Returns at once, for the whole workgroup, when j0 >= n.
-// s_q: [D], s_part: [4][256] doubles of LDS.
-template <typename T, int D, bool VEC4, bool APPEND = false, typename NOf, typename Emit>
+// n_of() gives the blocks of its sequence, and emit(j, score) is called once
+// for every j < n of the chunk, by thread j - j0.  Returns at once, for the
+// whole workgroup, when j0 >= n.  EARLY: the pooled loads go out before the
+// length is known, block ids clamped into the table's row (for chunks of long
+// tables, which the sequence mostly fills); otherwise after it, clamped into
+// the sequence's blocks (for one-chunk tables of varied lengths, where the
+// row's unused tail would otherwise be read).  s_q: [D], s_part: [4][256]
+// doubles of LDS.
+template <typename T, int D, bool VEC4, bool APPEND, bool EARLY, typename NOf, typename Emit>
 __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int g, NOf n_of,
                                             int j0, double* s_q, double (*s_part)[kScoreChunk],
                                             Emit emit, int lens_old = 0) {
@@ -488,15 +492,22 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
   const int NB = a.NB;
   const int G = a.Hq / a.Hkv;
 
-  // ---- pooled loads first, before the length is known: block ids clamped
-  // into the table's [0, NB), always in bounds; blocks at or past n are
-  // scored from whatever the table holds there and never emitted ----
+  // ---- pooled loads first (EARLY: before the length is known).  Block ids
+  // are clamped into [0, lim) -- the table's row (EARLY) or the sequence's
+  // blocks -- so every load is in bounds; blocks at or past n are scored from
+  // whatever the table holds there and never emitted ----
+  int n = 0;
+  if constexpr (!EARLY) {
+    n = n_of();
+    if (j0 >= n) return;  // the whole workgroup: nothing of this chunk is in the sequence
+  }
+  const int lim = EARLY ? NB : n;
   const float* pu = a.pooled + ((int64_t)u * D + (int64_t)qd * DQ) * NB;
   auto blk = [&](int e) { return VEC4 ? j0 + 4 * lane + e : j0 + lane + 64 * e; };
   float pv[DQ][4];
   if constexpr (VEC4) {
     // an aligned group of 4 (NB % 4 == 0, so it stays inside the row)
-    const uint32_t jg = (uint32_t)min(j0 + 4 * lane, NB - 4);
+    const uint32_t jg = (uint32_t)min(j0 + 4 * lane, ((lim - 1) >> 2) << 2);
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
       const float4 v = *(const float4*)(pu + (uint32_t)(i * NB) + jg);
@@ -506,10 +517,12 @@ __device__ __forceinline__ void score_chunk(const GateArgs& a, int u, int b, int
 #pragma unroll
     for (int i = 0; i < DQ; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), NB - 1))];
+      for (int e = 0; e < 4; ++e) pv[i][e] = pu[(uint32_t)(i * NB + min(blk(e), lim - 1))];
   }
-  const int n = n_of();  // the sequence's blocks: the length's round trip overlaps the loads
-  if (j0 >= n) return;   // the whole workgroup: nothing of this chunk is in the sequence
+  if constexpr (EARLY) {
+    n = n_of();           // the length's round trip overlaps the loads
+    if (j0 >= n) return;  // the whole workgroup: nothing of this chunk is in the sequence
+  }
   ChunkAppend<T, D> ap;
   __shared__ float s_new[APPEND ? kStash : 1][D];
   if constexpr (APPEND) ap.issue(a, u, b, g, n, j0, lens_old);
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(kScoreThreads) void gate_score_kernel(GateArgs a) {
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
   double* out = a.scores + (int64_t)u * a.NB;
-  score_chunk<T, D, VEC4, APPEND>(
+  score_chunk<T, D, VEC4, APPEND, true>(
       a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, c * kScoreChunk, s_q, s_part,
       [&](int j, double sc) { out[j] = key_score(order_key(sc)); }, lens_old);
 }
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   __shared__ int s_scan[kScoreThreads / 64 + 1];
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
-  score_chunk<T, D, VEC4, APPEND>(
+  score_chunk<T, D, VEC4, APPEND, false>(
       a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, 0, s_q, s_part,
       [&](int j, double sc) { s_key[j] = order_key(sc); }, lens_old);
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
