@@ -119,12 +119,14 @@ __device__ __forceinline__ void load_pooled_vec(const float* p, float (&x)[VEC])
 template <typename T, int D, int QR, bool MULTI, int VEC, bool PRE>
 __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, const float* pu,
                                              int n, double* s_q, double* s_part,
-                                             uint64_t* s_key, const GatePreload<T, D, QR>& pre,
-                                             bool use_pre) {
+                                             uint64_t* s_key, int* s_hist,
+                                             const GatePreload<T, D, QR>& pre, bool use_pre) {
   constexpr int DQ = D / 4, PASS = 64 * VEC;
   const int NB = a.NB;
   const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
   const double inv = 1.0 / sqrt((double)D);
+  // the AND and OR of the keys this thread writes, for the selection
+  uint64_t kand = ~0ull, kor = 0;
   // One pass over blocks j0 .. j0 + PASS - 1; the first (FIRST) also sums the
   // query and may take the entry loads (peeled, so that they are dead after).
   auto pass = [&](int j0, auto first_tag) {
@@ -180,9 +182,15 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
       if (j < n) {
         const double sc = ((s_part[t] + s_part[PASS + t]) + s_part[2 * PASS + t]) +
                           s_part[3 * PASS + t];
-        s_key[j] = order_key(sc * inv);
+        const uint64_t key = order_key(sc * inv);
+        s_key[j] = key;
+        kand &= key;
+        kor |= key;
       }
     }
+    // the last pass hands the keys' AND and OR to the selection (behind this
+    // barrier; topk_keys_collect reads them)
+    if (j0 + PASS >= n) topk_keys_publish<kThreads>(kand, kor, s_hist);
     __syncthreads();
   };
   pass(0, BoolTag<true>{});  // n >= 1
@@ -205,11 +213,14 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   const float* pu = a.pooled + (int64_t)u * D * NB;
   const bool use_pre = u == pre.u;  // the entry loads are this unit's (uniform)
   if (NB % 4 == 0)
-    fused_scores<T, D, QR, MULTI, 4, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
+    fused_scores<T, D, QR, MULTI, 4, PRE>(a, b, g, pu, n, s_q, s_part, s_key, s_hist, pre,
+                                            use_pre);
   else if (NB % 2 == 0)
-    fused_scores<T, D, QR, MULTI, 2, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
+    fused_scores<T, D, QR, MULTI, 2, PRE>(a, b, g, pu, n, s_q, s_part, s_key, s_hist, pre,
+                                            use_pre);
   else
-    fused_scores<T, D, QR, MULTI, 1, PRE>(a, b, g, pu, n, s_q, s_part, s_key, pre, use_pre);
+    fused_scores<T, D, QR, MULTI, 1, PRE>(a, b, g, pu, n, s_q, s_part, s_key, s_hist, pre,
+                                            use_pre);
   // forced blocks rank above every score while the selection runs
   const bool forced = a.force_first || a.force_last;  // uniform
   uint64_t key_first = 0, key_last = 0;
@@ -225,6 +236,10 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   }
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
+  } else if (!forced) {  // the keys' AND and OR came with the scores
+    uint64_t kand, kor;
+    topk_keys_collect<kThreads>(s_hist, kand, kor);
+    block_topk_ids_from<kThreads>(s_key, n, k, kand, kor, s_hist, s_scan, dst);
   } else {
     block_topk_ids<kThreads>(s_key, n, k, s_hist, s_scan, dst);
   }

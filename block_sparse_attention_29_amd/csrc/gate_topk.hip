@@ -156,7 +156,10 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
 // above the threshold's key; then block_topk_ids (an exact radix select by the
 // whole workgroup); the ids go to the rows of KV heads g_lo .. g_hi - 1 (from
 // LDS when UNIFIED), the scores written out are the blocks' own.
-template <int NT, bool UNIFIED, bool SCORES = true>
+// ANDOR: the keys' AND and OR were published (topk_keys_publish) before the
+// barrier that preceded the call; the selection takes them from there unless
+// forced blocks change the keys.
+template <int NT, bool UNIFIED, bool SCORES = true, bool ANDOR = false>
 __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, int g_hi, int n,
                                             uint64_t* s_key, int32_t* s_ids, int* s_hist,
                                             int* s_scan) {
@@ -197,6 +200,10 @@ __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, 
     // one wave selects: with 16 waves a workgroup barrier costs more than the
     // one wave's extra work (with 4 waves the workgroup select is faster)
     if (tid < kWave) wave_topk_ids(s_key, n, k, s_hist, dst);
+  } else if (ANDOR && nf == 0) {
+    uint64_t kand, kor;
+    topk_keys_collect<NT>(s_hist, kand, kor);
+    block_topk_ids_from<NT>(s_key, n, k, kand, kor, s_hist, s_scan, dst);
   } else {
     block_topk_ids<NT>(s_key, n, k, s_hist, s_scan, dst);
   }
@@ -588,12 +595,20 @@ __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   __shared__ int s_scan[kScoreThreads / 64 + 1];
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
+  uint64_t kand = ~0ull, kor = 0;  // of the keys this thread writes
   score_chunk<T, D, VEC4, APPEND, false>(
       a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, 0, s_q, s_part,
-      [&](int j, double sc) { s_key[j] = order_key(sc); }, lens_old);
+      [&](int j, double sc) {
+        const uint64_t key = order_key(sc);
+        s_key[j] = key;
+        kand &= key;
+        kor |= key;
+      },
+      lens_old);
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  topk_keys_publish<kScoreThreads>(kand, kor, s_hist);
   __syncthreads();
-  gate_finish<kScoreThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+  gate_finish<kScoreThreads, false, true, true>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }
 
 __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a) {
@@ -610,18 +625,26 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = sc[min(tid + e * NT, a.NB - 1)];
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  uint64_t kand = ~0ull, kor = 0;  // of the keys this thread writes
+  auto put = [&](int j, double v) {
+    const uint64_t key = order_key(v);
+    s_key[j] = key;
+    kand &= key;
+    kor |= key;
+  };
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    if (tid + e * NT < n) s_key[tid + e * NT] = order_key(x[e]);
+    if (tid + e * NT < n) put(tid + e * NT, x[e]);
   for (int j0 = tid + 8 * NT; j0 < n; j0 += 8 * NT) {  // longer tables: eight at a time
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = sc[min(j0 + e * NT, n - 1)];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (j0 + e * NT < n) s_key[j0 + e * NT] = order_key(x[e]);
+      if (j0 + e * NT < n) put(j0 + e * NT, x[e]);
   }
+  topk_keys_publish<NT>(kand, kor, s_hist);
   __syncthreads();
-  gate_finish<NT, false, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+  gate_finish<NT, false, false, true>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }
 
 // ---------------------------------------------------------------- learned gate

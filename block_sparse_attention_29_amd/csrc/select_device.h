@@ -67,38 +67,18 @@ __device__ __forceinline__ int kept_count_forced(int n, const int32_t* top_k, in
 // Key that ranks a forced block above every score.
 constexpr uint64_t kForcedKey = ~0ull;
 
-// Writes the ids of the k largest keys of s_key[0..n) (ties to the lower id),
-// ascending, to out[0..k).  Requires 0 < k < n and NT >= 256; every thread of
-// the workgroup calls it (it contains __syncthreads()).  Scratch in LDS:
-// s_hist [3 * 256], s_scan [NT / 64 + 1].
-//
-// Exact radix select over the 64-bit keys.  Thread t owns the contiguous ids
-// [t*m, t*m + m).  A block-wide AND and OR of the keys give the bits every key
-// shares; the first digit is the 8 bits from the highest bit where keys
-// differ, each later digit the next 8 bits down.  Each pass histograms the
-// digit of the keys still matching the chosen prefix, and every wave scans
-// the 256 bins from the top (DPP) to find the digit that holds the krem-th
-// largest key, so one barrier per pass suffices: the histograms rotate over
-// three buffers, the one cleared during a pass last read two passes before.
-// Once every remaining candidate is needed (or all bits are used) the kept set
-// is every key with a larger prefix plus the first krem keys equal to it in id
-// order.  One block scan of packed (above, equal) counts then gives every
-// thread the output slots of its ids.
+// The block-wide AND and OR of the order keys, which give the bits every key
+// shares (the radix select starts below them).  Each thread folds the keys it
+// holds into (kand, kor); topk_keys_publish, called by every thread before a
+// workgroup barrier, reduces them per wave (DPP within rows, lane reads across
+// them) into s_hist[512 .. 512 + 4 NT/64) and clears the first histogram
+// s_hist[0 .. 256); after the barrier topk_keys_collect gives every thread the
+// block's values.  A caller that writes the keys can fold them as it writes
+// and publish before the barrier that follows the writes, saving the select a
+// pass over the keys and a barrier.
 template <int NT>
-__device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int* s_scan,
-                               int32_t* out) {
-  constexpr int NW = NT / 64;
+__device__ __forceinline__ void topk_keys_publish(uint64_t kand, uint64_t kor, int* s_hist) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int m = (n + NT - 1) / NT;
-  const int lo = min(n, tid * m), hi = min(n, lo + m);
-
-  // ---- bits shared by every key: block AND / OR (partials in buffer 2) ----
-  uint64_t kand = ~0ull, kor = 0;
-  for (int j = lo; j < hi; ++j) {
-    const uint64_t key = s_key[j];
-    kand &= key;
-    kor |= key;
-  }
   uint32_t r4[4] = {(uint32_t)kand, (uint32_t)(kand >> 32), (uint32_t)kor, (uint32_t)(kor >> 32)};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -121,7 +101,13 @@ __device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist,
   if (lane < 4)
     s_red[wv * 4 + lane] = (int)(lane == 0 ? r4[0] : lane == 1 ? r4[1] : lane == 2 ? r4[2] : r4[3]);
   if (tid < 256) s_hist[tid] = 0;
-  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void topk_keys_collect(const int* s_hist, uint64_t& kand,
+                                                  uint64_t& kor) {
+  constexpr int NW = NT / 64;
+  const int* s_red = s_hist + 2 * 256;
   uint32_t t4[4] = {~0u, ~0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -132,6 +118,32 @@ __device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist,
   }
   kand = ((uint64_t)t4[1] << 32) | t4[0];
   kor = ((uint64_t)t4[3] << 32) | t4[2];
+}
+
+// Writes the ids of the k largest keys of s_key[0..n) (ties to the lower id),
+// ascending, to out[0..k), given the keys' block-wide AND and OR (see
+// topk_keys_publish, whose barrier must have passed: it also clears the
+// first histogram).  Requires 0 < k < n and NT >= 256; every thread of the
+// workgroup calls it (it contains __syncthreads()).  Scratch in LDS: s_hist
+// [3 * 256], s_scan [NT / 64 + 1].
+//
+// Exact radix select over the 64-bit keys.  Thread t owns the contiguous ids
+// [t*m, t*m + m).  The first digit is the 8 bits from the highest bit where
+// keys differ, each later digit the next 8 bits down.  Each pass histograms
+// the digit of the keys still matching the chosen prefix, and every wave
+// scans the 256 bins from the top (DPP) to find the digit that holds the
+// krem-th largest key, so one barrier per pass suffices: the histograms
+// rotate over three buffers, the one cleared during a pass last read two
+// passes before.  Once every remaining candidate is needed (or all bits are
+// used) the kept set is every key with a larger prefix plus the first krem
+// keys equal to it in id order.  One block scan of packed (above, equal)
+// counts then gives every thread the output slots of its ids.
+template <int NT>
+__device__ void block_topk_ids_from(const uint64_t* s_key, int n, int k, uint64_t kand,
+                                    uint64_t kor, int* s_hist, int* s_scan, int32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int m = (n + NT - 1) / NT;
+  const int lo = min(n, tid * m), hi = min(n, lo + m);
   const uint64_t diff = kand ^ kor;
 
   int top = diff ? 63 - __builtin_clzll(diff) : -1;  // highest bit where keys differ
@@ -197,6 +209,26 @@ __device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist,
       ++eb;
     }
   }
+}
+
+// block_topk_ids_from with the AND and OR taken here: a pass over the keys
+// and a barrier.  Same requirements and scratch.
+template <int NT>
+__device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int* s_scan,
+                               int32_t* out) {
+  const int tid = threadIdx.x;
+  const int m = (n + NT - 1) / NT;
+  const int lo = min(n, tid * m), hi = min(n, lo + m);
+  uint64_t kand = ~0ull, kor = 0;
+  for (int j = lo; j < hi; ++j) {
+    const uint64_t key = s_key[j];
+    kand &= key;
+    kor |= key;
+  }
+  topk_keys_publish<NT>(kand, kor, s_hist);
+  __syncthreads();
+  topk_keys_collect<NT>(s_hist, kand, kor);
+  block_topk_ids_from<NT>(s_key, n, k, kand, kor, s_hist, s_scan, out);
 }
 
 }  // namespace seer
