@@ -679,6 +679,11 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
 // wave's units, then over the 16 waves in order.  The next chunk's pooled
 // loads fly while a chunk is scored.  The selection rule and outputs are the
 // gate kernel's.
+//
+// SPLIT: with fewer units than CUs, S = gridDim.x / units workgroups share a
+// unit, workgroup s taking a contiguous range of its 64-block chunks (the
+// same arithmetic per block); the scores go to memory and gate_select_kernel
+// selects afterwards.
 
 constexpr int kLgThreads = 1024;  // 16 waves x 16 hidden units = 256
 constexpr int kLgChunk = 64;      // blocks cut into limbs and scored per pass
@@ -686,7 +691,7 @@ constexpr int kLgLimbs = 5;       // int8 limbs per key element
 constexpr int kLgPad = 16;        // bytes added to every LDS row of int8 data (bank spread)
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int D>
+template <typename T, int D, bool SPLIT>
 __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
   constexpr int H = kGateHidden, JC = kLgChunk, NW = kLgThreads / 64, NL = kLgLimbs;
   constexpr int KS = D / 64;                 // MFMA k-steps
@@ -709,9 +714,14 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane >> 4, n16 = lane & 15;
-  const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
-  const int G = a.Hq / a.Hkv;
   const int NB = a.NB;
+  // SPLIT: workgroup s of the unit's S takes chunks [s cpw, (s + 1) cpw) of
+  // the table (a split by the table's width, so no load waits on the length)
+  const int S = SPLIT ? (int)gridDim.x / (a.B * a.Hkv) : 1;
+  const int u = (int)blockIdx.x / S, b = u / a.Hkv, g = u - b * a.Hkv;
+  const int cpw = ((NB + JC - 1) / JC + S - 1) / S;
+  const int jbeg = ((int)blockIdx.x - u * S) * cpw * JC;
+  const int G = a.Hq / a.Hkv;
   const int jl = lane, part = wv;  // limbs: block jl of a chunk, dims part*DQ ..
 
   // ---- loads that wait on nothing: the first chunk's pooled columns (clamped
@@ -724,7 +734,7 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
 #pragma unroll
     for (int i = 0; i < DQ; ++i) x[i] = c[(int64_t)i * NB];
   };
-  load_chunk(0);
+  load_chunk(jbeg);
   // A operand: W1 row 16 wv + n16, bytes 64 s + 16 r16 .. + 15 of k-step s.
   i32x4 wa[KS];
   {
@@ -749,6 +759,7 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
     betam[i] = (double)a.w1_scale[(int64_t)g * H + m];
   }
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
+  const int jend = SPLIT ? min(n, jbeg + cpw * JC) : n;
   if (tid < D) {  // the group-summed query, fp64, head order
     const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
     double sq = load_as_double<T>(q, tid);
@@ -779,7 +790,7 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) um[i] = s_u[wv * 16 + 4 * r16 + i];
 
-  for (int j0 = 0; j0 < n; j0 += JC) {
+  for (int j0 = jbeg; j0 < jend; j0 += JC) {
     // ---- limbs of blocks j0 .. j0 + JC - 1 ----
     {
       const bool live = j0 + jl < n;
@@ -824,7 +835,7 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
       }
       if (part == 0) s_exp[jl] = e;
     }
-    if (j0 + JC < n) load_chunk(j0 + JC);  // the next chunk's loads fly while this one is scored
+    if (j0 + JC < jend) load_chunk(j0 + JC);  // the next chunk's loads fly while this one is scored
     __syncthreads();
 
     // ---- first layer on MFMA, limb by limb; the rest in fp64 ----
@@ -863,20 +874,36 @@ __global__ __launch_bounds__(kLgThreads) void learned_gate_kernel(GateArgs a) {
       double sj = s_red[0][tid];
 #pragma unroll
       for (int w = 1; w < NW; ++w) sj = sj + s_red[w][tid];
-      s_key[j0 + tid] = order_key(sj);
+      if constexpr (SPLIT) a.scores[(int64_t)u * NB + j0 + tid] = key_score(order_key(sj));
+      else s_key[j0 + tid] = order_key(sj);
     }
     // (the next chunk rewrites s_red and s_amx only after its barriers)
   }
-  __syncthreads();
-  gate_finish<kLgThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+  if constexpr (!SPLIT) {
+    __syncthreads();
+    gate_finish<kLgThreads, false>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
+  }
 }
 
 template <typename T, int D>
-const void* learned_fn() { return (const void*)&learned_gate_kernel<T, D>; }
+const void* learned_fn(bool split) {
+  return split ? (const void*)&learned_gate_kernel<T, D, true>
+               : (const void*)&learned_gate_kernel<T, D, false>;
+}
 
-const void* learned_kernel(int dtype, int D) {
-  if (dtype == 1) return D == 64 ? learned_fn<uint16_t, 64>() : learned_fn<uint16_t, 128>();
-  return D == 64 ? learned_fn<float, 64>() : learned_fn<float, 128>();
+const void* learned_kernel(int dtype, int D, bool split = false) {
+  if (dtype == 1) return D == 64 ? learned_fn<uint16_t, 64>(split) : learned_fn<uint16_t, 128>(split);
+  return D == 64 ? learned_fn<float, 64>(split) : learned_fn<float, 128>(split);
+}
+
+// Workgroups per unit of the learned gate: enough to give the chip's 256 CUs
+// about one each when units are fewer, at most one per 64-block chunk.
+int learned_gate_split(int U, int NB) {
+  constexpr int kCus = 256;
+  const int chunks = (NB + kLgChunk - 1) / kLgChunk;
+  if (U >= kCus || chunks < 2) return 1;
+  const int s = kCus / U;
+  return s < chunks ? s : chunks;
 }
 
 }  // namespace
@@ -951,8 +978,17 @@ size_t learned_gate_smem_total(int D, int NB) {
 hipError_t launch_learned_gate(const GateArgs& a, hipStream_t stream) {
   GateArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(learned_kernel(a.dtype, a.D), dim3(a.B * a.Hkv), dim3(kLgThreads), params,
-                         learned_gate_smem_dynamic(a.NB), stream);
+  const int U = a.B * a.Hkv;
+  const int S = learned_gate_split(U, a.NB);
+  if (S == 1)
+    return hipLaunchKernel(learned_kernel(a.dtype, a.D), dim3(U), dim3(kLgThreads), params,
+                           learned_gate_smem_dynamic(a.NB), stream);
+  // scores by S workgroups per unit, then the selection
+  hipError_t e = hipLaunchKernel(learned_kernel(a.dtype, a.D, true), dim3(U * S), dim3(kLgThreads),
+                                 params, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&gate_select_kernel, dim3(U), dim3(kSelectThreads), params,
+                         (size_t)a.NB * sizeof(uint64_t), stream);
 }
 
 }  // namespace seer
