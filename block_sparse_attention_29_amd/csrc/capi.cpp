@@ -470,13 +470,14 @@ seer_status gated_partial(const seer_shape* shape, const void* q, const seer_kv*
                           hipStream_t stream) {
   seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (st) return st;
+  const bool append = lens_old != nullptr;
+  if (append && (!open_sum || ((uintptr_t)open_sum & 7) != 0))
+    return fail(SEER_ERR_INVALID_ARG, "open_sum missing or not 8-byte aligned");
+  if (append && (st = check_kv(kv))) return st;
   seer::DecodeArgs a;
   if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
                            workspace, workspace_bytes, &a)))
     return st;
-  const bool append = lens_old != nullptr;
-  if (append && (!open_sum || ((uintptr_t)open_sum & 7) != 0))
-    return fail(SEER_ERR_INVALID_ARG, "open_sum missing or not 8-byte aligned");
   seer::GateArgs ga = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
   if (append) {
     ga.lens_old = lens_old;

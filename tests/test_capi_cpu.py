@@ -126,6 +126,30 @@ def test_pointer_and_rule_validation(lib):
     assert st == seer.SEER_ERR_INVALID_ARG
 
 
+def test_append_step_validation(lib):
+    """seer_gated_sparse_decode_append checks its own arguments (out, lens_old,
+    open_sum, the cache) and the gate's before any device work."""
+    sh = _shape()
+    kv = seer.KV(0x1000, 0x1000, None, 0)
+    rule = seer.make_select(keep=(1, 10))
+
+    def call(q=FAKE, kvp=ctypes.byref(kv), lens_old=FAKE, open_sum=FAKE, out=FAKE, ws=FAKE):
+        return lib.seer_gated_sparse_decode_append(
+            ctypes.byref(sh), q, kvp, lens_old, FAKE, FAKE, open_sum, ctypes.byref(rule), 4,
+            ctypes.c_float(0.0), FAKE, FAKE, FAKE, out, None, ws, 1 << 20, None)
+
+    assert call(out=None) == seer.SEER_ERR_INVALID_ARG and b"out" in lib.seer_last_error()
+    assert call(lens_old=None) == seer.SEER_ERR_INVALID_ARG
+    assert b"lens_old" in lib.seer_last_error()
+    assert call(open_sum=None) == seer.SEER_ERR_INVALID_ARG
+    assert b"open_sum" in lib.seer_last_error()
+    assert call(open_sum=ctypes.c_void_p(0x1004)) == seer.SEER_ERR_INVALID_ARG
+    assert call(q=None) == seer.SEER_ERR_INVALID_ARG
+    bad_kv = seer.KV(0x1000, None, None, 0)
+    assert call(kvp=ctypes.byref(bad_kv)) == seer.SEER_ERR_INVALID_ARG
+    assert call(kvp=None) == seer.SEER_ERR_INVALID_ARG
+
+
 def test_execution_choices_are_arguments(lib):
     """The fused-gate choice is the rule's fuse field and the combine kernel
     an argument of seer_sparse_decode_combine_mode; values outside their enums
