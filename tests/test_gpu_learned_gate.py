@@ -24,6 +24,7 @@ import numpy as np
 import pytest
 import torch
 
+from block_sparse_attention_29_amd.pipeline import DecodeState
 from oracle import seer_oracle as O
 from tests.gpu_util import TOL, f64, unit_kv
 from tests.test_gpu_parity import SMALL, state_for, units_of
@@ -240,3 +241,37 @@ def test_learned_gate_full_size(name):
         check_learned_unit(st, case, w, b, g, tag=name)
     print(f"[report] {name}: smallest selection margin / score bound over "
           f"{len(MARGINS)} units = {min(MARGINS):.3g}", flush=True)
+
+
+def test_learned_gate_split_equals_one_launch():
+    """With fewer units than CUs a unit's chunks are scored by several
+    workgroups and selected by a second launch; with as many units as CUs by
+    one workgroup in one launch.  The same sequences gated both ways (a batch
+    of 32, 256 units, and its first 8 sequences, 64 units) give bit-identical
+    scores, ids and counts."""
+    wl = WORKLOADS["planted_8k"].with_(batch=32)
+    print("[case] learned gate split vs one launch, planted_8k shape, 32 and 8 sequences",
+          flush=True)
+    case = make_case(wl, "cuda")
+    w = make_gate_weights(wl.num_kv_heads, wl.head_dim, seed=7).to("cuda")
+    full = state_for(case, gate_weights=w)
+    full.build_pool(case.lens)
+    full.select(case.q, case.lens)
+    part_b = 8
+    part = DecodeState(batch=part_b, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                       head_dim=wl.head_dim, block_size=wl.block_size, max_blocks=wl.max_blocks,
+                       dtype=torch.bfloat16, k=case.k[:part_b], v=case.v[:part_b], keep=wl.keep,
+                       gate_weights=w)
+    lens = case.lens[:part_b].contiguous()
+    part.build_pool(lens)
+    part.select(case.q[:part_b].contiguous(), lens)
+    torch.cuda.synchronize()
+    U = part_b * wl.num_kv_heads
+    NB = wl.max_blocks
+    s_full = full.scores.view(-1, NB)[:U].cpu()
+    s_part = part.scores.view(-1, NB).cpu()
+    n = (wl.context + wl.block_size - 1) // wl.block_size
+    assert torch.equal(s_full[:, :n].view(torch.int64), s_part[:, :n].view(torch.int64))
+    assert torch.equal(full.sel_cnt[:U].cpu(), part.sel_cnt.cpu())
+    assert torch.equal(full.sel_idx.view(-1, full.k_max)[:U].cpu(),
+                       part.sel_idx.view(-1, part.k_max).cpu())
