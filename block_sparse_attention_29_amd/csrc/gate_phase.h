@@ -197,10 +197,24 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
   for (int j0 = PASS; j0 < n; j0 += PASS) pass(j0, BoolTag<false>{});
 }
 
+// The selection outputs of unit u from LDS: its k kept ids (dst, then -1 up to
+// k_max), its count and the scores of its n blocks (s_key).  Thread-strided, no
+// barrier: the LDS values must have been final before a barrier every thread
+// has passed.
+__device__ __forceinline__ void fused_gate_write(const DecodeArgs& a, int u, int n, int k,
+                                                 const int32_t* dst, const uint64_t* s_key) {
+  const int tid = threadIdx.x;
+  int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
+  for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
+  if (tid == 0) a.sel_cnt_out[u] = k;
+  double* sc = a.scores + (int64_t)u * a.NB;
+  for (int j = tid; j < n; j += kThreads) sc[j] = key_score(s_key[j]);
+}
+
 // Gate of unit u inside a decode workgroup (the fused mode): the fp64 scores
 // of its n blocks (fused_scores), then its k kept ids, ascending, into dst
-// (LDS).  The owner workgroup of the unit also writes the scores, ids and
-// count out.
+// (LDS).  With `owner` the workgroup also writes the scores, ids and count out
+// (fused_gate_write); a caller may instead write them later from the same LDS.
 template <typename T, int D, int QR, bool MULTI, bool PRE>
 __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
                                                 int32_t* dst,
@@ -251,13 +265,7 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
     }
     __syncthreads();
   }
-  if (owner) {
-    int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
-    for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
-    if (tid == 0) a.sel_cnt_out[u] = k;
-    double* sc = a.scores + (int64_t)u * NB;
-    for (int j = tid; j < n; j += kThreads) sc[j] = key_score(s_key[j]);
-  }
+  if (owner) fused_gate_write(a, u, n, k, dst, s_key);
   __syncthreads();  // s_key, s_q and s_part are reused by the next unit
 }
 

@@ -119,10 +119,6 @@ void decode_multi_kernel(DecodeArgs a) {
     }
     if (tid == 0) s_prefix[U] = total;
     __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int u = tid; u <= U; u += kThreads) a.prefix[u] = s_prefix[u];
-      if (tid == 0) a.hdr[0] = a.W;
-    }
   }
 
   const int lane = tid & 63, wv = tid >> 6;
@@ -136,13 +132,19 @@ void decode_multi_kernel(DecodeArgs a) {
   // LDS (a unit shared by workgroups is selected by each, bit-identically) ----
   int32_t* s_ids = s_len + U;  // [ids_cap] kept ids of this workgroup's units, slot - ids_base
   int ids_base = 0;
+  // The scores of the unit gated last stay in s_key (LDS) to the end.
+  uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
+  // The unit whose selection this workgroup writes out after its tiles (-1:
+  // none): outputs still in flight would hold the first tile back (stores and
+  // loads share one memory counter).  Only the last unit gated can wait: the
+  // next unit's gate reuses s_key.
+  int late_u = -1;
   if constexpr (GATED) {
     __shared__ double s_q[D];
     __shared__ double s_part[4 * 256];  // quarter sums of one pass
     __shared__ int s_hist[3 * 256];
     __shared__ int s_sel_scan[kWavesPerWG + 1];
     __shared__ int s_wgu[2];            // units of the workgroup's first and last tile
-    uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
     const int Y0 = split.start(wg0);
     const int Y1 = split.start(wg0 + kWavesPerWG);
     if (Y0 < Y1) {
@@ -162,27 +164,45 @@ void decode_multi_kernel(DecodeArgs a) {
         if (k == 0) return;
         // the owner holds the unit's first tile
         const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
+        const bool late = owner == wg && u == u1;
+        if (late) late_u = u;
         fused_gate_unit<T, D, kRows, true, decltype(pre_tag)::value>(
             a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
-            owner == wg, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
+            owner == wg && !late, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
       };
       // The first unit may use the entry loads; peeled off, so that they are
       // dead in the loop.
       gate(u0, BoolTag<true>{});
       for (int u = u0 + 1; u <= u1; ++u) gate(u, BoolTag<false>{});
     }
-    // Units without a kept block (a sequence of length 0) belong to nobody:
-    // workgroup 0 writes their (empty) selection.
+  }
+  // The stores that nothing in this launch reads, issued by every thread once
+  // its own tiles are done (from LDS values that were final before a barrier
+  // it has passed): workgroup 0's copy of the plan for the merge and, with the
+  // gate, the (empty) selections of units without a kept block (a sequence of
+  // length 0, which belong to nobody), and the late unit's outputs.
+  auto write_late = [&]() {
     if (blockIdx.x == 0) {
-      for (int u = tid; u < U; u += kThreads) {
-        if (s_prefix[u] != s_prefix[u + 1]) continue;
-        for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)u * a.k_max + i] = -1;
-        a.sel_cnt_out[u] = 0;
+      for (int uu = tid; uu <= U; uu += kThreads) a.prefix[uu] = s_prefix[uu];
+      if (tid == 0) a.hdr[0] = a.W;
+      if (GATED) {
+        for (int uu = tid; uu < U; uu += kThreads) {
+          if (s_prefix[uu] != s_prefix[uu + 1]) continue;
+          for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)uu * a.k_max + i] = -1;
+          a.sel_cnt_out[uu] = 0;
+        }
       }
     }
-  }
+    if (GATED && late_u >= 0)
+      fused_gate_write(a, late_u, seq_blocks(s_len[late_u], a.S, a.NB),
+                       s_prefix[late_u + 1] - s_prefix[late_u],
+                       s_ids + (s_prefix[late_u] - ids_base), s_key);
+  };
   const int y0 = split.start(w), y1 = split.start(w + 1);
-  if (y0 >= y1) return;
+  if (y0 >= y1) {
+    write_late();
+    return;
+  }
 
   const bool sparse = a.sel_idx != nullptr;
   const int Hkv = a.Hkv, S = a.S, NB = a.NB;
@@ -451,6 +471,7 @@ void decode_multi_kernel(DecodeArgs a) {
       }
     }
   }
+  write_late();
 }
 
 // Merges a unit's records for one query row (token t = row / G, head

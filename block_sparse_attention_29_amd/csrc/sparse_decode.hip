@@ -117,10 +117,6 @@ void decode_partial_kernel(DecodeArgs a) {
     }
     if (tid == 0) s_prefix[U] = total;
     __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int u = tid; u <= U; u += kThreads) a.prefix[u] = s_prefix[u];
-      if (tid == 0) a.hdr[0] = a.W;
-    }
   }
 
   // The wave index is uniform per wave; say so, so that everything derived
@@ -154,12 +150,19 @@ void decode_partial_kernel(DecodeArgs a) {
   // selected by each of them, bit-identically) ----
   int32_t* s_ids = s_len + U;  // [ids_cap] kept ids of this workgroup's units, slot - ids_base
   int ids_base = 0;
+  // The scores of the unit gated last stay in s_key (LDS) to the end.
+  uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
+  // The unit whose selection this workgroup writes out after its tiles (-1:
+  // none).  Stores share the one memory counter with loads, so outputs still in
+  // flight when the first tile is requested would hold its QK^T back until
+  // they are acknowledged; written at the end they cost nothing.  Only the
+  // last unit gated can wait: the next unit's gate reuses s_key.
+  int late_u = -1;
   if constexpr (GATED) {
     __shared__ double s_q[D];
     __shared__ double s_part[4 * 256];  // quarter sums of one pass (4 x 64*VEC)
     __shared__ int s_hist[3 * 256];
     __shared__ int s_sel_scan[kWavesPerWG + 1];
-    uint64_t* s_key = (uint64_t*)(((uintptr_t)(s_ids + a.ids_cap) + 7) & ~(uintptr_t)7);
     const int Y0 = split.start(wg0);
     const int Y1 = split.start(wg0 + kWavesPerWG);
     if (Y0 < Y1) {
@@ -170,28 +173,46 @@ void decode_partial_kernel(DecodeArgs a) {
         if (k == 0) return;
         // the owner holds the unit's first tile
         const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
+        const bool late = owner == wg && u == u1;
+        if (late) late_u = u;
         fused_gate_unit<T, D, G, false, decltype(pre_tag)::value>(
             a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
-            owner == wg, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
+            owner == wg && !late, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
       };
       // The first unit may use the entry loads; peeled off, so that they are
       // dead in the loop.
       gate(u0, BoolTag<true>{});
       for (int u = u0 + 1; u <= u1; ++u) gate(u, BoolTag<false>{});
     }
-    // Units without a kept block (a sequence of length 0) belong to nobody:
-    // workgroup 0 writes their (empty) selection.
+  }
+  // The stores that nothing in this launch reads, issued by every thread once
+  // its own tiles are done (from LDS values that were final before a barrier
+  // it has passed): workgroup 0's copy of the plan for the merge and, with the
+  // gate, the (empty) selections of units without a kept block (a sequence of
+  // length 0, which belong to nobody), and the late unit's outputs.
+  auto write_late = [&]() {
     if (blockIdx.x == 0) {
-      for (int u = tid; u < U; u += kThreads) {
-        if (s_prefix[u] != s_prefix[u + 1]) continue;
-        for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)u * a.k_max + i] = -1;
-        a.sel_cnt_out[u] = 0;
+      for (int uu = tid; uu <= U; uu += kThreads) a.prefix[uu] = s_prefix[uu];
+      if (tid == 0) a.hdr[0] = a.W;
+      if (GATED) {
+        for (int uu = tid; uu < U; uu += kThreads) {
+          if (s_prefix[uu] != s_prefix[uu + 1]) continue;
+          for (int i = 0; i < a.k_max; ++i) a.sel_idx_out[(int64_t)uu * a.k_max + i] = -1;
+          a.sel_cnt_out[uu] = 0;
+        }
       }
     }
-  }
+    if (GATED && late_u >= 0)
+      fused_gate_write(a, late_u, seq_blocks(s_len[late_u], a.S, a.NB),
+                       s_prefix[late_u + 1] - s_prefix[late_u],
+                       s_ids + (s_prefix[late_u] - ids_base), s_key);
+  };
   const int y0 = split.start(w);
   const int y1 = split.start(w + 1);
-  if (y0 >= y1) return;
+  if (y0 >= y1) {
+    write_late();
+    return;
+  }
 
   const bool sparse = a.sel_idx != nullptr;
   const int Hkv = a.Hkv, S = a.S, NB = a.NB;
@@ -507,6 +528,7 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
   }
+  write_late();
 }
 
 
