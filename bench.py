@@ -218,12 +218,16 @@ def run_workload(wl, args):
         return case.q, case.lens
 
     # does the step select inside the attention kernel for this shape?
-    fused = seer.gated_decode_is_fused(states[0].shape, states[0].rule, states[0].k_max, T)
+    # (2: the score kernel scores first and the attention kernel selects)
+    path = seer.gated_decode_path(states[0].shape, states[0].rule, states[0].k_max, T)
+    fused = path != 0
 
     def partial_only(i):
         """The step's dominant kernel alone (no combine): the fused gate +
-        partial-decode kernel, else the partial kernel (several query tokens:
-        the multi-token one) on the selection the step made."""
+        partial-decode kernel (with long tables the gate's score kernel and
+        the attention kernel that selects from its scores, both), else the
+        partial kernel (several query tokens: the multi-token one) on the
+        selection the step made."""
         st, case = layer_of(i)
         q, lens = q_lens(i)
         if T > 1 and fused:
@@ -537,12 +541,16 @@ def run_workload(wl, args):
         "step_hbm_gbps": step_gbps,
         "step_pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "gate_fused": fused,
+        "gate_path": ["gate kernels first", "scores and selection in the attention kernel",
+                      "score kernel, then selection in the attention kernel"][path],
         "unfused": None if unfused_ms is None else {
             "ms_per_step": unfused_ms, "speedup_fused_vs_unfused": unfused_ms / ms_per_step},
         "roofline": {"bound": "hbm",
-                     "kernel": ((f"decode_multi_kernel<{wl.dtype},{d}" if T > 1 else
-                                 f"decode_partial_kernel<{wl.dtype},{d},{G}")
-                                + (",gated>" if fused else ">")),
+                     "kernel": (("gate_score_kernel + " if path == 2 else "")
+                                + (f"decode_multi_kernel<{wl.dtype},{d}" if T > 1 else
+                                   f"decode_partial_kernel<{wl.dtype},{d},{G}")
+                                + (",gated from scores>" if path == 2 else
+                                   ",gated>" if fused else ">")),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": k_bytes, "launch_ms": k_ms},

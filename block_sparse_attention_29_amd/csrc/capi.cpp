@@ -245,15 +245,40 @@ bool fused_gate_runs(const seer_shape* s, const seer_select* rule, int32_t k_max
   return st + dyn <= max_block_smem();
 }
 
+// Whether a single-token call with W waves takes the scores from the gate's
+// score kernel and selects inside the attention kernel: a per-unit top-k rule
+// left to the library, a table of more than one 256-block score chunk (where
+// re-scoring it in every workgroup that shares a unit costs more than the
+// selection launch it saves), at most one unit per workgroup, and the LDS
+// fits.  Each workgroup then selects its units from their scores (the unit's
+// selection, bit-identical in every workgroup) in place of a selection launch
+// and its round trips.
+bool given_scores_runs(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
+                       int tokens) {
+  if (tokens != 1 || rule->mode != SEER_SELECT_TOPK || rule->unified) return false;
+  if (rule->fuse != SEER_FUSE_AUTO) return false;
+  if (s->max_blocks <= seer::kGateScoreChunk) return false;
+  const int U = s->batch * s->num_kv_heads;
+  if (U > W / seer::kDecodeWavesPerWG) return false;
+  const size_t st = gated_static_smem(s, tokens);
+  if (st == (size_t)-1) return false;
+  const size_t dyn = seer::gated_decode_smem_bytes(U, s->max_blocks,
+                                                   seer::gated_decode_ids_cap(U, k_max, W));
+  return st + dyn <= max_block_smem();
+}
+
 // How a gated call selects, for this shape, rule and wave count.
 enum GatePath {
   kGateKernels = 0,  // the gate kernel(s) first, then the attention kernel
   kGateFused = 1,    // scores and selection inside the attention kernel
+  kGateScoresThenFused = 2,  // the score kernel, then selection inside the attention kernel
 };
 
 GatePath gate_path(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
                    int tokens) {
-  return fused_gate_runs(s, rule, k_max, W, tokens) ? kGateFused : kGateKernels;
+  if (fused_gate_runs(s, rule, k_max, W, tokens)) return kGateFused;
+  if (given_scores_runs(s, rule, k_max, W, tokens)) return kGateScoresThenFused;
+  return kGateKernels;
 }
 
 // Turns the partial kernel's arguments into the fused gate's: the kernel
@@ -498,6 +523,14 @@ seer_status gated_partial(const seer_shape* shape, const void* q, const seer_kv*
   switch (path) {
     case kGateFused:
       set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
+      e = seer::launch_gated_decode_partial(a, stream);
+      if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
+      break;
+    case kGateScoresThenFused:
+      e = seer::launch_gate_scores(ga, stream);
+      if (e != hipSuccess) return hip_fail(e, "gate score launch");
+      set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
+      a.scores_in = scores;
       e = seer::launch_gated_decode_partial(a, stream);
       if (e != hipSuccess) return hip_fail(e, "gated decode_partial launch");
       break;

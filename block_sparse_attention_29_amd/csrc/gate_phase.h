@@ -65,11 +65,33 @@ struct GatePreload {
   int u;
   float pv[D / 4][4];
   T qr[QR];
+  // With scores given (a.scores_in): unit u's scores tid + 256 e instead
+  // (sx_ok says they were loaded).
+  double sx[8];
+  bool sx_ok;
 };
 
-template <typename T, int D, int QR, bool MULTI>
+// The first unit's given scores, requested at kernel entry (scores_in set;
+// u as in issue_gate_preload).  Ids past the table are clamped into the unit's
+// row (read, unused).
+__device__ __forceinline__ void issue_score_preload_into(const DecodeArgs& a, int u, int& pu,
+                                                         double (&sx)[8], bool& ok) {
+  const double* sc = a.scores_in + (int64_t)u * a.NB;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sx[e] = sc[min(tid + e * kThreads, a.NB - 1)];
+  pu = u;
+  ok = true;
+}
+
+template <typename T, int D, int QR, bool MULTI, bool GIVEN = false>
 __device__ __forceinline__ void issue_gate_preload(const DecodeArgs& a, int u,
                                                    GatePreload<T, D, QR>& pre) {
+  pre.sx_ok = false;
+  if constexpr (GIVEN) {  // the scores are given (a.scores_in): load those instead
+    issue_score_preload_into(a, u, pre.u, pre.sx, pre.sx_ok);
+    return;
+  }
   constexpr int DQ = D / 4;
   const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
   const int NB = a.NB;
@@ -197,16 +219,59 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
   for (int j0 = PASS; j0 < n; j0 += PASS) pass(j0, BoolTag<false>{});
 }
 
+// The order keys of unit u's n given scores (a.scores_in, as the gate's score
+// kernel wrote them) into s_key, their AND and OR published for the selection
+// like fused_scores does; ends with a barrier.  The first 8 * kThreads come
+// from the entry loads when those are this unit's.
+template <typename T, int D, int QR, bool PRE>
+__device__ __forceinline__ void given_score_keys(const DecodeArgs& a, int u, int n,
+                                                 uint64_t* s_key, int* s_hist,
+                                                 const GatePreload<T, D, QR>& pre, bool use_pre) {
+  const int tid = threadIdx.x;
+  const double* sc = a.scores_in + (int64_t)u * a.NB;
+  double x[8];
+  bool from_pre = false;
+  if constexpr (PRE) from_pre = use_pre;  // (peeled: the entry loads are dead after)
+  if (from_pre) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = pre.sx[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[min(tid + e * kThreads, n - 1)];
+  }
+  uint64_t kand = ~0ull, kor = 0;
+  auto put = [&](int j, double v) {
+    const uint64_t key = order_key(v);
+    s_key[j] = key;
+    kand &= key;
+    kor |= key;
+  };
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (tid + e * kThreads < n) put(tid + e * kThreads, x[e]);
+  for (int j0 = tid + 8 * kThreads; j0 < n; j0 += 8 * kThreads) {  // longer tables
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[min(j0 + e * kThreads, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j0 + e * kThreads < n) put(j0 + e * kThreads, x[e]);
+  }
+  topk_keys_publish<kThreads>(kand, kor, s_hist);
+  __syncthreads();
+}
+
 // The selection outputs of unit u from LDS: its k kept ids (dst, then -1 up to
-// k_max), its count and the scores of its n blocks (s_key).  Thread-strided, no
-// barrier: the LDS values must have been final before a barrier every thread
-// has passed.
+// k_max), its count and (unless GIVEN: they came from a.scores_in) the scores
+// of its n blocks (s_key).  Thread-strided, no barrier: the LDS values must
+// have been final before a barrier every thread has passed.
+template <bool GIVEN = false>
 __device__ __forceinline__ void fused_gate_write(const DecodeArgs& a, int u, int n, int k,
                                                  const int32_t* dst, const uint64_t* s_key) {
   const int tid = threadIdx.x;
   int32_t* ids = a.sel_idx_out + (int64_t)u * a.k_max;
   for (int i = tid; i < a.k_max; i += kThreads) ids[i] = i < k ? dst[i] : -1;
   if (tid == 0) a.sel_cnt_out[u] = k;
+  if constexpr (GIVEN) return;  // the given scores are already the output
   double* sc = a.scores + (int64_t)u * a.NB;
   for (int j = tid; j < n; j += kThreads) sc[j] = key_score(s_key[j]);
 }
@@ -215,7 +280,7 @@ __device__ __forceinline__ void fused_gate_write(const DecodeArgs& a, int u, int
 // of its n blocks (fused_scores), then its k kept ids, ascending, into dst
 // (LDS).  With `owner` the workgroup also writes the scores, ids and count out
 // (fused_gate_write); a caller may instead write them later from the same LDS.
-template <typename T, int D, int QR, bool MULTI, bool PRE>
+template <typename T, int D, int QR, bool MULTI, bool PRE, bool GIVEN = false>
 __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
                                                 int32_t* dst,
                                                 bool owner, uint64_t* s_key, double* s_q,
@@ -226,7 +291,9 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   const int NB = a.NB;
   const float* pu = a.pooled + (int64_t)u * D * NB;
   const bool use_pre = u == pre.u;  // the entry loads are this unit's (uniform)
-  if (NB % 4 == 0)
+  if constexpr (GIVEN)  // scores given by the gate's score kernel
+    given_score_keys<T, D, QR, PRE>(a, u, n, s_key, s_hist, pre, use_pre && pre.sx_ok);
+  else if (NB % 4 == 0)
     fused_scores<T, D, QR, MULTI, 4, PRE>(a, b, g, pu, n, s_q, s_part, s_key, s_hist, pre,
                                             use_pre);
   else if (NB % 2 == 0)
@@ -265,7 +332,7 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
     }
     __syncthreads();
   }
-  if (owner) fused_gate_write(a, u, n, k, dst, s_key);
+  if (owner) fused_gate_write<GIVEN>(a, u, n, k, dst, s_key);
   __syncthreads();  // s_key, s_q and s_part are reused by the next unit
 }
 

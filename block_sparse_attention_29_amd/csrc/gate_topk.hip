@@ -937,6 +937,17 @@ const void* pick_score_fn(const GateArgs& a, bool one_chunk) {
 
 bool gate_topk_appends(const GateArgs& a) { return !a.unified; }
 
+hipError_t launch_gate_scores(const GateArgs& a, hipStream_t stream) {
+  static_assert(kGateScoreChunk == kScoreChunk, "score chunk");
+  const int U = a.B * a.Hkv;
+  const int nchunk = (a.NB + kScoreChunk - 1) / kScoreChunk;
+  if (a.unified || nchunk < 2) return hipErrorInvalidValue;
+  GateArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(pick_score_fn(a, false), dim3(U * nchunk), dim3(kScoreThreads), params,
+                         0, stream);
+}
+
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream) {
   const int U = a.B * a.Hkv;
   GateArgs args = a;

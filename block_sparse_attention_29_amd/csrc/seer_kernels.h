@@ -50,6 +50,10 @@ struct DecodeArgs {
   int32_t ids_cap;        // kept ids one workgroup holds in LDS
   int32_t force_first, force_last;  // forced blocks of the fused gate's top-k
   int32_t tokens;         // new query tokens per sequence (multi-token kernel; q [B][tokens][Hq][D])
+  // Single-token gated kernel only: the units' scores [B][Hkv][NB], already
+  // written by the gate's score kernel; the kernel selects from them instead
+  // of scoring the pooled table (and leaves `scores` as it is).  nullptr: score.
+  const double* scores_in;
 };
 
 struct CombineArgs {
@@ -136,6 +140,12 @@ struct GateArgs {
 };
 
 hipError_t launch_gate_topk(const GateArgs& a, hipStream_t stream);
+// The per-chunk score kernel of launch_gate_topk alone (with a.append as
+// there), for a table of more than one 256-block chunk and a per-unit rule:
+// the scores go to a.scores and the selection is left to the caller.
+hipError_t launch_gate_scores(const GateArgs& a, hipStream_t stream);
+// Blocks per workgroup of that score kernel.
+constexpr int kGateScoreChunk = 256;
 // Whether launch_gate_topk can take a.append (per-unit rules; not unified).
 bool gate_topk_appends(const GateArgs& a);
 // Dynamic LDS of the gate kernel.

@@ -51,9 +51,12 @@
 namespace seer {
 namespace {
 
-template <typename T, int D, int G, bool GATED>
+// GIVEN (with GATED): the units' scores come from a.scores_in (the gate's
+// score kernel ran first); the workgroups only select.
+template <typename T, int D, int G, bool GATED, bool GIVEN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partial_kernel(DecodeArgs a) {
+  static_assert(GATED || !GIVEN, "given scores need the gate phase");
   using GE = Geo<T, D>;
   constexpr int EB = GE::EB, ROWB = GE::ROWB, E = GE::E, NKL = GE::NKL;
   constexpr int LPR = GE::LPR, RPI = GE::RPI, NVL = GE::NVL;
@@ -99,7 +102,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int aux_f = unit_aux<GATED>(a, u_f);
     // (wg0 * U < 2^31: fewer than 2^15 waves, at most 2^13 units)
     if constexpr (GATED)
-      issue_gate_preload<T, D, G, false>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
+      issue_gate_preload<T, D, G, false, GIVEN>(a, (int)((uint32_t)(wg0 * U) / (uint32_t)a.W), pre);
     int local = 0;
     for (int u = u_lo; u < u_hi; ++u) {
       const int L = u == u_lo ? L_f : a.lens[u / a.Hkv];
@@ -175,7 +178,7 @@ void decode_partial_kernel(DecodeArgs a) {
         const int owner = tile_owner((int64_t)s_prefix[u] << tsh, a.W, Tot) / kWavesPerWG;
         const bool late = owner == wg && u == u1;
         if (late) late_u = u;
-        fused_gate_unit<T, D, G, false, decltype(pre_tag)::value>(
+        fused_gate_unit<T, D, G, false, decltype(pre_tag)::value, GIVEN>(
             a, u, seq_blocks(s_len[u], a.S, a.NB), k, s_ids + (s_prefix[u] - ids_base),
             owner == wg && !late, s_key, s_q, s_part, s_hist, s_sel_scan, pre);
       };
@@ -203,7 +206,7 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
     if (GATED && late_u >= 0)
-      fused_gate_write(a, late_u, seq_blocks(s_len[late_u], a.S, a.NB),
+      fused_gate_write<GIVEN>(a, late_u, seq_blocks(s_len[late_u], a.S, a.NB),
                        s_prefix[late_u + 1] - s_prefix[late_u],
                        s_ids + (s_prefix[late_u] - ids_base), s_key);
   };
@@ -788,38 +791,43 @@ __global__ __launch_bounds__(D) void decode_combine_head_kernel(CombineArgs a) {
   if (a.lse && tid == 0) a.lse[head] = l > 0.f ? (M + log2f(l)) * 0.69314718055994530942f : kNegInf;
 }
 
-template <typename T, int D, int G, bool GATED>
-const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G, GATED>; }
+template <typename T, int D, int G, bool GATED, bool GIVEN>
+const void* partial_fn() { return (const void*)&decode_partial_kernel<T, D, G, GATED, GIVEN>; }
 
 using KernelFn = const void* (*)();
 
-template <typename T, int D, bool GATED>
+template <typename T, int D, bool GATED, bool GIVEN>
 KernelFn pick_g(int G) {
   switch (G) {
-    case 1: return &partial_fn<T, D, 1, GATED>;
-    case 2: return &partial_fn<T, D, 2, GATED>;
-    case 3: return &partial_fn<T, D, 3, GATED>;
-    case 4: return &partial_fn<T, D, 4, GATED>;
-    case 5: return &partial_fn<T, D, 5, GATED>;
-    case 6: return &partial_fn<T, D, 6, GATED>;
-    case 7: return &partial_fn<T, D, 7, GATED>;
-    case 8: return &partial_fn<T, D, 8, GATED>;
+    case 1: return &partial_fn<T, D, 1, GATED, GIVEN>;
+    case 2: return &partial_fn<T, D, 2, GATED, GIVEN>;
+    case 3: return &partial_fn<T, D, 3, GATED, GIVEN>;
+    case 4: return &partial_fn<T, D, 4, GATED, GIVEN>;
+    case 5: return &partial_fn<T, D, 5, GATED, GIVEN>;
+    case 6: return &partial_fn<T, D, 6, GATED, GIVEN>;
+    case 7: return &partial_fn<T, D, 7, GATED, GIVEN>;
+    case 8: return &partial_fn<T, D, 8, GATED, GIVEN>;
   }
   return nullptr;
 }
 
-template <bool GATED>
+template <bool GATED, bool GIVEN = false>
 const void* pick_kernel(int dtype, int D, int G) {
   KernelFn f = nullptr;
   if (dtype == 1)
-    f = D == 64 ? pick_g<uint16_t, 64, GATED>(G) : D == 128 ? pick_g<uint16_t, 128, GATED>(G) : nullptr;
+    f = D == 64 ? pick_g<uint16_t, 64, GATED, GIVEN>(G)
+                : D == 128 ? pick_g<uint16_t, 128, GATED, GIVEN>(G) : nullptr;
   else
-    f = D == 64 ? pick_g<float, 64, GATED>(G) : D == 128 ? pick_g<float, 128, GATED>(G) : nullptr;
+    f = D == 64 ? pick_g<float, 64, GATED, GIVEN>(G)
+                : D == 128 ? pick_g<float, 128, GATED, GIVEN>(G) : nullptr;
   return f ? f() : nullptr;
 }
 
 const void* partial_kernel(int dtype, int D, int G) { return pick_kernel<false>(dtype, D, G); }
 const void* gated_kernel(int dtype, int D, int G) { return pick_kernel<true>(dtype, D, G); }
+const void* gated_given_kernel(int dtype, int D, int G) {
+  return pick_kernel<true, true>(dtype, D, G);
+}
 
 template <int D, int G>
 const void* combine_fn(bool per_head) {
@@ -917,7 +925,7 @@ int gated_decode_ids_cap(int U, int k_max, int W) {
 
 hipError_t launch_gated_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  const void* fn = gated_kernel(a.dtype, a.D, G);
+  const void* fn = a.scores_in ? gated_given_kernel(a.dtype, a.D, G) : gated_kernel(a.dtype, a.D, G);
   if (!fn) return hipErrorInvalidValue;
   const int U = a.B * a.Hkv;
   DecodeArgs args = a;

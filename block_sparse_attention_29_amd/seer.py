@@ -447,15 +447,24 @@ def sparse_decode_combine(shape: Shape, out: torch.Tensor, lse: Optional[torch.T
                                                    workspace.numel(), _stream()))
 
 
-def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int, tokens: int = 1) -> bool:
-    """seer_gated_decode_is_fused: whether gated_sparse_decode (tokens = 1) or
-    multi_gated_sparse_decode selects inside the attention kernel for this
-    shape and rule on the current device."""
+def gated_decode_path(shape: Shape, rule: Select, k_max: int, tokens: int = 1) -> int:
+    """seer_gated_decode_is_fused's value: 1 if gated_sparse_decode (tokens = 1)
+    or multi_gated_sparse_decode scores and selects inside the attention
+    kernel for this shape and rule on the current device, 2 if the score
+    kernel scores first and the attention kernel selects, 0 if the gate
+    kernel(s) run first."""
     lib = load()
     f = ctypes.c_int32(0)
     _check(lib.seer_gated_decode_is_fused(ctypes.byref(shape), tokens, ctypes.byref(rule), k_max,
                                           ctypes.byref(f)))
-    return bool(f.value)
+    return int(f.value)
+
+
+def gated_decode_is_fused(shape: Shape, rule: Select, k_max: int, tokens: int = 1) -> bool:
+    """Whether gated_sparse_decode (tokens = 1) or multi_gated_sparse_decode
+    selects inside the attention kernel for this shape and rule on the
+    current device (gated_decode_path nonzero)."""
+    return gated_decode_path(shape, rule, k_max, tokens) != 0
 
 
 def multi_gated_sparse_decode(shape: Shape, tokens: int, q: torch.Tensor, kv: KV,

@@ -297,20 +297,25 @@ seer_status seer_sparse_decode_combine_mode(const seer_shape* shape, int32_t mod
  *  The selection is fused for top-k rules (forced blocks included) while
  *  every workgroup gates about one unit in one pass: at most one (sequence,
  *  KV head) unit per workgroup of the attention kernel and at most 256
- *  blocks per unit.  For a threshold or unified rule, more units or longer
- *  tables, or when one workgroup's selections would not fit in its LDS, the
- *  call runs the gate kernel first instead (same results, one launch more).
- *  seer_gated_decode_is_fused tells which for a shape.  rule->fuse
- *  overrides the choice (SEER_FUSE_ALWAYS fuses whenever the rule allows it
- *  and the selections fit in LDS, SEER_FUSE_NEVER never); the results do not
- *  depend on it.
+ *  blocks per unit.  With longer tables (and a top-k rule, at most one unit
+ *  per workgroup, rule->fuse left to the library) the gate's score kernel
+ *  scores the table first and the attention kernel's workgroups select from
+ *  those scores (the selection launch is saved).  For a threshold or unified
+ *  rule, more units, or when one workgroup's selections would not fit in its
+ *  LDS, the call runs the gate kernel(s) first instead (same results, one
+ *  launch more).  seer_gated_decode_is_fused tells which for a shape.
+ *  rule->fuse overrides the choice (SEER_FUSE_ALWAYS scores and selects in
+ *  the attention kernel whenever the rule allows it and the selections fit
+ *  in LDS, SEER_FUSE_NEVER never selects there); the results do not depend
+ *  on it.
  * _partial: the first launch(es) alone (gate + partial results in the
  * workspace, selections written); seer_sparse_decode_combine finishes it. */
 /* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode
  * (tokens = 1) or seer_multi_gated_sparse_decode (tokens > 1) with this shape,
- * rule and k_max selects inside the attention kernel on the current device,
- * 0 if it runs the gate kernel(s) first (no launch; results are the same
- * either way).  SEER_ERR_INVALID_ARG for NULL pointers, k_max outside [1,
+ * rule and k_max scores and selects inside the attention kernel on the
+ * current device, 2 if the gate's score kernel scores first and the attention
+ * kernel selects (tokens = 1 only), 0 if it runs the gate kernel(s) first (no
+ * launch; results are the same either way).  SEER_ERR_INVALID_ARG for NULL pointers, k_max outside [1,
  * max_blocks] or a token count outside [1, 16 / G]. */
 seer_status seer_gated_decode_is_fused(const seer_shape* shape, int32_t tokens,
                                        const seer_select* rule, int32_t k_max, int32_t* fused);

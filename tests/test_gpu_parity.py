@@ -564,14 +564,15 @@ def test_fused_forced_blocks_equal_separate_calls(rule):
         assert torch.equal(getattr(fused, attr), getattr(sep, attr)), attr
 
 
-@pytest.mark.parametrize("name,want", [("sparse90_32k", True), ("budget_32k", True),
-                                       ("planted_8k", True), ("tiny_1k", True),
-                                       ("long_131k", False), ("paged_var", False)])
+@pytest.mark.parametrize("name,want", [("sparse90_32k", 1), ("budget_32k", 1),
+                                       ("planted_8k", 1), ("tiny_1k", 1),
+                                       ("long_131k", 2), ("paged_var", 0)])
 def test_fusion_policy(name, want):
     """The gate is fused while each workgroup gates about one unit in one
-    pass (at most one unit per workgroup, at most 256 blocks per unit), and
-    never for a threshold or unified rule; the rule's fuse field forces
-    either way."""
+    pass (at most one unit per workgroup, at most 256 blocks per unit: 1);
+    with longer tables and at most one unit per workgroup the score kernel
+    scores and the attention kernel selects (2); never for a threshold or
+    unified rule; the rule's fuse field forces either way."""
     wl = WORKLOADS[name]
     shape = seer.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                             wl.block_size, wl.max_blocks, DT[wl.dtype])
@@ -582,11 +583,51 @@ def test_fusion_policy(name, want):
     def rule(fuse=None):
         return seer.make_select(keep=wl.keep, top_k=top_k, fuse=fuse)
 
-    assert seer.gated_decode_is_fused(shape, rule(), k_max) == want
+    assert seer.gated_decode_path(shape, rule(), k_max) == want
+    assert seer.gated_decode_is_fused(shape, rule(), k_max) == (want != 0)
     thr = seer.make_select(threshold=0.0, fuse=True)
-    assert not seer.gated_decode_is_fused(shape, thr, k_max)
-    assert not seer.gated_decode_is_fused(shape, rule(False), k_max)
-    assert seer.gated_decode_is_fused(shape, rule(True), k_max)      # these all fit in LDS
+    assert seer.gated_decode_path(shape, thr, k_max) == 0
+    assert seer.gated_decode_path(shape, seer.make_select(keep=wl.keep, top_k=top_k,
+                                                          unified=True), k_max) == 0
+    assert seer.gated_decode_path(shape, rule(False), k_max) == 0
+    assert seer.gated_decode_path(shape, rule(True), k_max) == 1   # these all fit in LDS
+
+
+@pytest.mark.parametrize("rule", [dict(), dict(force_first=True),
+                                  dict(force_first=True, force_last=True)],
+                         ids=["plain", "first", "both"])
+def test_given_scores_path_equals_separate_calls(rule):
+    """Tables longer than one score chunk, with at most one unit per
+    workgroup: the score kernel scores and the attention kernel's workgroups
+    select from those scores.  Scores, ids, counts, out and lse equal the gate
+    kernels followed by the attention kernel bitwise, forced blocks
+    included, and the selections match the oracle."""
+    wl = WORKLOADS["long_131k"].with_(batch=2)
+    print(f"[case] given-scores path, long table, rule {rule}", flush=True)
+    case = make_case(wl, "cuda")
+    given, sep = state_for(case, **rule), state_for(case, **rule)
+    assert seer.gated_decode_path(given.shape, given.rule, given.k_max) == 2
+    q = case.q[0]
+    for st in (given, sep):
+        st.build_pool(case.lens)
+    given.step(q, case.lens)
+    sep.step_unfused(q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(given, attr), getattr(sep, attr)), attr
+    S, d, G = wl.block_size, wl.head_dim, wl.group
+    lens = case.lens.tolist()
+    for (b, g) in [(0, 0), (1, wl.num_kv_heads - 1)]:
+        L = lens[b]
+        n = O.block_count(L, S)
+        k, _ = unit_kv(case, b, g, L)
+        s = O.gate_scores(f64(q[b, g * G:(g + 1) * G]), O.pool_keys(k, L, S)[0], d)
+        sel = O.select_blocks(s, k=O.keep_count(n, *wl.keep),
+                              force_first=rule.get("force_first", False),
+                              force_last=rule.get("force_last", False), k_max=given.k_max)
+        u = b * wl.num_kv_heads + g
+        cnt = int(given.sel_cnt[u])
+        assert cnt == len(sel) and np.array_equal(given.sel_idx[u].cpu().numpy()[:cnt], sel)
 
 
 def test_usage_example():
