@@ -147,8 +147,8 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
   const int NB = a.NB;
   const int tid = threadIdx.x, qd = tid >> 6, jq = tid & 63;
   const double inv = 1.0 / sqrt((double)D);
-  // the AND and OR of the keys this thread writes, for the selection
-  uint64_t kand = ~0ull, kor = 0;
+  // the fold of the keys this thread writes, for the selection
+  KeyFold kf;
   // One pass over blocks j0 .. j0 + PASS - 1; the first (FIRST) also sums the
   // query and may take the entry loads (peeled, so that they are dead after).
   auto pass = [&](int j0, auto first_tag) {
@@ -206,13 +206,12 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
                           s_part[3 * PASS + t];
         const uint64_t key = order_key(sc * inv);
         s_key[j] = key;
-        kand &= key;
-        kor |= key;
+        kf.add(key);
       }
     }
-    // the last pass hands the keys' AND and OR to the selection (behind this
-    // barrier; topk_keys_collect reads them)
-    if (j0 + PASS >= n) topk_keys_publish<kThreads>(kand, kor, s_hist);
+    // the last pass hands the keys' fold to the selection (behind this
+    // barrier; topk_keys_collect reads it)
+    if (j0 + PASS >= n) topk_keys_publish<kThreads>(kf, s_hist);
     __syncthreads();
   };
   pass(0, BoolTag<true>{});  // n >= 1
@@ -220,7 +219,7 @@ __device__ __forceinline__ void fused_scores(const DecodeArgs& a, int b, int g, 
 }
 
 // The order keys of unit u's n given scores (a.scores_in, as the gate's score
-// kernel wrote them) into s_key, their AND and OR published for the selection
+// kernel wrote them) into s_key, their fold published for the selection
 // like fused_scores does; ends with a barrier.  The first 8 * kThreads come
 // from the entry loads when those are this unit's.
 template <typename T, int D, int QR, bool PRE>
@@ -239,12 +238,11 @@ __device__ __forceinline__ void given_score_keys(const DecodeArgs& a, int u, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = sc[min(tid + e * kThreads, n - 1)];
   }
-  uint64_t kand = ~0ull, kor = 0;
+  KeyFold kf;
   auto put = [&](int j, double v) {
     const uint64_t key = order_key(v);
     s_key[j] = key;
-    kand &= key;
-    kor |= key;
+    kf.add(key);
   };
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -256,7 +254,7 @@ __device__ __forceinline__ void given_score_keys(const DecodeArgs& a, int u, int
     for (int e = 0; e < 8; ++e)
       if (j0 + e * kThreads < n) put(j0 + e * kThreads, x[e]);
   }
-  topk_keys_publish<kThreads>(kand, kor, s_hist);
+  topk_keys_publish<kThreads>(kf, s_hist);
   __syncthreads();
 }
 
@@ -317,10 +315,9 @@ __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int 
   }
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
-  } else if (!forced) {  // the keys' AND and OR came with the scores
-    uint64_t kand, kor;
-    topk_keys_collect<kThreads>(s_hist, kand, kor);
-    block_topk_ids_from<kThreads>(s_key, n, k, kand, kor, s_hist, s_scan, dst);
+  } else if (!forced) {  // the keys' fold came with the scores
+    block_topk_ids_from<kThreads>(s_key, n, k, topk_keys_collect<kThreads>(s_hist), s_hist,
+                                  s_scan, dst);
   } else {
     block_topk_ids<kThreads>(s_key, n, k, s_hist, s_scan, dst);
   }

@@ -156,9 +156,10 @@ __device__ __forceinline__ double load_as_double<float>(const float* p, int64_t 
 // above the threshold's key; then block_topk_ids (an exact radix select by the
 // whole workgroup); the ids go to the rows of KV heads g_lo .. g_hi - 1 (from
 // LDS when UNIFIED), the scores written out are the blocks' own.
-// ANDOR: the keys' AND and OR were published (topk_keys_publish) before the
-// barrier that preceded the call; the selection takes them from there unless
-// forced blocks change the keys.
+// ANDOR: the keys' fold (AND and OR, also of the keys >= 0, and their count)
+// was published (topk_keys_publish) before the barrier that preceded the
+// call; the selection takes it from there unless forced blocks change the
+// keys.
 template <int NT, bool UNIFIED, bool SCORES = true, bool ANDOR = false>
 __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, int g_hi, int n,
                                             uint64_t* s_key, int32_t* s_ids, int* s_hist,
@@ -201,9 +202,7 @@ __device__ __forceinline__ void gate_finish(const GateArgs& a, int b, int g_lo, 
     // one wave's extra work (with 4 waves the workgroup select is faster)
     if (tid < kWave) wave_topk_ids(s_key, n, k, s_hist, dst);
   } else if (ANDOR && nf == 0) {
-    uint64_t kand, kor;
-    topk_keys_collect<NT>(s_hist, kand, kor);
-    block_topk_ids_from<NT>(s_key, n, k, kand, kor, s_hist, s_scan, dst);
+    block_topk_ids_from<NT>(s_key, n, k, topk_keys_collect<NT>(s_hist), s_hist, s_scan, dst);
   } else {
     block_topk_ids<NT>(s_key, n, k, s_hist, s_scan, dst);
   }
@@ -595,18 +594,17 @@ __global__ __launch_bounds__(kScoreThreads) void gate_unit_kernel(GateArgs a) {
   __shared__ int s_scan[kScoreThreads / 64 + 1];
   const int u = blockIdx.x, b = u / a.Hkv, g = u - b * a.Hkv;
   const int lens_old = APPEND ? a.lens_old[b] : 0;  // requested with the length
-  uint64_t kand = ~0ull, kor = 0;  // of the keys this thread writes
+  KeyFold kf;  // of the keys this thread writes
   score_chunk<T, D, VEC4, APPEND, false>(
       a, u, b, g, [&] { return seq_blocks(a.lens[b], a.S, a.NB); }, 0, s_q, s_part,
       [&](int j, double sc) {
         const uint64_t key = order_key(sc);
         s_key[j] = key;
-        kand &= key;
-        kor |= key;
+        kf.add(key);
       },
       lens_old);
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
-  topk_keys_publish<kScoreThreads>(kand, kor, s_hist);
+  topk_keys_publish<kScoreThreads>(kf, s_hist);
   __syncthreads();
   gate_finish<kScoreThreads, false, true, true>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }
@@ -625,12 +623,11 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = sc[min(tid + e * NT, a.NB - 1)];
   const int n = seq_blocks(a.lens[b], a.S, a.NB);
-  uint64_t kand = ~0ull, kor = 0;  // of the keys this thread writes
+  KeyFold kf;  // of the keys this thread writes
   auto put = [&](int j, double v) {
     const uint64_t key = order_key(v);
     s_key[j] = key;
-    kand &= key;
-    kor |= key;
+    kf.add(key);
   };
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -642,7 +639,7 @@ __global__ __launch_bounds__(kSelectThreads) void gate_select_kernel(GateArgs a)
     for (int e = 0; e < 8; ++e)
       if (j0 + e * NT < n) put(j0 + e * NT, x[e]);
   }
-  topk_keys_publish<NT>(kand, kor, s_hist);
+  topk_keys_publish<NT>(kf, s_hist);
   __syncthreads();
   gate_finish<NT, false, false, true>(a, b, g, g + 1, n, s_key, nullptr, s_hist, s_scan);
 }

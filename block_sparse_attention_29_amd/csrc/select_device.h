@@ -67,61 +67,90 @@ __device__ __forceinline__ int kept_count_forced(int n, const int32_t* top_k, in
 // Key that ranks a forced block above every score.
 constexpr uint64_t kForcedKey = ~0ull;
 
-// The block-wide AND and OR of the order keys, which give the bits every key
-// shares (the radix select starts below them).  Each thread folds the keys it
-// holds into (kand, kor); topk_keys_publish, called by every thread before a
-// workgroup barrier, reduces them per wave (DPP within rows, lane reads across
-// them) into s_hist[512 .. 512 + 4 NT/64) and clears the first histogram
-// s_hist[0 .. 256); after the barrier topk_keys_collect gives every thread the
-// block's values.  A caller that writes the keys can fold them as it writes
-// and publish before the barrier that follows the writes, saving the select a
-// pass over the keys and a barrier.
+// What the radix select starts from, folded over the order keys: the AND and
+// OR of all keys, and the AND, OR and number of the keys with the top bit set
+// (the scores >= 0).  The bits every key of a set shares are bits the select
+// need not histogram; when at least k keys are >= 0, the kept keys are among
+// those, and their shared bits usually reach much further down (the sign and
+// most of the exponent), which saves a pass.  Each thread folds the keys it
+// holds (add); topk_keys_publish, called by every thread before a workgroup
+// barrier, reduces the folds per wave (DPP within rows, lane reads across
+// them) into s_hist[512 .. 512 + 9 NT/64) and clears the first histogram
+// s_hist[0 .. 256); after the barrier topk_keys_collect gives every thread
+// the block's fold.  A caller that writes the keys can fold them as it
+// writes and publish before the barrier that follows the writes, saving the
+// select a pass over the keys and a barrier.
+struct KeyFold {
+  uint64_t kand = ~0ull, kor = 0;  // all keys
+  uint64_t pand = ~0ull, por = 0;  // keys >= 2^63 (scores >= 0)
+  int np = 0;                      // how many of those
+  __device__ __forceinline__ void add(uint64_t key) {
+    kand &= key;
+    kor |= key;
+    const bool p = (key >> 63) != 0;
+    pand = p ? (pand & key) : pand;
+    por = p ? (por | key) : por;
+    np += p ? 1 : 0;
+  }
+};
+
+constexpr int kFoldWords = 9;  // per wave in s_hist[512 ..]: 4 ANDs, 4 ORs, the count
+
 template <int NT>
-__device__ __forceinline__ void topk_keys_publish(uint64_t kand, uint64_t kor, int* s_hist) {
+__device__ __forceinline__ void topk_keys_publish(const KeyFold& f, int* s_hist) {
+  static_assert(512 + kFoldWords * (NT / 64) <= 3 * 256, "fold words fit the third histogram");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t r4[4] = {(uint32_t)kand, (uint32_t)(kand >> 32), (uint32_t)kor, (uint32_t)(kor >> 32)};
+  uint32_t r[kFoldWords] = {(uint32_t)f.kand, (uint32_t)(f.kand >> 32),
+                            (uint32_t)f.pand, (uint32_t)(f.pand >> 32),
+                            (uint32_t)f.kor,  (uint32_t)(f.kor >> 32),
+                            (uint32_t)f.por,  (uint32_t)(f.por >> 32), (uint32_t)f.np};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t x = r4[i];
-    const bool isand = i < 2;
-    uint32_t y;
-    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xF, 0xF, true);
-    x = isand ? (x & y) : (x | y);
-    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xF, 0xF, true);
-    x = isand ? (x & y) : (x | y);
-    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xF, 0xF, true);
-    x = isand ? (x & y) : (x | y);
-    y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xF, 0xF, true);
-    x = isand ? (x & y) : (x | y);
+  for (int i = 0; i < kFoldWords; ++i) {
+    // words 0-3 fold by AND, 4-7 by OR, 8 by addition
+    auto op = [&](uint32_t x, uint32_t y) { return i < 4 ? (x & y) : i < 8 ? (x | y) : x + y; };
+    uint32_t x = r[i];
+    x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xF, 0xF, true));
+    x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xF, 0xF, true));
+    x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xF, 0xF, true));
+    x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xF, 0xF, true));
     const uint32_t a0 = (uint32_t)readlane_i((int)x, 0), a1 = (uint32_t)readlane_i((int)x, 16);
     const uint32_t a2 = (uint32_t)readlane_i((int)x, 32), a3 = (uint32_t)readlane_i((int)x, 48);
-    r4[i] = isand ? (a0 & a1 & a2 & a3) : (a0 | a1 | a2 | a3);
+    r[i] = op(op(a0, a1), op(a2, a3));
   }
   int* s_red = s_hist + 2 * 256;
-  if (lane < 4)
-    s_red[wv * 4 + lane] = (int)(lane == 0 ? r4[0] : lane == 1 ? r4[1] : lane == 2 ? r4[2] : r4[3]);
+  if (lane < kFoldWords) {
+    uint32_t v = r[0];
+#pragma unroll
+    for (int i = 1; i < kFoldWords; ++i) v = lane == i ? r[i] : v;
+    s_red[wv * kFoldWords + lane] = (int)v;
+  }
   if (tid < 256) s_hist[tid] = 0;
 }
 
 template <int NT>
-__device__ __forceinline__ void topk_keys_collect(const int* s_hist, uint64_t& kand,
-                                                  uint64_t& kor) {
+__device__ __forceinline__ KeyFold topk_keys_collect(const int* s_hist) {
   constexpr int NW = NT / 64;
   const int* s_red = s_hist + 2 * 256;
-  uint32_t t4[4] = {~0u, ~0u, 0u, 0u};
+  uint32_t t[kFoldWords] = {~0u, ~0u, ~0u, ~0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    t4[0] &= (uint32_t)s_red[i * 4 + 0];
-    t4[1] &= (uint32_t)s_red[i * 4 + 1];
-    t4[2] |= (uint32_t)s_red[i * 4 + 2];
-    t4[3] |= (uint32_t)s_red[i * 4 + 3];
+  for (int w = 0; w < NW; ++w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] &= (uint32_t)s_red[w * kFoldWords + i];
+#pragma unroll
+    for (int i = 4; i < 8; ++i) t[i] |= (uint32_t)s_red[w * kFoldWords + i];
+    t[8] += (uint32_t)s_red[w * kFoldWords + 8];
   }
-  kand = ((uint64_t)t4[1] << 32) | t4[0];
-  kor = ((uint64_t)t4[3] << 32) | t4[2];
+  KeyFold f;
+  f.kand = ((uint64_t)t[1] << 32) | t[0];
+  f.pand = ((uint64_t)t[3] << 32) | t[2];
+  f.kor = ((uint64_t)t[5] << 32) | t[4];
+  f.por = ((uint64_t)t[7] << 32) | t[6];
+  f.np = (int)t[8];
+  return f;
 }
 
 // Writes the ids of the k largest keys of s_key[0..n) (ties to the lower id),
-// ascending, to out[0..k), given the keys' block-wide AND and OR (see
+// ascending, to out[0..k), given the keys' block-wide fold (see
 // topk_keys_publish, whose barrier must have passed: it also clears the
 // first histogram).  Requires 0 < k < n and NT >= 256; every thread of the
 // workgroup calls it (it contains __syncthreads()).  Scratch in LDS: s_hist
@@ -129,7 +158,8 @@ __device__ __forceinline__ void topk_keys_collect(const int* s_hist, uint64_t& k
 //
 // Exact radix select over the 64-bit keys.  Thread t owns the contiguous ids
 // [t*m, t*m + m).  The first digit is the 8 bits from the highest bit where
-// keys differ, each later digit the next 8 bits down.  Each pass histograms
+// the candidates differ (the keys >= 2^63 when at least k of them exist, else
+// all keys), each later digit the next 8 bits down.  Each pass histograms
 // the digit of the keys still matching the chosen prefix, and every wave
 // scans the 256 bins from the top (DPP) to find the digit that holds the
 // krem-th largest key, so one barrier per pass suffices: the histograms
@@ -139,16 +169,22 @@ __device__ __forceinline__ void topk_keys_collect(const int* s_hist, uint64_t& k
 // keys equal to it in id order.  One block scan of packed (above, equal)
 // counts then gives every thread the output slots of its ids.
 template <int NT>
-__device__ void block_topk_ids_from(const uint64_t* s_key, int n, int k, uint64_t kand,
-                                    uint64_t kor, int* s_hist, int* s_scan, int32_t* out) {
+__device__ void block_topk_ids_from(const uint64_t* s_key, int n, int k, const KeyFold& f,
+                                    int* s_hist, int* s_scan, int32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int m = (n + NT - 1) / NT;
   const int lo = min(n, tid * m), hi = min(n, lo + m);
-  const uint64_t diff = kand ^ kor;
+  // When at least k keys are >= 2^63 (and some are not), every kept key is
+  // one of them: start from the bits those share (bit 63 among them, so no
+  // smaller key matches the prefix and none exceeds it); else from the bits
+  // all keys share.
+  const bool upper = f.np >= k && f.np < n;
+  const uint64_t cand = upper ? f.pand : f.kand, cor = upper ? f.por : f.kor;
+  const uint64_t diff = cand ^ cor;
 
-  int top = diff ? 63 - __builtin_clzll(diff) : -1;  // highest bit where keys differ
+  int top = diff ? 63 - __builtin_clzll(diff) : -1;  // highest bit where candidates differ
   uint64_t mask = top >= 63 ? 0ull : (~0ull << (top + 1));
-  uint64_t prefix = kand & mask;
+  uint64_t prefix = cand & mask;
   int krem = k;
   int slot = 0, nxt = 1;
   while (top >= 0) {
@@ -211,7 +247,7 @@ __device__ void block_topk_ids_from(const uint64_t* s_key, int n, int k, uint64_
   }
 }
 
-// block_topk_ids_from with the AND and OR taken here: a pass over the keys
+// block_topk_ids_from with the fold taken here: a pass over the keys
 // and a barrier.  Same requirements and scratch.
 template <int NT>
 __device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist, int* s_scan,
@@ -219,16 +255,11 @@ __device__ void block_topk_ids(const uint64_t* s_key, int n, int k, int* s_hist,
   const int tid = threadIdx.x;
   const int m = (n + NT - 1) / NT;
   const int lo = min(n, tid * m), hi = min(n, lo + m);
-  uint64_t kand = ~0ull, kor = 0;
-  for (int j = lo; j < hi; ++j) {
-    const uint64_t key = s_key[j];
-    kand &= key;
-    kor |= key;
-  }
-  topk_keys_publish<NT>(kand, kor, s_hist);
+  KeyFold f;
+  for (int j = lo; j < hi; ++j) f.add(s_key[j]);
+  topk_keys_publish<NT>(f, s_hist);
   __syncthreads();
-  topk_keys_collect<NT>(s_hist, kand, kor);
-  block_topk_ids_from<NT>(s_key, n, k, kand, kor, s_hist, s_scan, out);
+  block_topk_ids_from<NT>(s_key, n, k, topk_keys_collect<NT>(s_hist), s_hist, s_scan, out);
 }
 
 }  // namespace seer
