@@ -335,7 +335,7 @@ def run_workload(wl, args):
 
     # ---- fused-kernel timing: back-to-back launches in one graph, events
     # around it on the launch stream ----
-    n_k = n_layers if loop else max(4 * n_layers, n_steps // 2)
+    n_k = 8 * n_layers if loop else max(4 * n_layers, n_steps // 2)
     if not fused:
         # the partial kernel runs on each layer's selection for the lengths it
         # is timed at (a decode loop's steps moved the lengths on)
