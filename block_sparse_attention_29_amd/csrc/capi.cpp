@@ -253,18 +253,25 @@ bool fused_gate_runs(const seer_shape* s, const seer_select* rule, int32_t k_max
 // fits.  Each workgroup then selects its units from their scores (the unit's
 // selection, bit-identical in every workgroup) in place of a selection launch
 // and its round trips.
-bool given_scores_runs(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
-                       int tokens) {
-  if (tokens != 1 || rule->mode != SEER_SELECT_TOPK || rule->unified) return false;
-  if (rule->fuse != SEER_FUSE_AUTO) return false;
-  if (s->max_blocks <= seer::kGateScoreChunk) return false;
+// Whether the single-token attention kernel with W waves can select from
+// given scores for this rule: a per-unit top-k rule, at most one unit per
+// workgroup, and its LDS fits.
+bool given_scores_fit(const seer_shape* s, const seer_select* rule, int32_t k_max, int W) {
+  if (rule->mode != SEER_SELECT_TOPK || rule->unified) return false;
   const int U = s->batch * s->num_kv_heads;
   if (U > W / seer::kDecodeWavesPerWG) return false;
-  const size_t st = gated_static_smem(s, tokens);
+  const size_t st = gated_static_smem(s, 1);
   if (st == (size_t)-1) return false;
   const size_t dyn = seer::gated_decode_smem_bytes(U, s->max_blocks,
                                                    seer::gated_decode_ids_cap(U, k_max, W));
   return st + dyn <= max_block_smem();
+}
+
+bool given_scores_runs(const seer_shape* s, const seer_select* rule, int32_t k_max, int W,
+                       int tokens) {
+  if (tokens != 1 || rule->fuse != SEER_FUSE_AUTO) return false;
+  if (s->max_blocks <= seer::kGateScoreChunk) return false;
+  return given_scores_fit(s, rule, k_max, W);
 }
 
 // How a gated call selects, for this shape, rule and wave count.
@@ -344,6 +351,36 @@ seer_status check_tokens(const seer_shape* shape, int32_t tokens) {
   return SEER_OK;
 }
 
+// Validates a learned gate call and fills the gate kernels' arguments.
+seer_status learned_gate_args(const seer_shape* shape, const void* q, const float* pooled,
+                              const int32_t* lens, const seer_gate_weights* weights,
+                              const seer_select* rule, int32_t k_max, double* scores,
+                              int32_t* sel_idx, int32_t* sel_cnt, seer::GateArgs* out) {
+  const seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  if (st) return st;
+  if (!weights || !weights->w1 || !weights->w1_scale || !weights->b1 || !weights->wq)
+    return fail(SEER_ERR_INVALID_ARG, "gate weights missing");
+  if (!aligned16(weights->w1) || !aligned16(weights->wq) || ((uintptr_t)weights->w1_scale & 3) ||
+      ((uintptr_t)weights->b1 & 3))
+    return fail(SEER_ERR_INVALID_ARG,
+                "gate weights misaligned (w1 and wq 16-byte aligned, w1_scale and b1 4-byte)");
+  if (weights->hidden != seer::kGateHidden)
+    return fail(SEER_ERR_UNSUPPORTED, "gate hidden width %d != %d", weights->hidden,
+                seer::kGateHidden);
+  if (rule->unified)
+    return fail(SEER_ERR_UNSUPPORTED, "a unified selection is not supported by the learned gate");
+  seer::GateArgs a = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  a.w1 = weights->w1;
+  a.w1_scale = weights->w1_scale;
+  a.b1 = weights->b1;
+  a.wq = weights->wq;
+  if (seer::learned_gate_smem_total(a.D, a.NB) > max_block_smem())
+    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
+  *out = a;
+  return SEER_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -416,30 +453,15 @@ seer_status seer_learned_gate_select(const seer_shape* shape, const void* q, con
                                      const int32_t* lens, const seer_gate_weights* weights,
                                      const seer_select* rule, int32_t k_max, double* scores,
                                      int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
-  const seer_status st = check_gate(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
+  seer::GateArgs a;
+  const seer_status st = learned_gate_args(shape, q, pooled, lens, weights, rule, k_max, scores,
+                                           sel_idx, sel_cnt, &a);
   if (st) return st;
-  if (!weights || !weights->w1 || !weights->w1_scale || !weights->b1 || !weights->wq)
-    return fail(SEER_ERR_INVALID_ARG, "gate weights missing");
-  if (!aligned16(weights->w1) || !aligned16(weights->wq) || ((uintptr_t)weights->w1_scale & 3) ||
-      ((uintptr_t)weights->b1 & 3))
-    return fail(SEER_ERR_INVALID_ARG,
-                "gate weights misaligned (w1 and wq 16-byte aligned, w1_scale and b1 4-byte)");
-  if (weights->hidden != seer::kGateHidden)
-    return fail(SEER_ERR_UNSUPPORTED, "gate hidden width %d != %d", weights->hidden,
-                seer::kGateHidden);
-  if (rule->unified)
-    return fail(SEER_ERR_UNSUPPORTED, "a unified selection is not supported by the learned gate");
-  seer::GateArgs a = gate_args(shape, q, pooled, lens, rule, k_max, scores, sel_idx, sel_cnt);
-  a.w1 = weights->w1;
-  a.w1_scale = weights->w1_scale;
-  a.b1 = weights->b1;
-  a.wq = weights->wq;
-  if (seer::learned_gate_smem_total(a.D, a.NB) > max_block_smem())
-    return fail(SEER_ERR_UNSUPPORTED, "max_blocks %d needs more LDS than a workgroup has", a.NB);
   const hipError_t e = seer::launch_learned_gate(a, stream);
   if (e != hipSuccess) return hip_fail(e, "learned_gate launch");
   return ok();
 }
+
 
 seer_status seer_gate_scores_topk(const seer_shape* shape, const void* q, const float* pooled,
                                   const int32_t* lens, const int32_t* top_k, int32_t keep_num,
@@ -576,6 +598,42 @@ seer_status seer_gated_sparse_decode_append(const seer_shape* shape, const void*
                                        k_max, softmax_scale, scores, sel_idx, sel_cnt, workspace,
                                        workspace_bytes, stream);
   if (st) return st;
+  return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
+}
+
+seer_status seer_learned_gated_sparse_decode(
+    const seer_shape* shape, const void* q, const seer_kv* kv, const int32_t* lens,
+    const float* pooled, const seer_gate_weights* weights, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, float* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  seer::GateArgs ga;
+  seer_status st = learned_gate_args(shape, q, pooled, lens, weights, rule, k_max, scores,
+                                     sel_idx, sel_cnt, &ga);
+  if (st) return st;
+  seer::DecodeArgs a;
+  if ((st = prepare_decode(shape, q, kv, lens, sel_idx, sel_cnt, k_max, softmax_scale,
+                           workspace, workspace_bytes, &a)))
+    return st;
+  const int U = shape->batch * shape->num_kv_heads;
+  hipError_t e;
+  // Where the learned gate splits a unit over several workgroups its scores go
+  // to memory anyway: the attention kernel's workgroups then select from them
+  // (as the selection launch would, bit for bit) instead of a selection launch.
+  if (seer::learned_gate_workgroups_per_unit(U, shape->max_blocks) > 1 &&
+      rule->fuse != SEER_FUSE_NEVER && given_scores_fit(shape, rule, k_max, a.W)) {
+    if ((e = seer::launch_learned_gate_scores(ga, stream)) != hipSuccess)
+      return hip_fail(e, "learned gate score launch");
+    set_fused_gate(shape, pooled, rule, k_max, scores, sel_idx, sel_cnt, a);
+    a.scores_in = scores;
+    if ((e = seer::launch_gated_decode_partial(a, stream)) != hipSuccess)
+      return hip_fail(e, "gated decode_partial launch");
+  } else {
+    if ((e = seer::launch_learned_gate(ga, stream)) != hipSuccess)
+      return hip_fail(e, "learned_gate launch");
+    if ((e = seer::launch_decode_partial(a, stream)) != hipSuccess)
+      return hip_fail(e, "decode_partial launch");
+  }
+  if (!out) return ok();
   return seer_sparse_decode_combine(shape, out, lse, workspace, workspace_bytes, stream);
 }
 

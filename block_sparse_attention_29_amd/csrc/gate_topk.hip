@@ -983,6 +983,18 @@ size_t learned_gate_smem_total(int D, int NB) {
   return attr.sharedSizeBytes + learned_gate_smem_dynamic(NB);
 }
 
+int learned_gate_workgroups_per_unit(int U, int NB) { return learned_gate_split(U, NB); }
+
+hipError_t launch_learned_gate_scores(const GateArgs& a, hipStream_t stream) {
+  const int U = a.B * a.Hkv;
+  const int S = learned_gate_split(U, a.NB);
+  if (S < 2) return hipErrorInvalidValue;  // one workgroup per unit selects itself
+  GateArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(learned_kernel(a.dtype, a.D, true), dim3(U * S), dim3(kLgThreads), params,
+                         0, stream);
+}
+
 hipError_t launch_learned_gate(const GateArgs& a, hipStream_t stream) {
   GateArgs args = a;
   void* params[] = {&args};

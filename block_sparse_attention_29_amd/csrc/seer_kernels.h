@@ -153,6 +153,11 @@ size_t gate_smem_bytes(int NB, int k_max);
 // The learned gate network's scores, then the same selection rule (not unified).
 constexpr int kGateHidden = 256;
 hipError_t launch_learned_gate(const GateArgs& a, hipStream_t stream);
+// Workgroups the learned gate gives each unit (more than one: the scores go to
+// a.scores and a separate selection follows), and that split score launch
+// alone (hipErrorInvalidValue when a unit has one workgroup).
+int learned_gate_workgroups_per_unit(int U, int NB);
+hipError_t launch_learned_gate_scores(const GateArgs& a, hipStream_t stream);
 // All LDS (static and dynamic) the learned gate kernel needs, and its dynamic part.
 size_t learned_gate_smem_total(int D, int NB);
 size_t learned_gate_smem_dynamic(int NB);

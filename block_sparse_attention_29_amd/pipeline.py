@@ -9,7 +9,9 @@ table, open-block sums, scores, selection, outputs, workspace) and enqueues:
                                  gate network when gate weights are given)
     attend(q, lens)              sparse (or dense) decode attention
     step(q, lens)                select + attend, the gate fused into the attention
-                                 kernel (two launches; with a learned gate, three)
+                                 kernel (two launches; with a learned gate, its
+                                 score launch, then the attention kernel selecting
+                                 from those scores where that applies, then the merge)
     step_append(q, old, new)     append, then step (the append inside the gate's score
                                  kernel where there is one)
     step_unfused(q, lens)        select, then attend (three launches)
@@ -123,7 +125,16 @@ class DecodeState:
         (the parameter-free gate fused into the attention kernel where that
         pays, for one or several query tokens)."""
         if self.gate_weights is not None:
-            return self.step_unfused(q, lens)
+            auto = self.combine == seer.SEER_COMBINE_AUTO
+            seer.learned_gated_sparse_decode(self.shape, q, self.kv, lens, self.pooled,
+                                             self.gate_weights, self.rule, self.k_max,
+                                             self.scores, self.sel_idx, self.sel_cnt,
+                                             self.out if auto else None, self.lse if auto else None,
+                                             self.workspace)
+            if not auto:
+                seer.sparse_decode_combine(self.shape, self.out, self.lse, self.workspace,
+                                           self.combine)
+            return self.out, self.lse
         if self.T > 1:
             seer.multi_gated_sparse_decode(self.shape, self.T, q, self.kv, lens, self.pooled,
                                            self.rule, self.k_max, self.scores, self.sel_idx,

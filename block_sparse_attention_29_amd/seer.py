@@ -32,6 +32,7 @@ EXPORTS = (
     "seer_gate_scores_topk",
     "seer_gate_select",
     "seer_learned_gate_select",
+    "seer_learned_gated_sparse_decode",
     "seer_sparse_decode_workspace_size",
     "seer_sparse_decode",
     "seer_sparse_decode_partial",
@@ -164,6 +165,10 @@ def load(path: str = LIB_PATH):
     lib.seer_gate_select.argtypes = [SP, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
     lib.seer_learned_gate_select.argtypes = [SP, _P, _P, _P, ctypes.POINTER(GateWeightsC), RP,
                                              _I32, _P, _P, _P, _P]
+    lib.seer_learned_gated_sparse_decode.argtypes = [SP, _P, KP, _P, _P,
+                                                     ctypes.POINTER(GateWeightsC), RP, _I32,
+                                                     ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                                     ctypes.c_size_t, _P]
     lib.seer_multi_gate_select.argtypes = [SP, _I32, _P, _P, _P, RP, _I32, _P, _P, _P, _P]
     lib.seer_multi_sparse_decode_workspace_size.argtypes = [SP, _I32,
                                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -196,7 +201,8 @@ def load(path: str = LIB_PATH):
     lib.seer_last_error.argtypes = []
     lib.seer_last_error.restype = ctypes.c_char_p
     for name in ("seer_block_pool_keys", "seer_gate_scores_topk", "seer_gate_select",
-                 "seer_learned_gate_select", "seer_multi_gate_select",
+                 "seer_learned_gate_select", "seer_learned_gated_sparse_decode",
+                 "seer_multi_gate_select",
                  "seer_multi_sparse_decode_workspace_size", "seer_multi_sparse_decode",
                  "seer_sparse_decode_workspace_size", "seer_sparse_decode",
                  "seer_sparse_decode_partial", "seer_sparse_decode_combine",
@@ -326,6 +332,43 @@ def learned_gate_select(shape: Shape, q: torch.Tensor, pooled: torch.Tensor,
     _check(lib.seer_learned_gate_select(ctypes.byref(shape), _ptr(q), _ptr(pooled), _ptr(lens),
                                         ctypes.byref(w), ctypes.byref(rule), k_max,
                                         _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _stream()))
+
+
+def _gate_weights_c(shape: Shape, weights) -> GateWeightsC:
+    H = int(weights.w1.shape[-2])
+    _need(weights.w1, torch.int8, shape.num_kv_heads * H * shape.head_dim, "w1")
+    _need(weights.w1_scale, torch.float32, shape.num_kv_heads * H, "w1_scale")
+    _need(weights.b1, torch.float32, shape.num_kv_heads * H, "b1")
+    _need(weights.wq, torch.float32, shape.num_kv_heads * H * shape.head_dim, "wq")
+    return GateWeightsC(_ptr(weights.w1), _ptr(weights.w1_scale), _ptr(weights.b1),
+                        _ptr(weights.wq), H)
+
+
+def learned_gated_sparse_decode(shape: Shape, q: torch.Tensor, kv: KV, lens: torch.Tensor,
+                                pooled: torch.Tensor, weights, rule: Select, k_max: int,
+                                scores: torch.Tensor, sel_idx: torch.Tensor,
+                                sel_cnt: torch.Tensor, out: Optional[torch.Tensor],
+                                lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                                softmax_scale: float = 0.0):
+    """seer_learned_gated_sparse_decode: the learned gate's step (gate, selection,
+    sparse decode, merge; out=None stops before the merge)."""
+    lib = load()
+    _need_q(shape, q)
+    U = shape.batch * shape.num_kv_heads
+    _need(pooled, torch.float32, U * shape.head_dim * shape.max_blocks, "pooled")
+    _need(lens, torch.int32, shape.batch, "lens")
+    _need(scores, torch.float64, U * shape.max_blocks, "scores")
+    _need(sel_idx, torch.int32, U * k_max, "sel_idx")
+    _need(sel_cnt, torch.int32, U, "sel_cnt")
+    if out is not None:
+        _need(out, torch.float32, shape.batch * shape.num_q_heads * shape.head_dim, "out")
+    if lse is not None:
+        _need(lse, torch.float32, shape.batch * shape.num_q_heads, "lse")
+    w = _gate_weights_c(shape, weights)
+    _check(lib.seer_learned_gated_sparse_decode(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(lens), _ptr(pooled),
+        ctypes.byref(w), ctypes.byref(rule), k_max, softmax_scale, _ptr(scores), _ptr(sel_idx),
+        _ptr(sel_cnt), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
 
 
 def sparse_decode_workspace_size(shape: Shape) -> int:

@@ -310,6 +310,27 @@ seer_status seer_sparse_decode_combine_mode(const seer_shape* shape, int32_t mod
  *  on it.
  * _partial: the first launch(es) alone (gate + partial results in the
  * workspace, selections written); seer_sparse_decode_combine finishes it. */
+/* seer_learned_gated_sparse_decode -- one decode step with the learned gate:
+ * seer_learned_gate_select followed by seer_sparse_decode on its selection,
+ * with bit-identical results (scores, sel_idx, sel_cnt, out, lse) ("Sparse
+ * Attention Reasoning", Step 1: the gate network and its top-k; Step 4: the
+ * attention over the kept blocks).  Where the learned gate gives each
+ * (sequence, KV head) unit several workgroups (few units: its scores go to
+ * memory), the rule is a per-unit top-k (forced blocks allowed), every
+ * attention workgroup meets at most one unit and rule->fuse is not
+ * SEER_FUSE_NEVER, the attention kernel's workgroups select from those
+ * scores in place of a selection launch; otherwise the three launches run
+ * as the two calls would.
+ *  Arguments: as seer_learned_gate_select (q, pooled, lens, weights, rule,
+ *  k_max, scores, sel_idx, sel_cnt, all written) and seer_sparse_decode (kv,
+ *  softmax_scale, out, lse, workspace); out = NULL stops after the partial
+ *  results in the workspace (seer_sparse_decode_combine finishes them).
+ *  Errors: those of the two calls, before any launch. */
+seer_status seer_learned_gated_sparse_decode(
+    const seer_shape* shape, const void* q, const seer_kv* kv, const int32_t* lens,
+    const float* pooled, const seer_gate_weights* weights, const seer_select* rule, int32_t k_max,
+    float softmax_scale, double* scores, int32_t* sel_idx, int32_t* sel_cnt, float* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 /* seer_gated_decode_is_fused -- *fused = 1 if seer_gated_sparse_decode
  * (tokens = 1) or seer_multi_gated_sparse_decode (tokens > 1) with this shape,
  * rule and k_max scores and selects inside the attention kernel on the

@@ -276,3 +276,25 @@ def test_learned_gate_split_equals_one_launch():
     assert torch.equal(full.sel_cnt[:U].cpu(), part.sel_cnt.cpu())
     assert torch.equal(full.sel_idx.view(-1, full.k_max)[:U].cpu(),
                        part.sel_idx.view(-1, part.k_max).cpu())
+
+
+@pytest.mark.parametrize("rule", [dict(), dict(force_first=True, force_last=True),
+                                  dict(threshold=0.0)], ids=["topk", "forced", "threshold"])
+@pytest.mark.parametrize("name", ["planted_8k", "sparse90_32k"])
+def test_learned_step_equals_separate_calls(name, rule):
+    """The learned gate's one-call step (its score launch, then the attention
+    kernel selecting from those scores where the gate splits units over
+    workgroups) writes exactly what the gate call followed by the attention
+    call writes: scores, ids, counts, out, lse."""
+    wl = WORKLOADS[name].with_(batch=4)
+    print(f"[case] learned step vs separate calls, {name}, {rule}", flush=True)
+    case = make_case(wl, "cuda")
+    w = make_gate_weights(wl.num_kv_heads, wl.head_dim, seed=5).to("cuda")
+    one, sep = state_for(case, gate_weights=w, **rule), state_for(case, gate_weights=w, **rule)
+    for st in (one, sep):
+        st.build_pool(case.lens)
+    one.step(case.q, case.lens)
+    sep.step_unfused(case.q, case.lens)
+    torch.cuda.synchronize()
+    for attr in ("scores", "sel_idx", "sel_cnt", "out", "lse"):
+        assert torch.equal(getattr(one, attr), getattr(sep, attr)), attr
