@@ -275,9 +275,8 @@ __device__ __forceinline__ void fused_gate_write(const DecodeArgs& a, int u, int
 }
 
 // Gate of unit u inside a decode workgroup (the fused mode): the fp64 scores
-// of its n blocks (fused_scores; with GIVEN the gate's score kernel already
-// wrote them to a.scores_in and they are read back), then its k kept ids,
-// ascending, into dst (LDS).  With `owner` the workgroup also writes the scores, ids and count out
+// of its n blocks (fused_scores), then its k kept ids, ascending, into dst
+// (LDS).  With `owner` the workgroup also writes the scores, ids and count out
 // (fused_gate_write); a caller may instead write them later from the same LDS.
 template <typename T, int D, int QR, bool MULTI, bool PRE, bool GIVEN = false>
 __device__ __forceinline__ void fused_gate_unit(const DecodeArgs& a, int u, int n, int k,
